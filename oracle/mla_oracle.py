@@ -1,0 +1,223 @@
+"""Plain fp64 CPU oracle for MLA prefill: the definition of what the HIP path computes.
+
+TEST INFRASTRUCTURE ONLY. This module is imported by ``tests/``, by the entry point's smoke
+check and by the bench's ``cpu_baseline`` leg, never by the product path. It shares no code with
+the HIP kernels or their host layer; it only reads the bf16 bit patterns the input generators
+produce and widens them to float64.
+
+Every function is the plain mathematical definition, written two-pass (scores, then a max, then
+the normaliser) with an explicit visibility mask. There is no tiling, no online softmax and no
+reordering beyond what the definition states.
+
+What the pages fix:
+  * The operation is ``O = softmax(Q K^T * softmax_scale) V`` where the K and V that take part are
+    selected by the inputs (page "SparseFlashMla", Description: the formula, with K~ = V~ the
+    participating KV).
+  * Dense MLA prefill runs with K/V expanded to every query head, q/k head 192 = 128 nope + 64
+    rope and v head 128, over ``cu_seqlens`` (page "FlashAttention backend for MLA prefill",
+    ``dispatch`` and the "MLA prefill expands K/V" comment); new tokens attend causally to
+    themselves (``run_prefill_new_tokens``, causal=True, cu_seqlens_q = cu_seqlens_k) and a
+    context chunk attends without a mask and always returns the LSE
+    (``run_prefill_context_chunk``).
+  * The LSE is float32 log-sum-exp of the softmax (page "Sgl project Sglang FA4 Interface",
+    I/O Contract; page "SparseFlashMla", ``softmax_lse``).
+  * Sparse indices are int32; -1 marks an invalid or padded slot; ``topk_length`` gives the valid,
+    left-aligned prefix of each index row (page "SparseFlashMla", Parameters table and
+    Constraints). Sinks are float values per head (same table; page "mla_prefill_branch_sparse_fp8",
+    ``attn_sink_ptr``).
+  * Split partial results are combined into the final result (page "Mojo module mla",
+    ``mla_splitk_reduce``; page "Sgl project Sglang FA4 Interface", Description: split-KV with a
+    combine kernel).
+
+Readings taken where the pages are silent (each also listed with the design notes):
+  R1 LSE is the natural log of the sum of exp of the *scaled* logits.
+  R3 Causal masking is bottom-right aligned: key j is visible to query i of a sequence with
+     Sq queries and Sk keys iff j <= i + Sk - Sq ("RightDownCausal", page "SparseFlashMla",
+     ``ori_mask_mode``). For Sq == Sk this is the ordinary causal mask.
+  R4 A row with no visible key and no sink gets O = 0 and LSE = -inf. With a sink it gets O = 0
+     and LSE = sink.
+  R6 A sink is one extra logit per head, added as-is (not multiplied by the scale), whose value
+     vector is zero. It counts in the normaliser and in the LSE.
+  R7 In the sparse path V is the first ``dv`` columns of the same gathered rows as K.
+  R8 Indices are physical pool rows; any index outside [0, N_kv) is skipped like -1.
+  R9 Slots at or beyond ``topk_length[t]`` are ignored even when they hold a valid row.
+"""
+from __future__ import annotations
+
+import math
+from typing import Iterable, Optional, Sequence, Tuple
+
+import numpy as np
+
+NEG_INF = -math.inf
+
+
+def widen_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns (uint16) -> float64, exactly (a bf16 is the top half of a float32)."""
+    f32 = (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+    return f32.astype(np.float64)
+
+
+def _softmax_rows(scores: np.ndarray, visible: np.ndarray, values: np.ndarray,
+                  sink: Optional[float]) -> Tuple[np.ndarray, np.ndarray]:
+    """Two-pass masked softmax-weighted sum for a block of rows.
+
+    scores: [R, N] scaled logits; visible: [R, N] bool; values: [N, Dv]; sink: scalar logit or None.
+    Returns O [R, Dv] and LSE [R] in float64.
+    """
+    masked = np.where(visible, scores, NEG_INF)
+    row_max = masked.max(axis=1) if masked.shape[1] else np.full(masked.shape[0], NEG_INF)
+    if sink is not None:
+        row_max = np.maximum(row_max, sink)
+    empty = ~np.isfinite(row_max)
+    shift = np.where(empty, 0.0, row_max)
+    weights = np.where(visible, np.exp(masked - shift[:, None]), 0.0)
+    z = weights.sum(axis=1)
+    if sink is not None:
+        z = z + np.exp(sink - shift)
+    out = np.zeros((scores.shape[0], values.shape[1]), dtype=np.float64)
+    ok = ~empty
+    if ok.any():
+        out[ok] = (weights[ok] @ values) / z[ok, None]
+    lse = np.full(scores.shape[0], NEG_INF, dtype=np.float64)
+    lse[ok] = shift[ok] + np.log(z[ok])
+    return out, lse
+
+
+def dense_visible(sq: int, sk: int, causal: bool, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """Visibility mask [len(rows), sk] for one sequence (reading R3: bottom-right causal)."""
+    i = np.arange(sq) if rows is None else np.asarray(rows)
+    j = np.arange(sk)
+    if not causal:
+        return np.ones((i.size, sk), dtype=bool)
+    return j[None, :] <= (i[:, None] + (sk - sq))
+
+
+def dense_mla_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Sequence[int],
+                      cu_k: Sequence[int], scale: float, causal: bool,
+                      sink: Optional[np.ndarray] = None,
+                      heads: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Dense varlen attention, per sequence and head, straight from the definition.
+
+    q [Tq, H, Dqk], k [Tk, H, Dqk], v [Tk, H, Dv] (float64 or bf16 bits). Sequence b owns query
+    rows cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1]. For query i of sequence b and head h:
+    s_j = scale * <q_i, k_j> over all Dqk columns, visible keys per R3, softmax with the optional
+    sink (R6), O = sum_j p_j v_j, LSE = log(sum exp). Returns O [Tq, H, Dv] and LSE [Tq, H]
+    (rows of heads not requested stay NaN).
+    """
+    q, k, v = (_as_f64(x) for x in (q, k, v))
+    tq, h_all, _ = q.shape
+    dv = v.shape[2]
+    heads = list(range(h_all)) if heads is None else list(heads)
+    out = np.full((tq, h_all, dv), np.nan)
+    lse = np.full((tq, h_all), np.nan)
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+        sq, sk = q1 - q0, k1 - k0
+        if sq == 0:
+            continue
+        vis = dense_visible(sq, sk, causal)
+        for h in heads:
+            scores = scale * (q[q0:q1, h, :] @ k[k0:k1, h, :].T)
+            s = None if sink is None else float(sink[h])
+            o, l = _softmax_rows(scores, vis, v[k0:k1, h, :], s)
+            out[q0:q1, h, :] = o
+            lse[q0:q1, h] = l
+    return out, lse
+
+
+def dense_mla_prefill_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Sequence[int],
+                           cu_k: Sequence[int], scale: float, causal: bool,
+                           tokens: Sequence[int], heads: Sequence[int],
+                           sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """The same definition evaluated only at the given (token, head) grid: O [n_tok, n_head, Dv],
+    LSE [n_tok, n_head]. Used to check large problems at sampled rows."""
+    cu_q = np.asarray(cu_q)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    dv = v.shape[2]
+    out = np.zeros((tokens.size, len(heads), dv))
+    lse = np.zeros((tokens.size, len(heads)))
+    for ti, t in enumerate(tokens):
+        b = int(np.searchsorted(cu_q, t, side="right") - 1)
+        q0, k0, k1 = int(cu_q[b]), int(cu_k[b]), int(cu_k[b + 1])
+        sq, sk = int(cu_q[b + 1]) - q0, k1 - k0
+        i = int(t) - q0
+        vis = dense_visible(sq, sk, causal, rows=np.array([i]))
+        for hi, h in enumerate(heads):
+            qrow = _as_f64(q[t, h, :])[None, :]
+            scores = scale * (qrow @ _as_f64(k[k0:k1, h, :]).T)
+            s = None if sink is None else float(sink[h])
+            o, l = _softmax_rows(scores, vis, _as_f64(v[k0:k1, h, :]), s)
+            out[ti, hi] = o[0]
+            lse[ti, hi] = l[0]
+    return out, lse
+
+
+def sparse_valid_slots(indices_row: np.ndarray, n_kv: int, length: Optional[int]) -> np.ndarray:
+    """Valid slots of one token's index row (page "SparseFlashMla": -1 = padded; readings R8, R9)."""
+    idx = np.asarray(indices_row, dtype=np.int64)
+    ok = (idx >= 0) & (idx < n_kv)
+    if length is not None:
+        ok &= np.arange(idx.size) < int(length)
+    return ok
+
+
+def sparse_mla_prefill(q: np.ndarray, kv: np.ndarray, indices: np.ndarray, scale: float,
+                       dv: int = 512, topk_length: Optional[np.ndarray] = None,
+                       sink: Optional[np.ndarray] = None,
+                       tokens: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Sparse top-k attention over one shared latent KV (page "SparseFlashMla" formula, KV_N = 1).
+
+    q [T, H, D], kv [N_kv, D], indices [T, topk] int32. For token t and head h, every valid slot
+    contributes the logit scale * <q[t,h,:], kv[idx,:]> and the value kv[idx, :dv] (R7); each slot
+    counts once, so a duplicated index counts once per slot. Returns O [T, H, dv] and LSE [T, H]
+    (tokens not requested stay NaN).
+    """
+    q = _as_f64(q)
+    kvf = _as_f64(kv)
+    t_all, h_all, _ = q.shape
+    n_kv = kvf.shape[0]
+    toks = range(t_all) if tokens is None else tokens
+    out = np.full((t_all, h_all, dv), np.nan)
+    lse = np.full((t_all, h_all), np.nan)
+    for t in toks:
+        length = None if topk_length is None else int(topk_length[t])
+        ok = sparse_valid_slots(indices[t], n_kv, length)
+        rows = kvf[np.asarray(indices[t], dtype=np.int64)[ok]]
+        scores = scale * (q[t] @ rows.T)                      # [H, n_valid]
+        vis = np.ones(scores.shape, dtype=bool)
+        for h in range(h_all):
+            s = None if sink is None else float(sink[h])
+            o, l = _softmax_rows(scores[h:h + 1], vis[h:h + 1], rows[:, :dv], s)
+            out[t, h] = o[0]
+            lse[t, h] = l[0]
+    return out, lse
+
+
+def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray,
+                     sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Merge S normalised partial results of disjoint key sets (page "Mojo module mla",
+    ``mla_splitk_reduce``; page "Sgl project Sglang FA4 Interface", split-KV combine).
+
+    o_parts [S, R, Dv], lse_parts [S, R]; sink [R] or None (an extra logit with a zero value).
+    LSE = log(sum_s exp(LSE_s) [+ exp(sink)]), O = sum_s exp(LSE_s - LSE) O_s. Rows whose partials
+    are all -inf (and no sink) give O = 0, LSE = -inf.
+    """
+    o_parts = np.asarray(o_parts, dtype=np.float64)
+    lse_parts = np.asarray(lse_parts, dtype=np.float64)
+    terms = lse_parts if sink is None else np.concatenate([lse_parts, np.asarray(sink, np.float64)[None, :]])
+    m = terms.max(axis=0)
+    empty = ~np.isfinite(m)
+    shift = np.where(empty, 0.0, m)
+    total = np.exp(terms - shift[None, :]).sum(axis=0)
+    lse = np.where(empty, NEG_INF, shift + np.log(np.where(empty, 1.0, total)))
+    w = np.where(empty[None, :], 0.0, np.exp(lse_parts - np.where(empty, 0.0, lse)[None, :]))
+    out = (w[:, :, None] * o_parts).sum(axis=0)
+    return out, lse
+
+
+def _as_f64(x: np.ndarray) -> np.ndarray:
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        return widen_bf16(x)
+    return x.astype(np.float64, copy=False)

@@ -1,0 +1,71 @@
+"""CPU reference of the varlen tile plan: the specification of the plan bytes.
+
+TEST INFRASTRUCTURE ONLY (imported by ``tests/`` and nowhere in the product path). The GPU
+planner must produce exactly these int32 words.
+
+The pages describe a GPU kernel that plans a batch of varying-length sequences through a
+fixed-size buffer, plus a helper that zeroes its length counters (page "Mojo module mla":
+``mla_prefill_plan``, ``mla_prefill_plan_kernel``, ``set_buffer_lengths_to_zero``), and a
+separate metadata call whose fixed-size int32 output is the task split the attention operator
+consumes (page "SparseFlashMla", Description: call ``SparseFlashMlaMetadata`` first, and
+Constraints: ``metadata`` is int32 of fixed size). The page gives no format, so the format
+below is this library's own.
+
+Plan format
+-----------
+Slots: ``slot = b * Mt + m`` for sequence ``b`` in [0, B) and query tile ``m`` in [0, Mt) with
+``Mt = ceil(max_seqlen_q / BM)``. A slot is a work item iff ``m * BM < Sq_b``.
+
+For an item: ``kv_end`` is the number of leading keys any row of the tile can see:
+``Sk_b`` without a causal mask; with the bottom-right causal mask it is
+``clamp(i_last + Sk_b - Sq_b + 1, 0, Sk_b)`` where ``i_last = min((m+1)*BM, Sq_b) - 1``.
+``n_blocks = ceil(kv_end / BN)``.
+
+Each item is four int32 words ``(b, m, n_blocks, kv_end)``. Items are ordered longest first:
+by ``n_blocks`` descending, ties by slot ascending. When there are more than ``SORT_CAPACITY``
+slots the items stay in slot order. Words past the last item, up to ``capacity`` items, are -1.
+"""
+from __future__ import annotations
+
+from typing import Sequence, Tuple
+
+import numpy as np
+
+SORT_CAPACITY = 16384
+MAX_BLOCKS = 0x3FFFE
+
+
+def plan_items(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: int, bn: int,
+               causal: bool) -> list:
+    """The work items as (b, m, n_blocks, kv_end) tuples, in plan order."""
+    b_count = len(cu_q) - 1
+    mt = -(-int(max_seqlen_q) // bm) if max_seqlen_q > 0 else 0
+    items = []
+    for b in range(b_count):
+        sq = int(cu_q[b + 1]) - int(cu_q[b])
+        sk = int(cu_k[b + 1]) - int(cu_k[b])
+        for m in range(mt):
+            if m * bm >= sq:
+                continue
+            if causal:
+                i_last = min((m + 1) * bm, sq) - 1
+                kv_end = min(max(i_last + sk - sq + 1, 0), sk)
+            else:
+                kv_end = sk
+            n_blocks = -(-kv_end // bn)
+            items.append((b * mt + m, (b, m, n_blocks, kv_end)))
+    if b_count * mt <= SORT_CAPACITY:
+        items.sort(key=lambda it: (-it[1][2], it[0]))
+    return [it[1] for it in items]
+
+
+def plan_buffer(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: int, bn: int,
+                causal: bool, capacity: int) -> Tuple[np.ndarray, int]:
+    """The full plan buffer (int32 [capacity, 4]) and the item count."""
+    items = plan_items(cu_q, cu_k, max_seqlen_q, bm, bn, causal)
+    if len(items) > capacity:
+        raise ValueError("plan capacity too small")
+    buf = np.full((capacity, 4), -1, dtype=np.int32)
+    if items:
+        buf[: len(items)] = np.asarray(items, dtype=np.int32)
+    return buf, len(items)

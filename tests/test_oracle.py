@@ -1,0 +1,318 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Each test checks the oracle against something other than itself: hand-derived examples, closed
+forms, a library routine the oracle does not use (PyTorch's CPU scaled_dot_product_attention and
+logsumexp, SciPy's softmax), invariants of the definition and brute force on tiny inputs. Together
+they are chosen so that a dropped scale, a wrong mask alignment, a transposed operand, a sink
+multiplied by the scale, a log in the wrong base, the wrong value columns or an ignored
+``topk_length`` each fail at least one test.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mla_oracle as O
+from workloads import f32_to_bf16_bits, bf16_bits_to_f32, make_dense, make_sparse
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "dense_hand_examples.json")
+
+
+def _f(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+# ---------------------------------------------------------------- hand-derived examples
+@pytest.mark.parametrize("case", json.load(open(GOLDEN))["cases"], ids=lambda c: c["name"])
+def test_hand_examples(case):
+    q = _f(case["q"])[:, None, :]
+    k = _f(case["k"])[:, None, :]
+    v = _f(case["v"])[:, None, :]
+    sink = None if case["sink"] is None else _f(case["sink"])
+    o, lse = O.dense_mla_prefill(q, k, v, [0, q.shape[0]], [0, k.shape[0]], case["scale"],
+                                 case["causal"], sink=sink)
+    np.testing.assert_allclose(o[:, 0, :], _f(case["O"]), rtol=0, atol=1e-12)
+    want_lse = np.array([-math.inf if x == "-inf" else x for x in case["LSE"]], dtype=np.float64)
+    assert np.array_equal(np.isinf(lse[:, 0]), np.isinf(want_lse))
+    fin = np.isfinite(want_lse)
+    np.testing.assert_allclose(lse[fin, 0], want_lse[fin], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- library special case
+def _torch_reference(q, k, v, cu_q, cu_k, scale, causal):
+    """PyTorch fp64 CPU SDPA with an explicit boolean mask, and logsumexp of the masked logits."""
+    outs, lses = [], []
+    for b in range(len(cu_q) - 1):
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        sq, sk = q1 - q0, k1 - k0
+        qt = torch.from_numpy(q[q0:q1]).transpose(0, 1)  # [H, sq, d]
+        kt = torch.from_numpy(k[k0:k1]).transpose(0, 1)
+        vt = torch.from_numpy(v[k0:k1]).transpose(0, 1)
+        i = torch.arange(sq)[:, None]
+        j = torch.arange(sk)[None, :]
+        mask = (j <= i + (sk - sq)) if causal else torch.ones(sq, sk, dtype=torch.bool)
+        o = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mask, scale=scale)
+        logits = torch.matmul(qt, kt.transpose(1, 2)) * scale
+        lse = torch.logsumexp(logits.masked_fill(~mask, -math.inf), dim=-1)
+        outs.append(o.transpose(0, 1).numpy())
+        lses.append(lse.transpose(0, 1).numpy())
+    return np.concatenate(outs), np.concatenate(lses)
+
+
+@pytest.mark.parametrize("lens_q,lens_k,causal", [
+    ([7, 33, 1], [7, 33, 1], True),
+    ([7, 33, 1], [7, 33, 1], False),
+    ([5, 16], [40, 16], True),      # Sq < Sk: bottom-right aligned
+    ([12], [30], False),
+])
+def test_dense_matches_torch_sdpa(lens_q, lens_k, causal):
+    c = make_dense("t", lens_q, lens_k, heads=3, causal=causal, seed=11, dqk=24, dv=16)
+    q, k, v = (O.widen_bf16(x) for x in (c.q, c.k, c.v))
+    o, lse = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal)
+    ro, rl = _torch_reference(q, k, v, list(c.cu_q), list(c.cu_k), c.scale, causal)
+    np.testing.assert_allclose(o, ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, rl, rtol=0, atol=1e-12)
+
+
+def test_bottom_right_empty_rows_match_definition():
+    # Sq > Sk with the bottom-right mask: the first Sq - Sk rows see nothing (reading R4).
+    c = make_dense("t", [9], [4], heads=2, causal=True, seed=12, dqk=16, dv=8)
+    o, lse = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True)
+    assert np.all(o[:5] == 0) and np.all(np.isneginf(lse[:5]))
+    q, k, v = (O.widen_bf16(x) for x in (c.q, c.k, c.v))
+    ro, rl = _torch_reference(q[5:], k, v, [0, 4], [0, 4], c.scale, True)
+    np.testing.assert_allclose(o[5:], ro, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse[5:], rl, rtol=0, atol=1e-12)
+
+
+def test_bottom_right_equals_prefix_plus_causal_merge():
+    """Chunked prefill decomposition (page "FlashAttention backend for MLA prefill": context chunk
+    non-causal with LSE, new tokens causal): the bottom-right causal result over [prefix | new]
+    equals the LSE merge of (new tokens vs prefix, unmasked) and (new tokens vs themselves, causal)."""
+    sq, prefix = 11, 23
+    c = make_dense("t", [sq], [prefix + sq], heads=2, causal=True, seed=13, dqk=32, dv=16)
+    full_o, full_l = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True)
+    o1, l1 = O.dense_mla_prefill(c.q, c.k[:prefix], c.v[:prefix], [0, sq], [0, prefix], c.scale, False)
+    o2, l2 = O.dense_mla_prefill(c.q, c.k[prefix:], c.v[prefix:], [0, sq], [0, sq], c.scale, True)
+    mo, ml = O.combine_partials(np.stack([o1.reshape(-1, 16), o2.reshape(-1, 16)]),
+                                np.stack([l1.reshape(-1), l2.reshape(-1)]))
+    np.testing.assert_allclose(mo.reshape(full_o.shape), full_o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ml.reshape(full_l.shape), full_l, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- closed forms
+def test_identical_keys_give_mean_of_visible_values():
+    rng = np.random.default_rng(0)
+    sq = sk = 6
+    q = rng.standard_normal((sq, 1, 8))
+    kvec = rng.standard_normal(8)
+    k = np.tile(kvec, (sk, 1))[:, None, :]
+    v = rng.standard_normal((sk, 1, 5))
+    scale = 0.3
+    o, lse = O.dense_mla_prefill(q, k, v, [0, sq], [0, sk], scale, True)
+    for i in range(sq):
+        n = i + 1
+        np.testing.assert_allclose(o[i, 0], v[:n, 0].mean(axis=0), atol=1e-12)
+        np.testing.assert_allclose(lse[i, 0], math.log(n) + scale * q[i, 0] @ kvec, atol=1e-12)
+
+
+def test_identical_keys_with_sink_closed_form():
+    rng = np.random.default_rng(1)
+    n = 5
+    q = rng.standard_normal((1, 1, 4))
+    kvec = rng.standard_normal(4)
+    k = np.tile(kvec, (n, 1))[:, None, :]
+    v = rng.standard_normal((n, 1, 3))
+    scale, sigma = 0.7, 1.3
+    a = scale * float(q[0, 0] @ kvec)
+    o, lse = O.dense_mla_prefill(q, k, v, [0, 1], [0, n], scale, False, sink=np.array([sigma]))
+    z = n * math.exp(a) + math.exp(sigma)
+    np.testing.assert_allclose(o[0, 0], n * math.exp(a) / z * v[:, 0].mean(axis=0), atol=1e-12)
+    np.testing.assert_allclose(lse[0, 0], math.log(z), atol=1e-12)
+
+
+def test_single_visible_key():
+    c = make_dense("t", [4], [4], heads=2, causal=True, seed=14, dqk=16, dv=8)
+    q, k, v = (O.widen_bf16(x) for x in (c.q, c.k, c.v))
+    o, lse = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True)
+    for h in range(2):
+        np.testing.assert_array_equal(o[0, h], v[0, h])
+        np.testing.assert_allclose(lse[0, h], c.scale * q[0, h] @ k[0, h], atol=1e-12)
+
+
+def test_sparse_all_padded():
+    c = make_sparse("t", 3, 4, 50, 8, seed=15, pad_p=0.0, with_sink=True, dqk=40)
+    idx = -np.ones_like(c.indices)
+    o, lse = O.sparse_mla_prefill(c.q, c.kv, idx, c.scale, dv=32, sink=c.sink)
+    assert np.all(o == 0)
+    np.testing.assert_array_equal(lse, np.tile(c.sink.astype(np.float64), (3, 1)))
+    o, lse = O.sparse_mla_prefill(c.q, c.kv, idx, c.scale, dv=32, sink=None)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
+# ---------------------------------------------------------------- invariants
+def test_rows_sum_to_one_including_sink():
+    c = make_sparse("t", 4, 3, 64, 16, seed=16, pad_p=0.2, with_sink=True, dqk=24)
+    kv = O.widen_bf16(c.kv)
+    kv[:, :8] = 1.0  # value columns all ones: O = total softmax mass on keys
+    o, lse = O.sparse_mla_prefill(c.q, kv, c.indices, c.scale, dv=8, sink=c.sink)
+    p_sink = np.exp(c.sink[None, :].astype(np.float64) - lse)
+    np.testing.assert_allclose(o[..., 0] + p_sink, 1.0, atol=1e-12)
+
+
+def test_padded_slot_contributes_nothing():
+    c = make_sparse("t", 3, 2, 40, 10, seed=17, pad_p=0.0, with_sink=False, dqk=16)
+    idx = c.indices.copy()
+    idx[:, 3] = -1
+    o1, l1 = O.sparse_mla_prefill(c.q, c.kv, idx, c.scale, dv=12)
+    o2, l2 = O.sparse_mla_prefill(c.q, c.kv, np.delete(idx, 3, axis=1), c.scale, dv=12)
+    idx_oob = idx.copy()
+    idx_oob[:, 3] = 40  # out of range is skipped like -1 (reading R8)
+    o3, l3 = O.sparse_mla_prefill(c.q, c.kv, idx_oob, c.scale, dv=12)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+    np.testing.assert_allclose(o1, o3, atol=1e-13)
+
+
+def test_sparse_slot_permutation_invariance():
+    c = make_sparse("t", 3, 2, 40, 10, seed=18, pad_p=0.3, with_sink=True, dqk=16)
+    perm = np.random.default_rng(3).permutation(10)
+    o1, l1 = O.sparse_mla_prefill(c.q, c.kv, c.indices, c.scale, dv=12, sink=c.sink)
+    o2, l2 = O.sparse_mla_prefill(c.q, c.kv, c.indices[:, perm], c.scale, dv=12, sink=c.sink)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+
+
+def test_key_shift_and_scale_transfer():
+    c = make_dense("t", [5, 8], [5, 8], heads=2, causal=True, seed=19, dqk=16, dv=8)
+    q, k, v = (O.widen_bf16(x) for x in (c.q, c.k, c.v))
+    o, lse = O.dense_mla_prefill(q, k, v, c.cu_q, c.cu_k, c.scale, True)
+    shift = np.random.default_rng(4).standard_normal(16)
+    o2, lse2 = O.dense_mla_prefill(q, k + shift, v, c.cu_q, c.cu_k, c.scale, True)
+    np.testing.assert_allclose(o2, o, atol=1e-12)
+    np.testing.assert_allclose(lse2, lse + c.scale * (q @ shift), atol=1e-12)
+    o3, lse3 = O.dense_mla_prefill(2.5 * q, k, v, c.cu_q, c.cu_k, c.scale / 2.5, True)
+    np.testing.assert_allclose(o3, o, atol=1e-12)
+    np.testing.assert_allclose(lse3, lse, atol=1e-12)
+
+
+def test_sink_to_minus_infinity_is_no_sink():
+    c = make_dense("t", [6], [6], heads=2, causal=True, seed=20, dqk=16, dv=8)
+    o1, l1 = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True)
+    o2, l2 = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True,
+                                 sink=np.array([-np.inf, -1e300]))
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, atol=1e-12)
+
+
+def test_zero_padded_value_columns():
+    """Zero-padding V to the q/k width, as the vLLM backend does for kernels that need equal head
+    dims (page "FlashAttention backend for MLA prefill", ``_flash_attn_varlen_diff_headdims``),
+    leaves the first Dv output columns unchanged and makes the pad columns zero."""
+    c = make_dense("t", [7], [7], heads=2, causal=True, seed=21, dqk=16, dv=8)
+    v = O.widen_bf16(c.v)
+    vpad = np.concatenate([v, np.zeros((7, 2, 8))], axis=2)
+    o1, _ = O.dense_mla_prefill(c.q, c.k, v, c.cu_q, c.cu_k, c.scale, True)
+    o2, _ = O.dense_mla_prefill(c.q, c.k, vpad, c.cu_q, c.cu_k, c.scale, True)
+    np.testing.assert_array_equal(o2[..., :8], o1)
+    assert np.all(o2[..., 8:] == 0)
+
+
+# ---------------------------------------------------------------- sparse vs dense, brute force
+def test_sparse_with_all_causal_indices_equals_dense():
+    """Indices [0..p_t] for every token reproduce dense causal attention with the latent row used as
+    K for every head and its first dv columns as V (page "SparseFlashMla": K~ = V~)."""
+    t, h, n, d, dv = 5, 3, 9, 24, 16
+    c = make_sparse("t", t, h, n, n, seed=22, pad_p=0.0, with_sink=True, dqk=d)
+    idx = -np.ones((t, n), dtype=np.int32)
+    for ti in range(t):
+        p = n - t + ti
+        idx[ti, : p + 1] = np.random.default_rng(ti).permutation(p + 1)
+    o_s, l_s = O.sparse_mla_prefill(c.q, c.kv, idx, c.scale, dv=dv, sink=c.sink)
+    kv = O.widen_bf16(c.kv)
+    k = np.repeat(kv[:, None, :], h, axis=1)
+    v = np.repeat(kv[:, None, :dv], h, axis=1)
+    o_d, l_d = O.dense_mla_prefill(c.q, k, v, [0, t], [0, n], c.scale, True, sink=c.sink)
+    np.testing.assert_allclose(o_s, o_d, atol=1e-12)
+    np.testing.assert_allclose(l_s, l_d, atol=1e-12)
+
+
+def test_sparse_brute_force_with_topk_length_and_duplicates():
+    """Pure-Python loops with math.exp, no max shift, on a tiny case with duplicate indices, -1
+    slots, out-of-range slots and a topk_length that cuts valid slots (readings R8, R9)."""
+    from scipy.special import softmax, logsumexp
+    rng = np.random.default_rng(5)
+    t, h, n, d, dv, topk = 3, 2, 7, 6, 4, 6
+    q = rng.standard_normal((t, h, d)) * 0.5
+    kv = rng.standard_normal((n, d)) * 0.5
+    idx = np.array([[2, 2, -1, 5, 0, 9], [1, -1, -1, 3, 3, 3], [6, 4, 0, 1, 2, 5]], dtype=np.int32)
+    tl = np.array([6, 5, 3], dtype=np.int32)
+    sink = np.array([0.25, -0.5])
+    scale = 0.8
+    o, lse = O.sparse_mla_prefill(q, kv, idx, scale, dv=dv, topk_length=tl, sink=sink)
+    for ti in range(t):
+        for hi in range(h):
+            logits, vals = [], []
+            for s in range(tl[ti]):
+                j = int(idx[ti, s])
+                if 0 <= j < n:
+                    logits.append(scale * sum(q[ti, hi, x] * kv[j, x] for x in range(d)))
+                    vals.append(kv[j, :dv])
+            z = sum(math.exp(a) for a in logits) + math.exp(sink[hi])
+            want = sum(math.exp(a) * vv for a, vv in zip(logits, vals)) / z
+            np.testing.assert_allclose(o[ti, hi], want, atol=1e-12)
+            np.testing.assert_allclose(lse[ti, hi], math.log(z), atol=1e-12)
+            # library cross-check of the same row
+            lg = np.array(logits + [sink[hi]])
+            np.testing.assert_allclose(lse[ti, hi], logsumexp(lg), atol=1e-12)
+            np.testing.assert_allclose(o[ti, hi], softmax(lg)[:-1] @ np.array(vals), atol=1e-12)
+
+
+# ---------------------------------------------------------------- combine
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_combine_of_disjoint_key_splits_equals_unsplit(with_sink):
+    t, h, n, d, dv = 4, 3, 30, 16, 8
+    c = make_sparse("t", t, h, n, 20, seed=23, pad_p=0.1, with_sink=with_sink, dqk=d)
+    full_o, full_l = O.sparse_mla_prefill(c.q, c.kv, c.indices, c.scale, dv=dv, sink=c.sink)
+    cuts = [0, 3, 4, 11, 20]   # includes a 1-slot split
+    parts_o, parts_l = [], []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        po, pl = O.sparse_mla_prefill(c.q, c.kv, c.indices[:, a:b], c.scale, dv=dv)
+        parts_o.append(po.reshape(-1, dv))
+        parts_l.append(pl.reshape(-1))
+    sink_rows = None if c.sink is None else np.tile(c.sink.astype(np.float64), t)
+    mo, ml = O.combine_partials(np.stack(parts_o), np.stack(parts_l), sink=sink_rows)
+    np.testing.assert_allclose(mo.reshape(full_o.shape), full_o, atol=1e-12)
+    np.testing.assert_allclose(ml.reshape(full_l.shape), full_l, atol=1e-12)
+
+
+def test_combine_all_empty_partials():
+    o, l = O.combine_partials(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf))
+    assert np.all(o == 0) and np.all(np.isneginf(l))
+    o, l = O.combine_partials(np.zeros((3, 2, 4)), np.full((3, 2), -np.inf), sink=np.array([0.5, -2.0]))
+    assert np.all(o == 0)
+    np.testing.assert_array_equal(l, [0.5, -2.0])
+
+
+# ---------------------------------------------------------------- rows helper, inputs
+def test_rows_helper_matches_full():
+    c = make_dense("t", [9, 20, 3], [15, 20, 3], heads=4, causal=True, seed=24, dqk=16, dv=8,
+                   with_sink=True)
+    o, lse = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True, sink=c.sink)
+    toks, heads = [0, 8, 9, 28, 31], [0, 3]
+    ro, rl = O.dense_mla_prefill_rows(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, True, toks, heads,
+                                      sink=c.sink)
+    np.testing.assert_allclose(ro, o[np.ix_(toks, heads)], atol=1e-13)
+    np.testing.assert_allclose(rl, lse[np.ix_(toks, heads)], atol=1e-13)
+
+
+def test_bf16_rounding_is_round_to_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.0e38], dtype=np.float32)
+    bits = f32_to_bf16_bits(x)
+    back = bf16_bits_to_f32(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins (1.0).
+    np.testing.assert_array_equal(back[:4], np.array([1.0, 1.0, 1.0 + 2**-6, -2.5], dtype=np.float32))
+    np.testing.assert_array_equal(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), bits)

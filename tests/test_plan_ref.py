@@ -1,0 +1,60 @@
+"""Pins for the CPU reference planner (the plan-byte specification the GPU planner must match).
+
+The item extents are checked by brute force against the explicit visibility mask of the oracle's
+reading of the causal rule, and the ordering and coverage against their definitions.
+"""
+import numpy as np
+import pytest
+
+from oracle import plan_ref
+from oracle.mla_oracle import dense_visible
+from workloads import cu_from_lens
+
+
+def _brute_kv_end(sq, sk, m, bm, causal):
+    rows = np.arange(m * bm, min((m + 1) * bm, sq))
+    vis = dense_visible(sq, sk, causal, rows=rows)
+    cols = np.nonzero(vis.any(axis=0))[0]
+    return 0 if cols.size == 0 else int(cols.max()) + 1
+
+
+@pytest.mark.parametrize("lens_q,lens_k,causal,bm,bn", [
+    ([128], [128], True, 128, 64),
+    ([1726, 583, 280, 656, 885, 1680, 959, 246], None, True, 128, 64),
+    ([2048] * 4, [16384, 12345, 8191, 4097], True, 128, 64),
+    ([0, 5, 129, 1, 300], [7, 0, 129, 4096, 100], True, 64, 32),
+    ([0, 5, 129, 1, 300], [7, 0, 129, 4096, 100], False, 256, 64),
+    ([1, 129, 1, 129], [128, 512, 8192, 4096], True, 128, 128),
+])
+def test_plan_items_cover_and_order(lens_q, lens_k, causal, bm, bn):
+    lens_k = lens_q if lens_k is None else lens_k
+    cu_q, cu_k = cu_from_lens(lens_q), cu_from_lens(lens_k)
+    max_q = max(lens_q)
+    items = plan_ref.plan_items(cu_q, cu_k, max_q, bm, bn, causal)
+    want = {(b, m) for b, sq in enumerate(lens_q) for m in range(-(-sq // bm))}
+    got = [(it[0], it[1]) for it in items]
+    assert sorted(got) == sorted(want) and len(got) == len(set(got))
+    mt = -(-max_q // bm)
+    for (b, m, nb, kv_end) in items:
+        assert kv_end == _brute_kv_end(lens_q[b], lens_k[b], m, bm, causal)
+        assert nb == -(-kv_end // bn)
+    keys = [(-it[2], it[0] * mt + it[1]) for it in items]
+    assert keys == sorted(keys)
+
+
+def test_plan_buffer_fill_and_capacity():
+    cu = cu_from_lens([3, 200])
+    buf, n = plan_ref.plan_buffer(cu, cu, 200, 64, 64, True, capacity=10)
+    assert n == 5 and buf.shape == (10, 4)
+    assert np.all(buf[n:] == -1)
+    assert buf[0].tolist() == [1, 3, 4, 200]   # the last tile of the long sequence is longest
+    with pytest.raises(ValueError):
+        plan_ref.plan_buffer(cu, cu, 200, 64, 64, True, capacity=4)
+
+
+def test_plan_unsorted_beyond_sort_capacity():
+    lens = [1] * (plan_ref.SORT_CAPACITY + 1)
+    lens[-1] = 1
+    cu = cu_from_lens(lens)
+    items = plan_ref.plan_items(cu, cu, 1, 64, 64, True)
+    assert [it[0] for it in items] == list(range(len(lens)))
