@@ -1,0 +1,200 @@
+/*
+ * mla_prefill.h -- C ABI of the MI355X (gfx950) MLA prefill library (libmla_prefill.so).
+ *
+ * Multi-head Latent Attention prefill, forward only:
+ *   O = softmax(Q K^T * softmax_scale + mask) V, with an optional float32 log-sum-exp (LSE).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every tensor pointer is caller-owned DEVICE memory on the current HIP device. The library
+ *    never allocates or frees memory in these calls and keeps no pointer after a call returns.
+ *  - Calls only enqueue work on `hip_stream` (a hipStream_t; NULL = the default stream) and
+ *    never synchronise; the caller keeps every buffer alive until the stream has consumed it.
+ *    Device-side faults surface at the caller's next synchronisation.
+ *  - bf16 tensors are row-major with a contiguous last dimension. Strides are in ELEMENTS,
+ *    must be multiples of 8 (16 bytes) and non-negative; base pointers must be 16-byte aligned.
+ *  - LSE is the natural-log log-sum-exp of the *scaled* logits, float32. A row that sees no key
+ *    gets O = 0 and LSE = -inf (LSE = sink when a sink is given).
+ *  - `sink` (nullable) is one float32 logit per head, used as-is (not scaled) as an extra key
+ *    whose value vector is zero.
+ *  - Errors are returned as mla_status_t; nothing is launched when a call returns an error.
+ *    Per-element contents (cu_seqlens values, index values) are not validated: out-of-range
+ *    sparse indices are skipped, which is memory-safe; malformed cu_seqlens are the caller's bug.
+ *  - `out`/`lse` must not alias any input or the workspace.
+ */
+#ifndef MLA_PREFILL_H
+#define MLA_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,  /* null required pointer, bad size, bad stride, bad num_splits     */
+  MLA_ERR_UNSUPPORTED = 2,  /* head dims, head count, top-k or device outside what is built    */
+  MLA_ERR_ALIGNMENT = 3,    /* base pointer not 16-byte aligned or stride not a multiple of 8  */
+  MLA_ERR_WORKSPACE = 4,    /* workspace missing or smaller than the *_workspace_size result   */
+  MLA_ERR_HIP = 5           /* a HIP runtime call or kernel launch failed                      */
+} mla_status_t;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* mla_status_string(int status);
+
+/* Library ABI version (increments on any signature change). */
+int32_t mla_abi_version(void);
+
+/* Query-tile rows (BM) and key-block size (BN) the dense kernel is built with; the plan uses
+ * the same values. */
+void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n);
+
+/* ------------------------------------------------------------------------------------------
+ * Varlen tile plan (GPU kernel, no host synchronisation).
+ *
+ * Prior art: a GPU kernel that plans a batch of varying-length sequences through a fixed-size
+ * buffer, and a helper that zeroes its length counters (page "Mojo module mla",
+ * mla_prefill_plan / mla_prefill_plan_kernel / set_buffer_lengths_to_zero); a separate metadata
+ * call producing the fixed-size int32 task split of the attention operator (page
+ * "SparseFlashMla", Description and Constraints, SparseFlashMlaMetadata / metadata).
+ *
+ * Slots are (b, m) for b < batch and m < Mt = ceil(max_seqlen_q / block_m); slot (b, m) is an
+ * item iff m * block_m < Sq_b. Each item is four int32 words (b, m, n_blocks, kv_end): kv_end is
+ * the count of leading keys any row of the tile may see (Sk_b when causal == 0, else the
+ * bottom-right causal bound clamp(i_last + Sk_b - Sq_b + 1, 0, Sk_b) with i_last the tile's last
+ * row) and n_blocks = ceil(kv_end / block_n). Items are ordered by n_blocks descending, then by
+ * slot (b * Mt + m) ascending; with more than 16384 slots they stay in slot order. Words of
+ * unused items up to plan_capacity are set to -1.
+ *
+ *   cu_seqlens_q, cu_seqlens_k : device int32 [batch + 1], non-decreasing, starting at 0.
+ *   plan                       : device int32 [plan_capacity * 4], written.
+ *   num_items                  : device int32 [1], written.
+ * Errors: INVALID_ARG for null pointers, batch < 0, max_seqlen_q < 0, block sizes that are not
+ * powers of two in [16, 1024], or plan_capacity < batch * Mt.
+ * ------------------------------------------------------------------------------------------ */
+mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t batch, int32_t max_seqlen_q, int32_t block_m,
+                              int32_t block_n, int32_t causal, int32_t* plan,
+                              int32_t plan_capacity, int32_t* num_items, void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Dense varlen MLA prefill.
+ *
+ * The vLLM MLA prefill backend expands K/V to every query head and calls a varlen attention
+ * kernel with q/k head 192 (128 nope + 64 rope), v head 128, int32 cu_seqlens [B+1], an explicit
+ * softmax scale, causal on for new tokens and off for context chunks, optional LSE and a
+ * caller-owned `out` (page "FlashAttention backend for MLA prefill": dispatch,
+ * _flash_attn_varlen_diff_headdims, run_prefill_new_tokens, run_prefill_context_chunk); the
+ * varlen API's I/O contract and num_splits (0 = heuristic, 1 = no split) follow page
+ * "Sgl project Sglang FA4 Interface" (Signature, I/O Contract).
+ *
+ *   q   : bf16 [total_q, H, 192], strides (q_stride_tok, q_stride_head)
+ *   k   : bf16 [total_k, H, 192], strides (k_stride_tok, k_stride_head)
+ *   v   : bf16 [total_k, H, 128], strides (v_stride_tok, v_stride_head); V may be a strided view
+ *         (e.g. token stride H*256, head stride 256 inside a packed K/V buffer)
+ *   cu_seqlens_q/k : device int32 [batch + 1]; sequence b owns query rows [cu_q[b], cu_q[b+1])
+ *         and key rows [cu_k[b], cu_k[b+1]); max_seqlen_q/k bound every Sq_b / Sk_b.
+ *   causal : 0 = no mask; 1 = bottom-right aligned causal (key j visible to query i iff
+ *         j <= i + Sk_b - Sq_b), which is the usual causal mask when Sq_b == Sk_b.
+ *   num_splits : 0 = library heuristic, 1 = no split, n in [2, 64] = split each row's keys into n
+ *         parts merged by the combine kernel (results agree within rounding, not bitwise).
+ *   sink : nullable float32 [H].
+ *   out  : bf16 [total_q, H, 128], strides (o_stride_tok, o_stride_head), written.
+ *   lse  : nullable float32 [total_q, H], strides (lse_stride_tok, lse_stride_head), written.
+ *   workspace : device memory of at least mla_prefill_varlen_workspace_size(...) bytes with the
+ *         same batch/total_q/max_seqlen/H/num_splits; scratch only, contents undefined after.
+ * With num_splits == 1 a sequence's result does not depend on the other sequences in the batch,
+ * and repeated calls are bitwise identical.
+ * Errors: INVALID_ARG (null q/k/v/cu/out, sizes <= 0 where a count is required, strides smaller
+ * than the row they hold, num_splits outside [0, 64]); UNSUPPORTED (head dims other than
+ * 192/128, H > 65535, max_seqlen_k beyond 2^24); ALIGNMENT; WORKSPACE; HIP.
+ * ------------------------------------------------------------------------------------------ */
+size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                         int32_t max_seqlen_k, int32_t num_heads,
+                                         int32_t head_dim_v, int32_t causal, int32_t num_splits);
+
+mla_status_t mla_prefill_varlen(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* The number of key splits mla_prefill_varlen uses for these arguments (resolves num_splits=0). */
+int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int32_t num_heads, int32_t causal, int32_t num_splits);
+
+/* ------------------------------------------------------------------------------------------
+ * Sparse top-k MLA prefill over one shared latent KV (absorbed MLA, KV_N = 1).
+ *
+ * Formula O = softmax(Q K~^T * softmax_scale) V~ with K~ = V~ the gathered rows; int32 indices
+ * with -1 marking an invalid/padded slot; optional topk_length (valid, left-aligned prefix of
+ * each index row, in [0, topk]); optional float sinks; nullable LSE (page "SparseFlashMla",
+ * Description: formula; Parameters table; Constraints). Indices are physical pool rows, already
+ * remapped by the caller (page "mla_prefill_branch_sparse_fp8", description of d_indices).
+ * The 576-column rows hold 512 latent columns then 64 rope columns; V is the first 512 columns.
+ *
+ *   q       : bf16 [num_tokens, H, 576], strides (q_stride_tok, q_stride_head)
+ *   kv      : bf16 [n_kv, 576], row stride kv_stride_row
+ *   indices : int32 [num_tokens, topk], row stride idx_stride_tok (>= topk). Slot s of token t
+ *             takes part iff s < topk_length[t] (when given) and 0 <= indices[t][s] < n_kv.
+ *             Each slot counts once, so a repeated index counts once per slot.
+ *   topk_length : nullable int32 [num_tokens]
+ *   sink    : nullable float32 [H]
+ *   out     : bf16 [num_tokens, H, 512], strides (o_stride_tok, o_stride_head), written.
+ *   lse     : nullable float32 [num_tokens, H], strides (lse_stride_tok, lse_stride_head).
+ *   workspace : may be NULL when mla_prefill_sparse_workspace_size(...) returns 0.
+ * Errors: INVALID_ARG; UNSUPPORTED (head dims other than 576/512, H outside [1, 128], topk
+ * outside [1, 8192]); ALIGNMENT; WORKSPACE; HIP.
+ * ------------------------------------------------------------------------------------------ */
+size_t mla_prefill_sparse_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,
+                                         int32_t head_dim_v);
+
+mla_status_t mla_prefill_sparse(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* kv, int64_t kv_stride_row, int64_t n_kv,
+    const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
+    const int32_t* topk_length,
+    int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Combine S partial results of disjoint key sets into the final result (split-KV reduction;
+ * also merges a context-chunk result with a new-token result through their LSEs).
+ *
+ * Prior art: per-partition partial outputs reduced into the final result (page "Mojo module
+ * mla", mla_splitk_reduce; page "Sgl project Sglang FA4 Interface", Description: split-KV with a
+ * combine kernel); the LSE-returning context-chunk call exists to allow this merge (page
+ * "FlashAttention backend for MLA prefill", run_prefill_context_chunk).
+ *
+ *   o_part   : float32 [num_splits, num_rows, head_dim_v] contiguous, each partial normalised
+ *   lse_part : float32 [num_splits, num_rows] contiguous; -inf marks an empty partial
+ *   num_rows = num_tokens * num_heads with row r = t * num_heads + h
+ *   sink     : nullable float32 [num_heads], merged as one more partial with a zero value
+ *   out      : bf16 [num_tokens, num_heads, head_dim_v], strides (o_stride_tok, o_stride_head)
+ *   lse      : nullable float32 [num_tokens, num_heads], strides (lse_stride_tok, lse_stride_head)
+ * LSE = log(sum_s exp(LSE_s) [+ exp(sink)]); O = sum_s exp(LSE_s - LSE) O_s.
+ * Errors: INVALID_ARG (nulls, num_splits outside [1, 256], head_dim_v not a multiple of 8 or
+ * above 1024); ALIGNMENT; HIP.
+ * ------------------------------------------------------------------------------------------ */
+mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num_splits,
+                         int32_t num_tokens, int32_t num_heads, int32_t head_dim_v,
+                         const float* sink, void* out, int64_t o_stride_tok,
+                         int64_t o_stride_head, float* lse, int64_t lse_stride_tok,
+                         int64_t lse_stride_head, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_PREFILL_H */

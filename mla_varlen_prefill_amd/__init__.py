@@ -1,0 +1,235 @@
+"""MI355X (gfx950) MLA prefill: thin Python binding over the C ABI of libmla_prefill.so.
+
+Every step of the computation runs in the HIP kernels behind the C ABI (see ``include/mla_prefill.h``).
+This module only marshals arguments: it takes PyTorch tensors (device memory and the current
+stream are PyTorch's), checks shapes/dtypes, allocates outputs and the workspace with PyTorch,
+and passes raw pointers. There is no fallback: if the library is missing or the device is not a
+gfx950 GPU, every call raises.
+
+Entry points (same names as the C ABI):
+  mla_prefill_varlen  dense varlen prefill, q/k 192 = 128 nope + 64 rope, v 128, causal or not
+  mla_prefill_sparse  sparse top-k prefill over one shared 576-wide latent KV (v = first 512)
+  mla_combine         merge split partial results through their LSEs
+  mla_prefill_plan    the varlen tile plan (test hook for the bit-exact plan checks)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG_DIR, "libmla_prefill.so")
+
+MLA_OK = 0
+STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
+                3: "MLA_ERR_ALIGNMENT", 4: "MLA_ERR_WORKSPACE", 5: "MLA_ERR_HIP"}
+
+EXPORTED_SYMBOLS = (
+    "mla_status_string", "mla_abi_version", "mla_dense_tile_shape", "mla_prefill_plan",
+    "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_num_splits",
+    "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_combine",
+)
+
+_c_i32, _c_i64, _c_f32, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS_NAMES.get(status, status)}")
+        self.status = status
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmla_prefill.so (built in-tree by ``mla_varlen_prefill_amd._build``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m mla_varlen_prefill_amd._build`")
+    lib = ctypes.CDLL(path)
+    lib.mla_status_string.restype = ctypes.c_char_p
+    lib.mla_status_string.argtypes = [ctypes.c_int]
+    lib.mla_abi_version.restype = _c_i32
+    lib.mla_dense_tile_shape.restype = None
+    lib.mla_dense_tile_shape.argtypes = [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]
+    lib.mla_prefill_plan.restype = ctypes.c_int
+    lib.mla_prefill_plan.argtypes = [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_i32, _vp, _vp]
+    lib.mla_prefill_varlen_workspace_size.restype = _c_sz
+    lib.mla_prefill_varlen_workspace_size.argtypes = [_c_i32] * 8
+    lib.mla_prefill_varlen_num_splits.restype = _c_i32
+    lib.mla_prefill_varlen_num_splits.argtypes = [_c_i32] * 6
+    lib.mla_prefill_varlen.restype = ctypes.c_int
+    lib.mla_prefill_varlen.argtypes = [
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+        _c_f32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_sz, _vp]
+    lib.mla_prefill_sparse_workspace_size.restype = _c_sz
+    lib.mla_prefill_sparse_workspace_size.argtypes = [_c_i32] * 4
+    lib.mla_prefill_sparse.restype = ctypes.c_int
+    lib.mla_prefill_sparse.argtypes = [
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i32, _vp,
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64,
+        _vp, _c_sz, _vp]
+    lib.mla_combine.restype = ctypes.c_int
+    lib.mla_combine.argtypes = [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64,
+                                _vp, _c_i64, _c_i64, _vp]
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != MLA_OK:
+        raise MLAError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _require_cuda(*ts) -> None:
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def dense_tile_shape() -> Tuple[int, int]:
+    lib = load_library()
+    bm, bn = _c_i32(), _c_i32()
+    lib.mla_dense_tile_shape(ctypes.byref(bm), ctypes.byref(bn))
+    return bm.value, bn.value
+
+
+def mla_prefill_plan(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
+                     causal: bool, block_m: Optional[int] = None, block_n: Optional[int] = None,
+                     capacity: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Run the GPU planner; returns (plan int32 [capacity, 4], num_items int32 [1])."""
+    lib = load_library()
+    _require_cuda(cu_seqlens_q, cu_seqlens_k)
+    bm0, bn0 = dense_tile_shape()
+    bm = bm0 if block_m is None else block_m
+    bn = bn0 if block_n is None else block_n
+    batch = cu_seqlens_q.numel() - 1
+    mt = -(-max_seqlen_q // bm) if max_seqlen_q > 0 else 0
+    cap = batch * mt if capacity is None else capacity
+    plan = torch.empty((max(cap, 1), 4), dtype=torch.int32, device=cu_seqlens_q.device)
+    n = torch.empty(1, dtype=torch.int32, device=cu_seqlens_q.device)
+    _check("mla_prefill_plan", lib.mla_prefill_plan(
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, max_seqlen_q, bm, bn, int(bool(causal)),
+        _ptr(plan), cap, _ptr(n), _stream()))
+    return plan[:cap], n
+
+
+def varlen_workspace_bytes(batch: int, total_q: int, max_seqlen_q: int, max_seqlen_k: int,
+                           num_heads: int, causal: bool, num_splits: int) -> int:
+    return load_library().mla_prefill_varlen_workspace_size(
+        batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, 128, int(bool(causal)), num_splits)
+
+
+def varlen_num_splits(batch: int, max_seqlen_q: int, max_seqlen_k: int, num_heads: int,
+                      causal: bool, num_splits: int = 0) -> int:
+    return load_library().mla_prefill_varlen_num_splits(batch, max_seqlen_q, max_seqlen_k, num_heads,
+                                                        int(bool(causal)), num_splits)
+
+
+def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                       cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                       max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                       causal: bool = True, num_splits: int = 0,
+                       sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       return_lse: bool = True, lse: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """Dense varlen MLA prefill. q [Tq,H,192], k [Tk,H,192], v [Tk,H,128] bf16 (last dim
+    contiguous; V may be strided); cu_seqlens int32 [B+1]. Returns out [Tq,H,128] bf16 and, when
+    ``return_lse``, lse float32 [Tq,H]."""
+    lib = load_library()
+    _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, sink, out, lse, workspace)
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be a bf16 [tokens, heads, dim] tensor with a contiguous last dim")
+    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
+        raise ValueError("cu_seqlens must be int32")
+    total_q, heads, dqk = q.shape
+    dv = v.shape[2]
+    batch = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, heads, dv), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, heads), dtype=torch.float32, device=q.device)
+    ws_bytes = lib.mla_prefill_varlen_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k,
+                                                     heads, dv, int(bool(causal)), num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if sink is not None and (sink.dtype != torch.float32 or not sink.is_contiguous()):
+        raise ValueError("sink must be a contiguous float32 [H] tensor")
+    _check("mla_prefill_varlen", lib.mla_prefill_varlen(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+        _ptr(v), v.stride(0), v.stride(1), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+        batch, total_q, max_seqlen_q, max_seqlen_k, heads, dqk, dv,
+        float(softmax_scale), int(bool(causal)), num_splits, _ptr(sink),
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def mla_prefill_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
+                       softmax_scale: float, topk_length: Optional[torch.Tensor] = None,
+                       sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                       return_lse: bool = True, lse: Optional[torch.Tensor] = None, dv: int = 512):
+    """Sparse top-k MLA prefill. q [T,H,576] bf16, kv [N,576] bf16, indices int32 [T, topk]
+    (physical rows, -1 = padded). Returns out [T,H,512] bf16 (and lse float32 [T,H])."""
+    lib = load_library()
+    _require_cuda(q, kv, indices, topk_length, sink, out, lse)
+    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or q.stride(-1) != 1 or kv.stride(-1) != 1:
+        raise ValueError("q and kv must be bf16 with a contiguous last dim")
+    if indices.dtype != torch.int32 or indices.stride(-1) != 1:
+        raise ValueError("indices must be int32 [T, topk] with a contiguous last dim")
+    t, heads, dqk = q.shape
+    topk = indices.shape[1]
+    if out is None:
+        out = torch.empty((t, heads, dv), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((t, heads), dtype=torch.float32, device=q.device)
+    ws_bytes = lib.mla_prefill_sparse_workspace_size(t, heads, topk, dv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check("mla_prefill_sparse", lib.mla_prefill_sparse(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(kv), kv.stride(0), kv.shape[0],
+        _ptr(indices), indices.stride(0), topk, _ptr(topk_length),
+        t, heads, dqk, dv, float(softmax_scale), _ptr(sink),
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
+        _ptr(ws), ws_bytes, _stream()))
+    return (out, lse) if return_lse else out
+
+
+def mla_combine(o_part: torch.Tensor, lse_part: torch.Tensor, num_heads: int,
+                sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                return_lse: bool = True, lse: Optional[torch.Tensor] = None):
+    """Merge partials o_part float32 [S, T*H, Dv] / lse_part float32 [S, T*H] into out bf16
+    [T, H, Dv] (and lse float32 [T, H])."""
+    lib = load_library()
+    _require_cuda(o_part, lse_part, sink, out, lse)
+    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
+        raise ValueError("o_part and lse_part must be contiguous")
+    s, rows, dv = o_part.shape
+    t = rows // num_heads
+    if out is None:
+        out = torch.empty((t, num_heads, dv), dtype=torch.bfloat16, device=o_part.device)
+    if return_lse and lse is None:
+        lse = torch.empty((t, num_heads), dtype=torch.float32, device=o_part.device)
+    _check("mla_combine", lib.mla_combine(
+        _ptr(o_part), _ptr(lse_part), s, t, num_heads, dv, _ptr(sink),
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
+        _stream()))
+    return (out, lse) if return_lse else out

@@ -1,0 +1,357 @@
+// C-ABI host layer of libmla_prefill.so: argument validation, workspace layout, the split-KV
+// heuristic and kernel launches on the caller's stream. No allocation, no synchronisation.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/mla_prefill.h"
+#include "kernels.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+constexpr int kDenseBN = 64;
+constexpr int kDenseDqk = 192;
+constexpr int kDenseDv = 128;
+constexpr int kSparseDqk = 576;
+constexpr int kSparseDv = 512;
+constexpr int kMaxSplits = 64;
+constexpr int kMaxDevices = 64;
+
+struct DeviceInfo {
+  int cus = 0;
+  bool gfx950 = false;
+  bool ok = false;
+};
+
+DeviceInfo g_dev[kMaxDevices];
+std::once_flag g_dev_once[kMaxDevices];
+
+const DeviceInfo* device_info() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_dev_once[dev], [dev]() {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return;
+    g_dev[dev].cus = prop.multiProcessorCount;
+    g_dev[dev].gfx950 = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    g_dev[dev].ok = true;
+  });
+  return g_dev[dev].ok ? &g_dev[dev] : nullptr;
+}
+
+// Query rows per dense work-group: 128 (NQ = 1, two work-groups per CU) or 256 (NQ = 2).
+int dense_nq() {
+  static int nq = []() {
+    const char* e = std::getenv("MLA_DENSE_NQ");
+    return (e != nullptr && std::atoi(e) == 2) ? 2 : 1;
+  }();
+  return nq;
+}
+int dense_bm() { return 128 * dense_nq(); }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+inline bool stride_ok(int64_t s) { return s >= 0 && (s & 7) == 0; }
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct VarlenLayout {
+  int32_t bm, mt, n_slots, splits;
+  size_t off_count, off_plan, off_opart, off_lpart, total;
+};
+
+int32_t resolve_splits(int32_t batch, int32_t max_q, int32_t max_k, int32_t heads,
+                       int32_t num_splits) {
+  if (num_splits >= 1) return num_splits;
+  // Heuristic (our own; the pages name a num_splits_heuristic over M-blocks and SM count): split
+  // the keys only when the (tile, head) work items cannot fill every CU with two resident
+  // work-groups, and keep at least four key blocks per split.
+  const DeviceInfo* di = device_info();
+  const int cus = (di != nullptr && di->cus > 0) ? di->cus : 256;
+  const int64_t conc = (int64_t)cus * (dense_nq() == 1 ? 2 : 1);
+  const int64_t items = (int64_t)batch * cdiv(max_q, dense_bm()) * heads;
+  if (items <= 0 || items >= conc) return 1;
+  const int64_t max_blocks = cdiv(max_k, kDenseBN);
+  int64_t s = cdiv(conc, items);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, max_blocks / 4));
+  s = std::min<int64_t>(s, kMaxSplits);
+  return (int32_t)std::max<int64_t>(1, s);
+}
+
+VarlenLayout varlen_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_t max_k,
+                           int32_t heads, int32_t num_splits) {
+  VarlenLayout L{};
+  L.bm = dense_bm();
+  L.mt = (int32_t)cdiv(std::max(max_q, 0), L.bm);
+  L.n_slots = batch * L.mt;
+  L.splits = resolve_splits(batch, max_q, max_k, heads, num_splits);
+  L.off_count = 0;
+  L.off_plan = 256;
+  size_t off = align256(L.off_plan + (size_t)L.n_slots * 16);
+  L.off_opart = off;
+  L.off_lpart = off;
+  if (L.splits > 1) {
+    L.off_opart = off;
+    off = align256(off + (size_t)L.splits * total_q * heads * kDenseDv * sizeof(float));
+    L.off_lpart = off;
+    off = align256(off + (size_t)L.splits * total_q * heads * sizeof(float));
+  }
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "MLA_OK";
+    case MLA_ERR_INVALID_ARG: return "MLA_ERR_INVALID_ARG";
+    case MLA_ERR_UNSUPPORTED: return "MLA_ERR_UNSUPPORTED";
+    case MLA_ERR_ALIGNMENT: return "MLA_ERR_ALIGNMENT";
+    case MLA_ERR_WORKSPACE: return "MLA_ERR_WORKSPACE";
+    case MLA_ERR_HIP: return "MLA_ERR_HIP";
+    default: return "MLA_ERR_UNKNOWN";
+  }
+}
+
+int32_t mla_abi_version(void) { return kAbiVersion; }
+
+void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n) {
+  if (block_m != nullptr) *block_m = dense_bm();
+  if (block_n != nullptr) *block_n = kDenseBN;
+}
+
+mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                              int32_t batch, int32_t max_seqlen_q, int32_t block_m,
+                              int32_t block_n, int32_t causal, int32_t* plan,
+                              int32_t plan_capacity, int32_t* num_items, void* hip_stream) {
+  if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr || plan == nullptr || num_items == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  auto pow2 = [](int32_t x) { return x >= 16 && x <= 1024 && (x & (x - 1)) == 0; };
+  if (batch < 0 || max_seqlen_q < 0 || !pow2(block_m) || !pow2(block_n) || plan_capacity < 0)
+    return MLA_ERR_INVALID_ARG;
+  const int64_t mt = cdiv(max_seqlen_q, block_m);
+  if ((int64_t)batch * mt > plan_capacity) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(plan)) return MLA_ERR_ALIGNMENT;
+  if (device_info() == nullptr) return MLA_ERR_HIP;
+  mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, (int32_t)mt, block_m, block_n,
+                     causal ? 1 : 0, plan, plan_capacity, num_items};
+  return mla::launch_plan(pp, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                      int32_t num_heads, int32_t causal, int32_t num_splits) {
+  (void)causal;
+  if (num_splits < 0 || num_splits > kMaxSplits) return -1;
+  return resolve_splits(batch, max_seqlen_q, max_seqlen_k, num_heads, num_splits);
+}
+
+size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                         int32_t max_seqlen_k, int32_t num_heads,
+                                         int32_t head_dim_v, int32_t causal, int32_t num_splits) {
+  (void)causal;
+  (void)head_dim_v;
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads <= 0 ||
+      num_splits < 0 || num_splits > kMaxSplits)
+    return 0;
+  return varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits).total;
+}
+
+mla_status_t mla_prefill_varlen(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
+      cu_seqlens_k == nullptr || out == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads <= 0 ||
+      num_splits < 0 || num_splits > kMaxSplits || !std::isfinite(softmax_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (head_dim_qk != kDenseDqk || head_dim_v != kDenseDv || num_heads > 65535 ||
+      max_seqlen_k > (1 << 24))
+    return MLA_ERR_UNSUPPORTED;
+  const int64_t H = num_heads;
+  auto rows_ok = [H](int64_t st, int64_t sh, int64_t width) {
+    return sh >= 0 && st >= 0 && (H == 1 || sh >= width) && st >= (H - 1) * sh + width;
+  };
+  if (!rows_ok(q_stride_tok, q_stride_head, kDenseDqk) || !rows_ok(k_stride_tok, k_stride_head, kDenseDqk) ||
+      !rows_ok(v_stride_tok, v_stride_head, kDenseDv) || !rows_ok(o_stride_tok, o_stride_head, kDenseDv))
+    return MLA_ERR_INVALID_ARG;
+  if (lse != nullptr && (lse_stride_tok < 0 || lse_stride_head < 0)) return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
+      !stride_ok(q_stride_tok) || !stride_ok(q_stride_head) || !stride_ok(k_stride_tok) ||
+      !stride_ok(k_stride_head) || !stride_ok(v_stride_tok) || !stride_ok(v_stride_head) ||
+      !stride_ok(o_stride_tok) || !stride_ok(o_stride_head) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+    return MLA_ERR_ALIGNMENT;
+  if (batch == 0 || total_q == 0) return MLA_OK;
+  const VarlenLayout L = varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits);
+  if ((int64_t)L.n_slots * num_heads * L.splits > INT32_MAX - 8) return MLA_ERR_UNSUPPORTED;
+  if (workspace == nullptr || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  const DeviceInfo* di = device_info();
+  if (di == nullptr) return MLA_ERR_HIP;
+  if (!di->gfx950) return MLA_ERR_UNSUPPORTED;
+
+  hipStream_t stream = (hipStream_t)hip_stream;
+  char* ws = static_cast<char*>(workspace);
+  int32_t* num_items = reinterpret_cast<int32_t*>(ws + L.off_count);
+  int32_t* plan = reinterpret_cast<int32_t*>(ws + L.off_plan);
+
+  mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, L.mt, L.bm, kDenseBN, causal ? 1 : 0,
+                     plan, L.n_slots, num_items};
+  if (mla::launch_plan(pp, stream) != hipSuccess) return MLA_ERR_HIP;
+
+  mla::DenseParams dp{};
+  dp.q = static_cast<const __bf16*>(q); dp.q_st = q_stride_tok; dp.q_sh = q_stride_head;
+  dp.k = static_cast<const __bf16*>(k); dp.k_st = k_stride_tok; dp.k_sh = k_stride_head;
+  dp.v = static_cast<const __bf16*>(v); dp.v_st = v_stride_tok; dp.v_sh = v_stride_head;
+  dp.cu_q = cu_seqlens_q;
+  dp.cu_k = cu_seqlens_k;
+  dp.plan = plan;
+  dp.num_items = num_items;
+  dp.n_slots = L.n_slots;
+  dp.num_heads = num_heads;
+  dp.num_splits = L.splits;
+  dp.causal = causal ? 1 : 0;
+  dp.scale = softmax_scale;
+  dp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  dp.sink = sink;
+  dp.out = static_cast<__bf16*>(out); dp.o_st = o_stride_tok; dp.o_sh = o_stride_head;
+  dp.lse = lse; dp.l_st = lse_stride_tok; dp.l_sh = lse_stride_head;
+  dp.total_q = total_q;
+  if (L.splits > 1) {
+    dp.o_part = reinterpret_cast<float*>(ws + L.off_opart);
+    dp.lse_part = reinterpret_cast<float*>(ws + L.off_lpart);
+  }
+  dp.total_work = L.n_slots * num_heads * L.splits;
+  dp.per_xcd = (dp.total_work + 7) / 8;
+  if (mla::launch_dense_fwd(dp, dense_nq(), stream) != hipSuccess) return MLA_ERR_HIP;
+
+  if (L.splits > 1) {
+    mla::CombineParams cp{};
+    cp.o_part = dp.o_part;
+    cp.lse_part = dp.lse_part;
+    cp.num_splits = L.splits;
+    cp.rows = total_q * num_heads;
+    cp.num_heads = num_heads;
+    cp.dv = kDenseDv;
+    cp.sink = sink;
+    cp.out = dp.out; cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
+    cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
+    if (mla::launch_combine(cp, stream) != hipSuccess) return MLA_ERR_HIP;
+  }
+  return MLA_OK;
+}
+
+size_t mla_prefill_sparse_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,
+                                         int32_t head_dim_v) {
+  (void)num_tokens;
+  (void)num_heads;
+  (void)topk;
+  (void)head_dim_v;
+  return 0;
+}
+
+mla_status_t mla_prefill_sparse(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* kv, int64_t kv_stride_row, int64_t n_kv,
+    const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
+    const int32_t* topk_length,
+    int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (q == nullptr || kv == nullptr || indices == nullptr || out == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (num_tokens < 0 || num_heads <= 0 || n_kv < 0 || topk <= 0 || !std::isfinite(softmax_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (head_dim_qk != kSparseDqk || head_dim_v != kSparseDv || num_heads > 128 || topk > 8192 ||
+      n_kv > INT32_MAX)
+    return MLA_ERR_UNSUPPORTED;
+  const int64_t H = num_heads;
+  if (idx_stride_tok < topk || kv_stride_row < kSparseDqk || q_stride_head < 0 || o_stride_head < 0 ||
+      (H > 1 && (q_stride_head < kSparseDqk || o_stride_head < kSparseDv)) ||
+      q_stride_tok < (H - 1) * q_stride_head + kSparseDqk ||
+      o_stride_tok < (H - 1) * o_stride_head + kSparseDv ||
+      (lse != nullptr && (lse_stride_tok < 0 || lse_stride_head < 0)))
+    return MLA_ERR_INVALID_ARG;
+  if (!aligned16(q) || !aligned16(kv) || !aligned16(out) || !stride_ok(q_stride_tok) ||
+      !stride_ok(q_stride_head) || !stride_ok(kv_stride_row) || !stride_ok(o_stride_tok) ||
+      !stride_ok(o_stride_head) || (reinterpret_cast<uintptr_t>(indices) & 3u) != 0 ||
+      (topk_length != nullptr && (reinterpret_cast<uintptr_t>(topk_length) & 3u) != 0) ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+    return MLA_ERR_ALIGNMENT;
+  if (num_tokens == 0) return MLA_OK;
+  const DeviceInfo* di = device_info();
+  if (di == nullptr) return MLA_ERR_HIP;
+  if (!di->gfx950) return MLA_ERR_UNSUPPORTED;
+
+  mla::SparseParams sp{};
+  sp.q = static_cast<const __bf16*>(q); sp.q_st = q_stride_tok; sp.q_sh = q_stride_head;
+  sp.kv = static_cast<const __bf16*>(kv); sp.kv_st = kv_stride_row; sp.n_kv = n_kv;
+  sp.idx = indices; sp.idx_st = idx_stride_tok; sp.topk = topk;
+  sp.topk_length = topk_length;
+  sp.num_tokens = num_tokens;
+  sp.num_heads = num_heads;
+  sp.scale = softmax_scale;
+  sp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  sp.sink = sink;
+  sp.out = static_cast<__bf16*>(out); sp.o_st = o_stride_tok; sp.o_sh = o_stride_head;
+  sp.lse = lse; sp.l_st = lse_stride_tok; sp.l_sh = lse_stride_head;
+  return mla::launch_sparse_fwd(sp, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num_splits,
+                         int32_t num_tokens, int32_t num_heads, int32_t head_dim_v,
+                         const float* sink, void* out, int64_t o_stride_tok,
+                         int64_t o_stride_head, float* lse, int64_t lse_stride_tok,
+                         int64_t lse_stride_head, void* hip_stream) {
+  if (o_part == nullptr || lse_part == nullptr || out == nullptr) return MLA_ERR_INVALID_ARG;
+  if (num_splits < 1 || num_splits > 256 || num_tokens < 0 || num_heads <= 0 || head_dim_v <= 0 ||
+      (head_dim_v & 7) != 0 || head_dim_v > 1024)
+    return MLA_ERR_INVALID_ARG;
+  const int64_t H = num_heads;
+  if (o_stride_head < 0 || (H > 1 && o_stride_head < head_dim_v) ||
+      o_stride_tok < (H - 1) * o_stride_head + head_dim_v ||
+      (lse != nullptr && (lse_stride_tok < 0 || lse_stride_head < 0)))
+    return MLA_ERR_INVALID_ARG;
+  if ((int64_t)num_tokens * num_heads > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(o_part) || !aligned16(out) || !stride_ok(o_stride_tok) || !stride_ok(o_stride_head) ||
+      (reinterpret_cast<uintptr_t>(lse_part) & 3u) != 0 ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+    return MLA_ERR_ALIGNMENT;
+  if (num_tokens == 0) return MLA_OK;
+  if (device_info() == nullptr) return MLA_ERR_HIP;
+  mla::CombineParams cp{};
+  cp.o_part = o_part;
+  cp.lse_part = lse_part;
+  cp.num_splits = num_splits;
+  cp.rows = num_tokens * num_heads;
+  cp.num_heads = num_heads;
+  cp.dv = head_dim_v;
+  cp.sink = sink;
+  cp.out = static_cast<__bf16*>(out); cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
+  cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
+  return mla::launch_combine(cp, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,76 @@
+// Internal launch interface between the C-ABI host layer and the HIP kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+constexpr int kPlanSortCapacity = 16384;  // slots sorted longest-first; beyond: slot order
+constexpr int kPlanMaxBlocks = 0x3FFFE;   // largest n_blocks the sort key can hold
+
+struct PlanParams {
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int32_t batch;
+  int32_t mt;        // query tiles per sequence slot = ceil(max_seqlen_q / bm)
+  int32_t bm, bn;
+  int32_t causal;
+  int32_t* plan;     // [capacity][4]
+  int32_t capacity;
+  int32_t* num_items;
+};
+
+struct DenseParams {
+  const __bf16* q; int64_t q_st, q_sh;
+  const __bf16* k; int64_t k_st, k_sh;
+  const __bf16* v; int64_t v_st, v_sh;
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  const int32_t* plan;
+  const int32_t* num_items;
+  int32_t n_slots;       // plan capacity (batch * Mt)
+  int32_t num_heads;
+  int32_t num_splits;
+  int32_t causal;
+  float scale;           // softmax scale
+  float scale_log2;      // softmax scale * log2(e)
+  const float* sink;     // nullable [H]; applied here only when unsplit
+  __bf16* out; int64_t o_st, o_sh;
+  float* lse; int64_t l_st, l_sh;
+  float* o_part;         // split mode: [S][total_q][H][128] fp32, else null
+  float* lse_part;       // split mode: [S][total_q][H]
+  int32_t total_q;
+  int32_t per_xcd;       // ceil(total_work / 8)
+  int32_t total_work;    // n_slots * H * S
+};
+
+struct SparseParams {
+  const __bf16* q; int64_t q_st, q_sh;
+  const __bf16* kv; int64_t kv_st; int64_t n_kv;
+  const int32_t* idx; int64_t idx_st; int32_t topk;
+  const int32_t* topk_length;
+  int32_t num_tokens, num_heads;
+  float scale, scale_log2;
+  const float* sink;
+  __bf16* out; int64_t o_st, o_sh;
+  float* lse; int64_t l_st, l_sh;
+};
+
+struct CombineParams {
+  const float* o_part;
+  const float* lse_part;
+  int32_t num_splits;
+  int32_t rows;          // tokens * heads
+  int32_t num_heads;
+  int32_t dv;
+  const float* sink;
+  __bf16* out; int64_t o_st, o_sh;
+  float* lse; int64_t l_st, l_sh;
+};
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+hipError_t launch_dense_fwd(const DenseParams& p, int nq, hipStream_t stream);
+hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+
+}  // namespace mla

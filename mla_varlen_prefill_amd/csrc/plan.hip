@@ -1,0 +1,133 @@
+// Varlen tile planner: one work-group turns cu_seqlens into the ordered list of query-tile work
+// items the dense kernel consumes, on the device (no host synchronisation, capturable).
+//
+// Prior art: a GPU kernel that plans varying-length sequences through a fixed-size buffer and a
+// helper that zeroes its counters (page "Mojo module mla", mla_prefill_plan_kernel,
+// set_buffer_lengths_to_zero); a metadata call producing a fixed-size int32 task split before
+// the attention call (page "SparseFlashMla", Description). The format is this library's own:
+// items (b, m, n_blocks, kv_end), longest first (n_blocks descending, then slot ascending),
+// unused entries -1. Longest-first dispatch keeps causal and varlen batches load-balanced.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+struct Item {
+  int b, m, nb, kv_end;
+  bool valid;
+};
+
+__device__ __forceinline__ Item slot_item(const PlanParams& p, int s) {
+  Item it;
+  it.b = s / p.mt;
+  it.m = s - it.b * p.mt;
+  const int sq = p.cu_q[it.b + 1] - p.cu_q[it.b];
+  const int sk = p.cu_k[it.b + 1] - p.cu_k[it.b];
+  it.valid = it.m * p.bm < sq;
+  int kv_end = sk;
+  if (p.causal) {
+    const int i_last = min((it.m + 1) * p.bm, sq) - 1;
+    kv_end = min(max(i_last + sk - sq + 1, 0), sk);
+  }
+  it.kv_end = kv_end;
+  it.nb = (kv_end + p.bn - 1) / p.bn;
+  return it;
+}
+
+__device__ __forceinline__ void write_item(int32_t* plan, int i, const Item& it) {
+  reinterpret_cast<int4*>(plan)[i] = make_int4(it.b, it.m, it.nb, it.kv_end);
+}
+
+}  // namespace
+
+__global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
+  __shared__ uint32_t keys[kPlanSortCapacity];
+  __shared__ int wave_tot[16];
+  __shared__ int count_sh;
+  const int tid = threadIdx.x;
+  const int n_slots = p.batch * p.mt;
+
+  if (n_slots <= kPlanSortCapacity) {
+    int P = 1;
+    while (P < n_slots) P <<= 1;
+    for (int s = tid; s < P; s += 1024) {
+      uint32_t key = 0xFFFFFFFFu;
+      if (s < n_slots) {
+        const Item it = slot_item(p, s);
+        if (it.valid) {
+          const uint32_t nb = (uint32_t)min(it.nb, kPlanMaxBlocks);
+          key = ((uint32_t)(kPlanMaxBlocks - nb) << 14) | (uint32_t)s;
+        }
+      }
+      keys[s] = key;
+    }
+    if (tid == 0) count_sh = 0;
+    __syncthreads();
+    // bitonic sort, ascending: longest first, ties by slot; invalid (all ones) last
+    for (int k = 2; k <= P; k <<= 1) {
+      for (int j = k >> 1; j > 0; j >>= 1) {
+        for (int i = tid; i < P; i += 1024) {
+          const int ixj = i ^ j;
+          if (ixj > i) {
+            const uint32_t a = keys[i], c = keys[ixj];
+            const bool up = (i & k) == 0;
+            if ((a > c) == up) {
+              keys[i] = c;
+              keys[ixj] = a;
+            }
+          }
+        }
+        __syncthreads();
+      }
+    }
+    for (int i = tid; i < P; i += 1024) {
+      const bool v = keys[i] != 0xFFFFFFFFu;
+      const bool next_v = (i + 1 < P) && keys[i + 1] != 0xFFFFFFFFu;
+      if (v && !next_v) count_sh = i + 1;  // the single last valid entry
+    }
+    __syncthreads();
+    const int count = count_sh;
+    for (int i = tid; i < p.capacity; i += 1024) {
+      if (i < count) {
+        write_item(p.plan, i, slot_item(p, (int)(keys[i] & 0x3FFFu)));
+      } else {
+        reinterpret_cast<int4*>(p.plan)[i] = make_int4(-1, -1, -1, -1);
+      }
+    }
+    if (tid == 0) *p.num_items = count;
+  } else {
+    // Too many slots to sort in LDS: compact the items in slot order.
+    const int lane = tid & 63, wave = tid >> 6;
+    int base = 0;
+    for (int s0 = 0; s0 < n_slots; s0 += 1024) {
+      const int s = s0 + tid;
+      Item it;
+      it.valid = false;
+      if (s < n_slots) it = slot_item(p, s);
+      const uint64_t mask = __ballot(it.valid);
+      const int pre = __popcll(mask & ((1ull << lane) - 1ull));
+      if (lane == 0) wave_tot[wave] = __popcll(mask);
+      __syncthreads();
+      int off = base, tot = 0;
+      for (int wv = 0; wv < 16; ++wv) {
+        if (wv < wave) off += wave_tot[wv];
+        tot += wave_tot[wv];
+      }
+      if (it.valid) write_item(p.plan, off + pre, it);
+      base += tot;
+      __syncthreads();
+    }
+    for (int i = base + tid; i < p.capacity; i += 1024)
+      reinterpret_cast<int4*>(p.plan)[i] = make_int4(-1, -1, -1, -1);
+    if (tid == 0) *p.num_items = base;
+  }
+}
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,123 @@
+"""CPU checks of the C ABI: the library loads, exports every function include/mla_prefill.h
+declares, and rejects bad arguments with the documented status codes before touching a GPU
+(no compute call is made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import mla_varlen_prefill_amd as mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_prefill.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(mla.LIB_PATH), reason="libmla_prefill.so not built")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_every_declared_symbol_is_exported():
+    lib = mla.load_library()
+    declared = _declared_functions()
+    assert set(declared) == set(mla.EXPORTED_SYMBOLS)
+    for name in declared:
+        assert hasattr(lib, name), name
+
+
+def test_status_strings_and_version():
+    lib = mla.load_library()
+    for code, name in mla.STATUS_NAMES.items():
+        assert lib.mla_status_string(code).decode() == name
+    assert lib.mla_abi_version() == 1
+    bm, bn = mla.dense_tile_shape()
+    assert bm in (128, 256) and bn == 64
+
+
+P = 0x10000  # a 16-byte aligned fake device address; never dereferenced by these calls
+
+
+def _varlen(lib, **kw):
+    a = dict(q=P, qst=128 * 192, qsh=192, k=P, kst=128 * 192, ksh=192, v=P, vst=128 * 128, vsh=128,
+             cuq=P, cuk=P, batch=1, total_q=16, max_q=16, max_k=16, heads=128, dqk=192, dv=128,
+             scale=0.07, causal=1, splits=1, sink=None, out=P, ost=128 * 128, osh=128, lse=None,
+             lst=128, lsh=1, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.mla_prefill_varlen(a["q"], a["qst"], a["qsh"], a["k"], a["kst"], a["ksh"], a["v"],
+                                  a["vst"], a["vsh"], a["cuq"], a["cuk"], a["batch"], a["total_q"],
+                                  a["max_q"], a["max_k"], a["heads"], a["dqk"], a["dv"], a["scale"],
+                                  a["causal"], a["splits"], a["sink"], a["out"], a["ost"], a["osh"],
+                                  a["lse"], a["lst"], a["lsh"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_varlen_argument_errors():
+    lib = mla.load_library()
+    assert _varlen(lib, q=None) == 1
+    assert _varlen(lib, out=None) == 1
+    assert _varlen(lib, heads=0) == 1
+    assert _varlen(lib, splits=-1) == 1
+    assert _varlen(lib, splits=65) == 1
+    assert _varlen(lib, scale=float("nan")) == 1
+    assert _varlen(lib, qsh=100) == 1                      # head stride smaller than the row
+    assert _varlen(lib, dqk=128) == 2                      # only 192/128 is built
+    assert _varlen(lib, dv=192) == 2
+    assert _varlen(lib, max_k=(1 << 24) + 1) == 2
+    assert _varlen(lib, q=P + 8) == 3                      # misaligned base
+    assert _varlen(lib, vst=128 * 128 + 4) == 3            # stride not a multiple of 8
+    assert _varlen(lib, ws=None) == 4
+    assert _varlen(lib, ws_bytes=64) == 4
+    assert _varlen(lib, batch=0) == 0                      # nothing to do, nothing launched
+    # vLLM-style strided V view (token stride H*256, head stride 256) passes validation up to the
+    # workspace check
+    assert _varlen(lib, vst=128 * 256, vsh=256, ws_bytes=64) == 4
+
+
+def test_workspace_size_grows_with_splits():
+    lib = mla.load_library()
+    w1 = lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 128, 1, 1)
+    w4 = lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 128, 1, 4)
+    assert w1 > 0 and w4 >= w1 + 4 * 300 * 8 * 128 * 4
+    assert lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 128, 1, 99) == 0
+
+
+def _sparse(lib, **kw):
+    a = dict(q=P, qst=128 * 576, qsh=576, kv=P, kvst=576, nkv=1000, idx=P, idxst=64, topk=64,
+             tl=None, t=4, heads=128, dqk=576, dv=512, scale=0.04, sink=None, out=P,
+             ost=128 * 512, osh=512, lse=None, lst=128, lsh=1, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.mla_prefill_sparse(a["q"], a["qst"], a["qsh"], a["kv"], a["kvst"], a["nkv"], a["idx"],
+                                  a["idxst"], a["topk"], a["tl"], a["t"], a["heads"], a["dqk"], a["dv"],
+                                  a["scale"], a["sink"], a["out"], a["ost"], a["osh"], a["lse"],
+                                  a["lst"], a["lsh"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_sparse_argument_errors():
+    lib = mla.load_library()
+    assert lib.mla_prefill_sparse_workspace_size(4096, 128, 2048, 512) == 0
+    assert _sparse(lib, kv=None) == 1
+    assert _sparse(lib, topk=0) == 1
+    assert _sparse(lib, idxst=32) == 1
+    assert _sparse(lib, heads=129) == 2
+    assert _sparse(lib, topk=8193, idxst=8193) == 2
+    assert _sparse(lib, dqk=512) == 2
+    assert _sparse(lib, kv=P + 4) == 3
+    assert _sparse(lib, idx=P + 2) == 3
+    assert _sparse(lib, t=0) == 0
+
+
+def test_combine_and_plan_argument_errors():
+    lib = mla.load_library()
+    args = [P, P, 2, 4, 8, 128, None, P, 8 * 128, 128, None, 8, 1, None]
+    bad = list(args); bad[2] = 0
+    assert lib.mla_combine(*bad) == 1
+    bad = list(args); bad[5] = 100
+    assert lib.mla_combine(*bad) == 1
+    bad = list(args); bad[0] = P + 4
+    assert lib.mla_combine(*bad) == 3
+    assert lib.mla_prefill_plan(P, P, 2, 300, 100, 64, 1, P, 100, P, None) == 1   # block_m not a power of 2
+    assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, P, 5, P, None) == 1     # capacity < 2*3
+    assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, P + 4, 6, P, None) == 3

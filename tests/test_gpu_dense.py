@@ -1,0 +1,177 @@
+"""GPU parity of the dense varlen MLA prefill (HIP path through the C ABI) against the fp64 oracle."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import mla_oracle as O
+from workloads import (make_dense, dense_small, dense_varlen, device_dense, bf16_tensor_to_bits,
+                       cu_from_lens, CHUNKED_SK)
+from tests.gpu_util import announce, dev_bf16, dev, host_f64, check_parity
+
+pytestmark = pytest.mark.gpu
+
+
+def run_case(c, num_splits=1, strided_v=False, return_lse=True):
+    import torch
+    import mla_varlen_prefill_amd as mla
+    q, k = dev_bf16(c.q), dev_bf16(c.k)
+    if strided_v:
+        # vLLM layout: V is a view into a packed [T, H, 128 nope + 128 v] buffer
+        tk, h, dv = c.v.shape
+        packed = torch.zeros((tk, h, 256), dtype=torch.bfloat16, device="cuda")
+        packed[:, :, 128:] = dev_bf16(c.v)
+        packed[:, :, :128] = 7.0
+        v = packed[:, :, 128:]
+        assert v.stride() == (h * 256, 256, 1)
+    else:
+        v = dev_bf16(c.v)
+    sink = dev(c.sink) if c.sink is not None else None
+    res = mla.mla_prefill_varlen(q, k, v, dev(c.cu_q), dev(c.cu_k), c.max_q, c.max_k, c.scale,
+                                 causal=c.causal, num_splits=num_splits, sink=sink, return_lse=return_lse)
+    torch.cuda.synchronize()
+    if return_lse:
+        return host_f64(res[0]), host_f64(res[1])
+    return host_f64(res), None
+
+
+def oracle(c, heads=None):
+    return O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, c.causal, sink=c.sink, heads=heads)
+
+
+def test_dense_small_config():
+    c = dense_small()
+    announce(f"dense {c.name}")
+    o, lse = run_case(c)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
+PROBES = [(1, 128), (129, 512), (1, 4096), (129, 4096), (129, 8192), (257, 300), (64, 64)]
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("sq,sk", PROBES)
+def test_dense_probe_shapes(sq, sk, causal):
+    c = make_dense(f"probe_{sq}x{sk}_c{int(causal)}", [sq], [sk], heads=2, causal=causal, seed=31)
+    announce(f"dense {c.name}")
+    o, lse = run_case(c)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_ragged_batch_with_sink(causal):
+    lens_q = [0, 5, 129, 1, 300, 64, 200]
+    lens_k = [7, 0, 129, 4096, 100, 64, 700]
+    c = make_dense(f"ragged_c{int(causal)}", lens_q, lens_k, heads=3, causal=causal, seed=32,
+                   with_sink=True)
+    announce(f"dense {c.name}")
+    o, lse = run_case(c)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
+def test_dense_more_queries_than_keys_bottom_right():
+    c = make_dense("sq_gt_sk", [300, 70], [100, 70], heads=2, causal=True, seed=33)
+    announce(f"dense {c.name}")
+    o, lse = run_case(c)
+    ro, rl = oracle(c)
+    assert np.isneginf(rl[:200]).all()
+    check_parity(o, lse, ro, rl, c.name)
+
+
+def test_dense_strided_v_and_no_lse():
+    c = make_dense("strided_v", [333, 90], [333, 90], heads=4, causal=True, seed=34)
+    announce(f"dense {c.name}")
+    o, _ = run_case(c, strided_v=True, return_lse=False)
+    ro, rl = oracle(c)
+    check_parity(o, None, ro, rl, c.name)
+
+
+@pytest.mark.parametrize("splits", [2, 3, 8])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_forced_splits(splits, causal):
+    c = make_dense(f"split{splits}_c{int(causal)}", [1000, 37], [1000, 1500], heads=4, causal=causal,
+                   seed=35, with_sink=True)
+    announce(f"dense {c.name}")
+    o, lse = run_case(c, num_splits=splits)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
+def test_dense_auto_splits_small_grid():
+    import mla_varlen_prefill_amd as mla
+    c = make_dense("auto_split", [4096], [4096], heads=2, causal=True, seed=36)
+    s = mla.varlen_num_splits(1, 4096, 4096, 2, True, 0)
+    assert s > 1
+    announce(f"dense {c.name} splits={s}")
+    o, lse = run_case(c, num_splits=0)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
+def test_dense_varlen_config_sampled_heads():
+    c = dense_varlen()
+    announce(f"dense {c.name} lens={c.meta['lens']}")
+    o, lse = run_case(c, num_splits=0)
+    heads = [0, 37, 90, 127]
+    ro, rl = oracle(c, heads=heads)
+    check_parity(o[:, heads], lse[:, heads], ro[:, heads], rl[:, heads], c.name)
+
+
+def test_dense_deterministic_and_batch_invariant():
+    import torch
+    import mla_varlen_prefill_amd as mla
+    lens = [700, 129, 1500]
+    c = make_dense("invariance", lens, lens, heads=8, causal=True, seed=37)
+    announce(f"dense {c.name}")
+    o1, l1 = run_case(c)
+    o2, l2 = run_case(c)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+    # the middle sequence alone gives the same bits as inside the batch
+    a, b = int(c.cu_q[1]), int(c.cu_q[2])
+    alone = make_dense("alone", [129], [129], heads=8, causal=True, seed=37)
+    alone.q, alone.k, alone.v = c.q[a:b], c.k[a:b], c.v[a:b]
+    o3, l3 = run_case(alone)
+    assert np.array_equal(o3, o1[a:b]) and np.array_equal(l3, l1[a:b])
+
+
+def _full_size_sampled(lens_q, lens_k, heads, seed, tokens, sample_heads, num_splits):
+    """Run a full-size case on the device and check sampled (token, head) rows against the oracle."""
+    import torch
+    import mla_varlen_prefill_amd as mla
+    q, k, v, cu_q, cu_k = device_dense(lens_q, lens_k, heads, seed)
+    scale = 192 ** -0.5
+    out, lse = mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max(lens_q), max(lens_k), scale,
+                                      causal=True, num_splits=num_splits)
+    torch.cuda.synchronize()
+    hs = list(sample_heads)
+    qb = bf16_tensor_to_bits(q[tokens][:, hs])
+    kb = bf16_tensor_to_bits(k[:, hs])
+    vb = bf16_tensor_to_bits(v[:, hs])
+    # oracle over the sampled tokens (their own sequences' keys), re-indexed to the sampled heads
+    cq = cu_from_lens(lens_q)
+    qfull = np.zeros((int(cq[-1]), len(hs), 192), dtype=np.uint16)
+    qfull[tokens] = qb
+    ro, rl = O.dense_mla_prefill_rows(qfull, kb, vb, cq, cu_from_lens(lens_k), float(np.float32(scale)),
+                                      True, tokens, list(range(len(hs))))
+    og = host_f64(out[tokens][:, hs])
+    lg = host_f64(lse[tokens][:, hs])
+    check_parity(og, lg, ro, rl, f"full-size {lens_q[:2]}.. splits={num_splits}")
+    del q, k, v, out, lse
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("num_splits", [0, 2, 4])
+def test_dense_long_context_sampled(num_splits):
+    announce(f"dense long 1x32768 h128 splits={num_splits}")
+    tokens = [0, 1, 127, 128, 4095, 16000, 32766, 32767]
+    _full_size_sampled([32768], [32768], 128, 3, tokens, [0, 5, 77, 127], num_splits)
+
+
+def test_dense_chunked_prefill_sampled():
+    announce("dense chunked b4 q2048")
+    cq = cu_from_lens([2048] * 4)
+    tokens = [0, 2047, 2048, 3000, 4096, 6143, 6144, 8191]
+    _full_size_sampled([2048] * 4, list(CHUNKED_SK), 128, 4, tokens, [1, 64, 126], 0)

@@ -204,3 +204,50 @@ def sparse_topk(seed: int = 5, num_tokens: int = 4096, heads: int = 128, n_kv: i
                 topk: int = 2048) -> SparseCase:
     """4096 query tokens x 128 heads over a 65536-row latent pool, top-k 2048, ~5% -1, fp32 sink."""
     return make_sparse(f"sparse_t{num_tokens}_h{heads}_k{topk}", num_tokens, heads, n_kv, topk, seed)
+
+
+# --------------------------------------------------------------------------------------------
+# On-device generation for the full-size workloads (hundreds of millions of values). Same value
+# distribution (N(0,1) rounded to bf16 by round-to-nearest-even), drawn by a seeded PyTorch
+# generator on the GPU; the oracle receives copies of exactly the rows it evaluates.
+# --------------------------------------------------------------------------------------------
+def device_randn_bf16(shape, seed: int, stream: int, device="cuda"):
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed) * 1000003 + int(stream))
+    out = torch.empty(tuple(shape), dtype=torch.bfloat16, device=device)
+    flat = out.view(-1)
+    chunk = 1 << 27
+    for s in range(0, flat.numel(), chunk):
+        e = min(flat.numel(), s + chunk)
+        flat[s:e] = torch.randn(e - s, generator=g, dtype=torch.float32, device=device).to(torch.bfloat16)
+    return out
+
+
+def device_dense(lens_q, lens_k, heads: int, seed: int, device="cuda",
+                 dqk: int = DQK_DENSE, dv: int = DV_DENSE):
+    """Full-size dense inputs on the device: (q, k, v, cu_q, cu_k) as torch tensors."""
+    import torch
+    cu_q, cu_k = cu_from_lens(lens_q), cu_from_lens(lens_k)
+    q = device_randn_bf16((int(cu_q[-1]), heads, dqk), seed, STREAM_Q, device)
+    k = device_randn_bf16((int(cu_k[-1]), heads, dqk), seed, STREAM_K, device)
+    v = device_randn_bf16((int(cu_k[-1]), heads, dv), seed, STREAM_V, device)
+    return q, k, v, torch.from_numpy(cu_q).to(device), torch.from_numpy(cu_k).to(device)
+
+
+def device_sparse(num_tokens: int, heads: int, n_kv: int, topk: int, seed: int, pad_p: float = 0.05,
+                  device="cuda", dqk: int = DQK_SPARSE):
+    """Full-size sparse inputs: q/kv drawn on the device, indices from ``sparse_indices`` (host,
+    numpy, seeded) copied over, sink float32 [H]. Returns (q, kv, idx, sink, idx_host)."""
+    import torch
+    q = device_randn_bf16((num_tokens, heads, dqk), seed, STREAM_Q, device)
+    kv = device_randn_bf16((n_kv, dqk), seed, STREAM_K, device)
+    idx_host = sparse_indices(seed, num_tokens, n_kv, topk, pad_p)
+    sink = np.random.default_rng([seed, STREAM_SINK]).standard_normal(heads, dtype=np.float32)
+    return q, kv, torch.from_numpy(idx_host).to(device), torch.from_numpy(sink).to(device), idx_host
+
+
+def bf16_tensor_to_bits(t) -> np.ndarray:
+    """Copy a torch bf16 tensor to the host as uint16 bit patterns (for the oracle)."""
+    import torch
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
