@@ -1,0 +1,320 @@
+#!/usr/bin/env python3
+"""MLA prefill throughput on one MI355X (gfx950), through the C ABI of libmla_prefill.so.
+
+One step = one full dense varlen MLA prefill call over the headline batch: the GPU tile planner,
+the dense attention kernel and (when the split heuristic splits the keys) the combine kernel.
+The headline batch is 8 sequences with lengths uniform in [64, 2048] (seeded), 128 heads, q/k
+head 192 (128 nope + 64 rope), v head 128, bf16, causal, LSE on.
+
+Printed: ONE JSON line with the throughput in TFLOP/s of algorithmic work (visible query-key
+pairs x 640 FLOP x heads), the dense kernel's roofline position (its own device time from HIP
+events recorded around each launch on its stream) and the fp64 CPU oracle timed on a bounded
+sample of the same batch. Secondary measurements of the other workloads (long context, chunked
+prefill, sparse top-k, the 128-token case) are included under "secondary" unless
+--no-secondary is given.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MLA prefill TFLOP/s (causal, varlen) + % bf16 MFMA peak on 1 MI355X"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X published dense bf16 matrix peak
+PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
+DQK, DV = 192, 128
+SP_D, SP_DV = 576, 512
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ----------------------------------------------------------------------------- work counting
+def dense_pairs(lens_q, lens_k, causal: bool) -> int:
+    """Visible (query, key) pairs: bottom-right causal, or all pairs."""
+    total = 0
+    for sq, sk in zip(lens_q, lens_k):
+        if not causal:
+            total += sq * sk
+            continue
+        for_all = 0
+        # row i sees min(sk, max(0, i + sk - sq + 1)) keys
+        lo = max(0, sq - sk)                      # rows before this see nothing
+        # rows lo..sq-1 see (i + sk - sq + 1) keys, capped at sk (never exceeds since i < sq)
+        n = sq - lo
+        first = lo + sk - sq + 1
+        for_all = n * first + n * (n - 1) // 2
+        total += for_all
+    return total
+
+
+def dense_flops(lens_q, lens_k, heads, causal) -> float:
+    return float(2 * (DQK + DV) * heads * dense_pairs(lens_q, lens_k, causal))
+
+
+def dense_bytes(lens_q, lens_k, heads, lse=True) -> float:
+    tq, tk = sum(lens_q), sum(lens_k)
+    return float(tq * heads * DQK * 2 + tk * heads * (DQK + DV) * 2 + tq * heads * DV * 2
+                 + (tq * heads * 4 if lse else 0))
+
+
+def sparse_flops(valid_slots, heads) -> float:
+    return float(2 * (SP_D + SP_DV) * heads * valid_slots)
+
+
+def sparse_bytes(valid_slots, tokens, heads, topk, lse=True) -> float:
+    return float(valid_slots * SP_D * 2 + tokens * heads * SP_D * 2 + tokens * heads * SP_DV * 2
+                 + tokens * topk * 4 + (tokens * heads * 4 if lse else 0))
+
+
+def kernel_source_hash(files=("dense_fwd.hip", "common.h", "kernels.h")) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "mla_varlen_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ----------------------------------------------------------------------------- timing helpers
+def time_steps(step, steps: int, warmup: int, kernel: str):
+    import torch
+    import mla_varlen_prefill_amd as mla
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mla.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k_ms, k_n = mla.profile_read(kernel)
+    mla.profile_enable(False)
+    return (t1 - t0) * 1e3 / steps, (k_ms / k_n if k_n else float("nan")), k_n
+
+
+def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_splits=0):
+    import torch
+    import mla_varlen_prefill_amd as mla
+    from workloads import device_dense
+    q, k, v, cu_q, cu_k = device_dense(lens_q, lens_k, heads, seed)
+    max_q, max_k = max(lens_q), max(lens_k)
+    out = torch.empty((q.shape[0], heads, DV), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((q.shape[0], heads), dtype=torch.float32, device="cuda")
+    ws_bytes = mla.varlen_workspace_bytes(len(lens_q), q.shape[0], max_q, max_k, heads, True, num_splits)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    scale = DQK ** -0.5
+
+    def step():
+        mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal=True,
+                               num_splits=num_splits, out=out, lse=lse, workspace=ws)
+
+    ms, kms, _ = time_steps(step, steps, warmup, "dense")
+    fl = dense_flops(lens_q, lens_k, heads, True)
+    by = dense_bytes(lens_q, lens_k, heads)
+    splits = mla.varlen_num_splits(len(lens_q), max_q, max_k, heads, True, num_splits)
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+    return {"workload": name, "ms_per_call": round(ms, 4), "dense_kernel_ms": round(kms, 4),
+            "splits": splits, "tflops": round(fl / ms / 1e9, 2),
+            "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "kernel_tflops": round(fl / kms / 1e9, 2), "alg_gbps": round(by / ms / 1e6, 1)}
+
+
+def sparse_case(steps, warmup):
+    import torch
+    import mla_varlen_prefill_amd as mla
+    from workloads import device_sparse
+    t, h, n_kv, topk = 4096, 128, 65536, 2048
+    q, kv, idx, sink, idx_host = device_sparse(t, h, n_kv, topk, seed=5)
+    out = torch.empty((t, h, SP_DV), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((t, h), dtype=torch.float32, device="cuda")
+    scale = SP_D ** -0.5
+
+    def step():
+        mla.mla_prefill_sparse(q, kv, idx, scale, sink=sink, out=out, lse=lse)
+
+    ms, kms, _ = time_steps(step, steps, warmup, "sparse")
+    valid = int(((idx_host >= 0) & (idx_host < n_kv)).sum())
+    fl = sparse_flops(valid, h)
+    by = sparse_bytes(valid, t, h, topk)
+    del q, kv, idx, out, lse
+    torch.cuda.empty_cache()
+    return {"workload": "sparse_t4096_h128_topk2048_pool65536", "ms_per_call": round(ms, 4),
+            "sparse_kernel_ms": round(kms, 4), "tflops": round(fl / ms / 1e9, 2),
+            "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+            "alg_gbps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
+            "kernel_alg_gbps": round(by / kms / 1e6, 1)}
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(case, budget_s: float):
+    """The fp64 oracle, as it stands, on heads 0, 1, ... of the headline batch until the budget."""
+    from oracle import mla_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    lens = list(map(int, (case.cu_q[1:] - case.cu_q[:-1])))
+    per_head = dense_flops(lens, lens, 1, True)
+    done = 0
+    t0 = time.perf_counter()
+    while done < case.heads:
+        O.dense_mla_prefill(case.q, case.k, case.v, case.cu_q, case.cu_k, case.scale, True, heads=[done])
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(per_head * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"heads 0..{done - 1} of {case.heads} of the headline batch (all 8 sequences, "
+                      f"all rows), {el:.1f} s wall, fp64 numpy"}
+
+
+# ----------------------------------------------------------------------------- traffic
+def measured_traffic(flops_unused=None):
+    """HBM bytes per dense-kernel launch from the committed rocprofv3 counter summary, if it was
+    taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, "dense_fwd_varlen_b8_h128_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- main
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--only", default=None,
+                    help="run one workload and print its line: dense_varlen, dense_long, dense_chunked, "
+                         "dense_small, sparse, copy (a plain 1 GiB device copy for counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this library has no "
+              "multi-GPU path: run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import mla_varlen_prefill_amd as mla
+    from workloads import dense_varlen
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    mla.load_library()
+
+    if args.only == "copy":
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty(n, dtype=torch.uint8, device="cuda")
+        a.fill_(1)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 3}))
+        return
+
+    if args.only not in (None, "dense_varlen"):
+        sec_runs = {
+            "dense_long": lambda: dense_device_case("dense_long_1x32768_h128", [32768], [32768], 128, 3,
+                                                    args.steps, args.warmup),
+            "dense_chunked": lambda: dense_device_case("dense_chunked_b4_q2048", [2048] * 4,
+                                                       [16384, 12345, 8191, 4097], 128, 4, args.steps,
+                                                       args.warmup),
+            "dense_small": lambda: dense_device_case("dense_small_1x128_h16", [128], [128], 16, 1,
+                                                     args.steps, args.warmup),
+            "sparse": lambda: sparse_case(args.steps, args.warmup),
+        }
+        print(json.dumps(sec_runs[args.only]()), flush=True)
+        return
+
+    # ---------------- headline: dense varlen batch of 8, lengths in [64, 2048], 128 heads
+    case = dense_varlen()
+    lens = list(map(int, (case.cu_q[1:] - case.cu_q[:-1])))
+    heads = case.heads
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
+
+    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
+    cu_q = torch.from_numpy(case.cu_q).cuda()
+    cu_k = torch.from_numpy(case.cu_k).cuda()
+    max_q, max_k = case.max_q, case.max_k
+    out = torch.empty((q.shape[0], heads, DV), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((q.shape[0], heads), dtype=torch.float32, device="cuda")
+    ws_bytes = mla.varlen_workspace_bytes(case.batch, q.shape[0], max_q, max_k, heads, True, 0)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    splits = mla.varlen_num_splits(case.batch, max_q, max_k, heads, True, 0)
+
+    def step():
+        mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max_q, max_k, case.scale, causal=True,
+                               num_splits=0, out=out, lse=lse, workspace=ws)
+
+    ms, dense_kernel_ms, launches = time_steps(step, args.steps, args.warmup, "dense")
+    flops = dense_flops(lens, lens, heads, True)
+    value = flops / (ms / 1e3) / 1e12
+    achieved = flops / (dense_kernel_ms / 1e3) / 1e12
+    traffic = measured_traffic()
+    result = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense_varlen_b8_h128_causal_lse", "batch": case.batch, "seq_lens": lens,
+                   "heads": heads, "head_dim_qk": DQK, "head_dim_v": DV, "causal": True, "lse": True,
+                   "num_splits": splits, "algorithmic_flop_per_step": flops,
+                   "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 3), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "kernel": "dense_fwd_kernel",
+                     "kernel_ms": round(dense_kernel_ms, 5), "launches_timed": launches},
+    }
+    del q, k, v, out, lse, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_secondary:
+        sec = []
+        ss, sw = max(2, min(args.steps, 5)), 2
+        sec.append(dense_device_case("dense_small_1x128_h16", [128], [128], 16, 1, args.steps, args.warmup))
+        sec.append(dense_device_case("dense_long_1x32768_h128", [32768], [32768], 128, 3, ss, sw))
+        sec.append(dense_device_case("dense_chunked_b4_q2048", [2048] * 4, [16384, 12345, 8191, 4097],
+                                     128, 4, ss, sw))
+        sec.append(sparse_case(ss, sw))
+        result["secondary"] = sec
+
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

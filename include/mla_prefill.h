@@ -193,6 +193,19 @@ mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num
                          int64_t o_stride_head, float* lse, int64_t lse_stride_tok,
                          int64_t lse_stride_head, void* hip_stream);
 
+/* ------------------------------------------------------------------------------------------
+ * Measurement aid (not part of the computation). While enabled, every kernel the library
+ * launches is bracketed by a pair of HIP events recorded on the launch stream; reading waits
+ * for the recorded events and accumulates per-kernel launch counts and total device time.
+ * Enabling clears the totals. Events are created on first use and reused; at most 65536
+ * launches are held between two reads (later ones are not timed).
+ *   kernel: MLA_KERNEL_PLAN, MLA_KERNEL_DENSE, MLA_KERNEL_COMBINE or MLA_KERNEL_SPARSE.
+ * Errors: INVALID_ARG (unknown kernel, null outputs); HIP (event calls failed).
+ * ------------------------------------------------------------------------------------------ */
+enum { MLA_KERNEL_PLAN = 0, MLA_KERNEL_DENSE = 1, MLA_KERNEL_COMBINE = 2, MLA_KERNEL_SPARSE = 3 };
+mla_status_t mla_profile_enable(int32_t enable);
+mla_status_t mla_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }
 #endif

@@ -31,7 +31,9 @@ EXPORTED_SYMBOLS = (
     "mla_status_string", "mla_abi_version", "mla_dense_tile_shape", "mla_prefill_plan",
     "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_num_splits",
     "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_combine",
+    "mla_profile_enable", "mla_profile_read",
 )
+KERNEL_IDS = {"plan": 0, "dense": 1, "combine": 2, "sparse": 3}
 
 _c_i32, _c_i64, _c_f32, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -79,6 +81,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_combine.restype = ctypes.c_int
     lib.mla_combine.argtypes = [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64,
                                 _vp, _c_i64, _c_i64, _vp]
+    lib.mla_profile_enable.restype = ctypes.c_int
+    lib.mla_profile_enable.argtypes = [_c_i32]
+    lib.mla_profile_read.restype = ctypes.c_int
+    lib.mla_profile_read.argtypes = [_c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64)]
     _lib = lib
     return lib
 
@@ -233,3 +239,16 @@ def mla_combine(o_part: torch.Tensor, lse_part: torch.Tensor, num_heads: int,
         _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
         _stream()))
     return (out, lse) if return_lse else out
+
+
+def profile_enable(enable: bool = True) -> None:
+    """Bracket every library kernel launch with HIP events on its stream (clears totals)."""
+    _check("mla_profile_enable", load_library().mla_profile_enable(int(bool(enable))))
+
+
+def profile_read(kernel: str) -> Tuple[float, int]:
+    """(total device ms, launches) of one kernel kind since profile_enable(): plan, dense,
+    combine or sparse. Waits for the recorded events."""
+    ms, n = ctypes.c_double(), _c_i64()
+    _check("mla_profile_read", load_library().mla_profile_read(KERNEL_IDS[kernel], ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value

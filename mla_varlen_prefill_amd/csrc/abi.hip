@@ -9,6 +9,8 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <utility>
+#include <vector>
 
 #include "../../include/mla_prefill.h"
 #include "kernels.h"
@@ -44,6 +46,49 @@ const DeviceInfo* device_info() {
     g_dev[dev].ok = true;
   });
   return g_dev[dev].ok ? &g_dev[dev] : nullptr;
+}
+
+// ---- launch timing (measurement aid) ------------------------------------------------------
+constexpr int kNumKernels = 4;
+constexpr size_t kMaxPending = 65536;
+
+struct Profiler {
+  std::mutex mu;
+  std::atomic<bool> enabled{false};
+  struct Rec {
+    int kind;
+    hipEvent_t a, b;
+  };
+  std::vector<Rec> pending;
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> pool;
+  double total_ms[kNumKernels] = {};
+  int64_t count[kNumKernels] = {};
+};
+Profiler g_prof;
+
+// Launch `fn` (which enqueues one kernel on `stream`), bracketed by timing events when enabled.
+template <typename F>
+hipError_t timed_launch(int kind, hipStream_t stream, F&& fn) {
+  if (!g_prof.enabled.load(std::memory_order_relaxed)) return fn();
+  std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
+  {
+    std::lock_guard<std::mutex> lk(g_prof.mu);
+    if (g_prof.pending.size() >= kMaxPending) return fn();
+    if (!g_prof.pool.empty()) {
+      ev = g_prof.pool.back();
+      g_prof.pool.pop_back();
+    }
+  }
+  if (ev.first == nullptr) {
+    if (hipEventCreate(&ev.first) != hipSuccess || hipEventCreate(&ev.second) != hipSuccess) return fn();
+  }
+  if (hipEventRecord(ev.first, stream) != hipSuccess) return fn();
+  const hipError_t e = fn();
+  if (e != hipSuccess) return e;
+  if (hipEventRecord(ev.second, stream) != hipSuccess) return hipErrorUnknown;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  g_prof.pending.push_back({kind, ev.first, ev.second});
+  return hipSuccess;
 }
 
 // Query rows per dense work-group: 128 (NQ = 1, two work-groups per CU) or 256 (NQ = 2).
@@ -144,7 +189,10 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
   if (device_info() == nullptr) return MLA_ERR_HIP;
   mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, (int32_t)mt, block_m, block_n,
                      causal ? 1 : 0, plan, plan_capacity, num_items};
-  return mla::launch_plan(pp, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return timed_launch(MLA_KERNEL_PLAN, (hipStream_t)hip_stream,
+                      [&] { return mla::launch_plan(pp, (hipStream_t)hip_stream); }) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
 }
 
 int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
@@ -215,7 +263,8 @@ mla_status_t mla_prefill_varlen(
 
   mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, L.mt, L.bm, kDenseBN, causal ? 1 : 0,
                      plan, L.n_slots, num_items};
-  if (mla::launch_plan(pp, stream) != hipSuccess) return MLA_ERR_HIP;
+  if (timed_launch(MLA_KERNEL_PLAN, stream, [&] { return mla::launch_plan(pp, stream); }) != hipSuccess)
+    return MLA_ERR_HIP;
 
   mla::DenseParams dp{};
   dp.q = static_cast<const __bf16*>(q); dp.q_st = q_stride_tok; dp.q_sh = q_stride_head;
@@ -241,7 +290,9 @@ mla_status_t mla_prefill_varlen(
   }
   dp.total_work = L.n_slots * num_heads * L.splits;
   dp.per_xcd = (dp.total_work + 7) / 8;
-  if (mla::launch_dense_fwd(dp, dense_nq(), stream) != hipSuccess) return MLA_ERR_HIP;
+  if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, dense_nq(), stream); }) !=
+      hipSuccess)
+    return MLA_ERR_HIP;
 
   if (L.splits > 1) {
     mla::CombineParams cp{};
@@ -254,7 +305,8 @@ mla_status_t mla_prefill_varlen(
     cp.sink = sink;
     cp.out = dp.out; cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
     cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
-    if (mla::launch_combine(cp, stream) != hipSuccess) return MLA_ERR_HIP;
+    if (timed_launch(MLA_KERNEL_COMBINE, stream, [&] { return mla::launch_combine(cp, stream); }) != hipSuccess)
+      return MLA_ERR_HIP;
   }
   return MLA_OK;
 }
@@ -317,7 +369,10 @@ mla_status_t mla_prefill_sparse(
   sp.sink = sink;
   sp.out = static_cast<__bf16*>(out); sp.o_st = o_stride_tok; sp.o_sh = o_stride_head;
   sp.lse = lse; sp.l_st = lse_stride_tok; sp.l_sh = lse_stride_head;
-  return mla::launch_sparse_fwd(sp, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return timed_launch(MLA_KERNEL_SPARSE, (hipStream_t)hip_stream,
+                      [&] { return mla::launch_sparse_fwd(sp, (hipStream_t)hip_stream); }) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
 }
 
 mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num_splits,
@@ -351,7 +406,41 @@ mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num
   cp.sink = sink;
   cp.out = static_cast<__bf16*>(out); cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
   cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
-  return mla::launch_combine(cp, (hipStream_t)hip_stream) == hipSuccess ? MLA_OK : MLA_ERR_HIP;
+  return timed_launch(MLA_KERNEL_COMBINE, (hipStream_t)hip_stream,
+                      [&] { return mla::launch_combine(cp, (hipStream_t)hip_stream); }) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+mla_status_t mla_profile_enable(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  for (int i = 0; i < kNumKernels; ++i) {
+    g_prof.total_ms[i] = 0.0;
+    g_prof.count[i] = 0;
+  }
+  g_prof.enabled.store(enable != 0);
+  return MLA_OK;
+}
+
+mla_status_t mla_profile_read(int32_t kernel, double* total_ms, int64_t* launches) {
+  if (kernel < 0 || kernel >= kNumKernels || total_ms == nullptr || launches == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  std::lock_guard<std::mutex> lk(g_prof.mu);
+  bool ok = true;
+  for (auto& r : g_prof.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) {
+      ok = false;
+    } else {
+      g_prof.total_ms[r.kind] += ms;
+      g_prof.count[r.kind] += 1;
+    }
+    g_prof.pool.push_back({r.a, r.b});
+  }
+  g_prof.pending.clear();
+  *total_ms = g_prof.total_ms[kernel];
+  *launches = g_prof.count[kernel];
+  return ok ? MLA_OK : MLA_ERR_HIP;
 }
 
 }  // extern "C"
