@@ -109,7 +109,8 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
  * and repeated calls are bitwise identical.
  * Errors: INVALID_ARG (null q/k/v/cu/out, sizes <= 0 where a count is required, strides smaller
  * than the row they hold, num_splits outside [0, 64]); UNSUPPORTED (head dims other than
- * 192/128, H > 65535, max_seqlen_k beyond 2^24); ALIGNMENT; WORKSPACE; HIP.
+ * 192/128, H > 65535, max_seqlen_k beyond 2^24, K or V token stride of 2^23 elements or more);
+ * ALIGNMENT; WORKSPACE; HIP.
  * ------------------------------------------------------------------------------------------ */
 size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
                                          int32_t max_seqlen_k, int32_t num_heads,

@@ -101,6 +101,15 @@ int dense_nq() {
 }
 int dense_bm() { return 128 * dense_nq(); }
 
+// XCD-aware work mapping (default on); MLA_XCD_REMAP=0 keeps plain dispatch order.
+bool xcd_remap_enabled() {
+  static bool on = []() {
+    const char* e = std::getenv("MLA_XCD_REMAP");
+    return !(e != nullptr && std::atoi(e) == 0);
+  }();
+  return on;
+}
+
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 inline bool stride_ok(int64_t s) { return s >= 0 && (s & 7) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -231,8 +240,8 @@ mla_status_t mla_prefill_varlen(
       num_splits < 0 || num_splits > kMaxSplits || !std::isfinite(softmax_scale))
     return MLA_ERR_INVALID_ARG;
   if (head_dim_qk != kDenseDqk || head_dim_v != kDenseDv || num_heads > 65535 ||
-      max_seqlen_k > (1 << 24))
-    return MLA_ERR_UNSUPPORTED;
+      max_seqlen_k > (1 << 24) || k_stride_tok >= (1 << 23) || v_stride_tok >= (1 << 23))
+    return MLA_ERR_UNSUPPORTED;  // key-block byte offsets are kept in 31 bits
   const int64_t H = num_heads;
   auto rows_ok = [H](int64_t st, int64_t sh, int64_t width) {
     return sh >= 0 && st >= 0 && (H == 1 || sh >= width) && st >= (H - 1) * sh + width;
@@ -290,6 +299,7 @@ mla_status_t mla_prefill_varlen(
   }
   dp.total_work = L.n_slots * num_heads * L.splits;
   dp.per_xcd = (dp.total_work + 7) / 8;
+  dp.xcd_remap = xcd_remap_enabled() ? 1 : 0;
   if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, dense_nq(), stream); }) !=
       hipSuccess)
     return MLA_ERR_HIP;

@@ -6,7 +6,8 @@
 //                             D (32x32): lane l holds D[8*(i/4) + 4*(l/32) + i%4][l%32], i = 0..15
 //   ds_read_b64_tr_b16        within each 16-lane group, lane i receives element (i%4) of the
 //                             4-element rows addressed by group lanes 4*j + i/4, j = 0..3.
-//   v_permlane32_swap(x, x)   returns (x[l], x[l^32]) in some order in its two results.
+//   v_permlane32_swap(x, x)   returns (x[l], x[l^32]) in some order in its two results;
+//   v_permlane16_swap(x, x)   likewise (x[l], x[l^16]).
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -30,6 +31,9 @@ constexpr float kLn2 = 0.6931471805599453f;
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mfma16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 // max / sum of a value and its partner lane l^32 (both halves end up with the result).
 __device__ __forceinline__ float xhalf_max(float x) {
@@ -40,6 +44,22 @@ __device__ __forceinline__ float xhalf_sum(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
+// max / sum over the four lanes l, l^16, l^32, l^48 (one 16x16 MFMA output column).
+__device__ __forceinline__ float xquad_max(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float xquad_sum(float x) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return xhalf_sum(__uint_as_float(r[0]) + __uint_as_float(r[1]));
+}
+
+// LDS row swizzle: chunk c (16 bytes) of row r is stored at chunk c ^ row_swz(r), with
+// row_swz(r) = 2 * ((r >> 1) & 3) + ((r >> 3) & 1). For a row pitch that is an odd multiple of
+// 128 bytes this keeps two read patterns free of bank conflicts on the 64-bank (256-byte) LDS:
+//   * 16 consecutive rows read at the same chunk (matrix operand reads);
+//   * 8 consecutive rows read at the same 32-byte segment (transposed 16x16 operand reads).
+__device__ __forceinline__ int row_swz(int r) { return 2 * ((r >> 1) & 3) + ((r >> 3) & 1); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 

@@ -20,9 +20,11 @@
 // order with two ds_read_b64_tr_b16 of four consecutive keys each.
 //
 // LDS layout per stage (16-byte chunks, XOR-swizzled so every MFMA operand read is free of bank
-// conflicts while each wave's copy still writes 1 KiB contiguous):
-//   K: 64 rows x 24 chunks (384 B/row); chunk c of row r sits at c ^ (r & 7).
-//   V: 64 rows x 16 chunks (256 B/row); chunk c of row r sits at c ^ ((r & 3) << 1).
+// conflicts on the 64-bank LDS while each wave's copy still writes 1 KiB contiguous):
+//   K: 64 rows x 24 chunks (384 B/row); chunk c of row r sits at c ^ row_swz(r) (16 rows per
+//      operand read hit 16 distinct 16-byte bank groups).
+//   V: 64 rows x 16 chunks (256 B/row); chunk c of row r sits at c ^ ((r & 3) << 2) (the four
+//      rows of a transposed read hit four distinct 64-byte segments).
 #include "common.h"
 #include "kernels.h"
 
@@ -38,51 +40,60 @@ constexpr int V_STAGE_BYTES = BN * DV * 2;    // 16384
 constexpr int K_CHUNKS_PER_WAVE = BN * (DQK / 8) / 256;  // 6 wave-wide 1 KiB copies
 constexpr int V_CHUNKS_PER_WAVE = BN * (DV / 8) / 256;   // 4
 
-struct Stage {
-  char* k;
-  char* v;
-};
+constexpr float kRescaleLog2 = 8.f;  // rescale O only when a row max grows by more than 2^8
 
 template <int NQ>
 struct DenseCtx {
   // per-lane constants
   int lane, wave, l32, hl;
   // problem
-  const __bf16* kbase;   // K of this sequence/head at key 0
-  const __bf16* vbase;
-  int64_t k_st, v_st;
+  const char* kbase;   // K of this sequence/head at key 0 (bytes)
+  const char* vbase;
+  int k_st_b, v_st_b;  // token strides in bytes (validated to keep 64-row offsets in 31 bits)
   int sk, sq, row0;
-  int koff[K_CHUNKS_PER_WAVE];  // element offset of this lane's chunk within a block (row*k_st + c*8)
-  int krow[K_CHUNKS_PER_WAVE];
-  int voff[V_CHUNKS_PER_WAVE];
-  int vrow[V_CHUNKS_PER_WAVE];
+  uint32_t koff[K_CHUNKS_PER_WAVE];  // byte offset of this lane's 16-byte chunk inside a block
+  uint32_t voff[V_CHUNKS_PER_WAVE];
+  int kdst, vdst;                    // this wave's first 1 KiB slot in a stage (bytes)
+  // LDS operand addresses (bytes, relative to a stage)
+  int ka[4];                         // K rows: + g*128 + mt*32*384 per 4-step group g
+  int va[DV / 32];                   // V rows: + (mt*32 + cc*16 [+8]) * 256 per step
 };
 
+// Row of the block that slot i of this lane's K (or V) copies holds.
 template <int NQ>
-__device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, int j, Stage st) {
+__device__ __forceinline__ int k_slot_row(const DenseCtx<NQ>& c, int i) {
+  return ((c.wave * K_CHUNKS_PER_WAVE + i) * 64 + c.lane) / 24;
+}
+template <int NQ>
+__device__ __forceinline__ int v_slot_row(const DenseCtx<NQ>& c, int i) {
+  return ((c.wave * V_CHUNKS_PER_WAVE + i) * 64 + c.lane) >> 4;
+}
+
+template <int NQ>
+__device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, int j, char* kst, char* vst) {
   const int key0 = j * BN;
-  const bool tail = key0 + BN > c.sk;
-  const __bf16* kb = c.kbase + (int64_t)key0 * c.k_st;
-  const __bf16* vb = c.vbase + (int64_t)key0 * c.v_st;
+  const char* kb = c.kbase + (int64_t)key0 * c.k_st_b;
+  const char* vb = c.vbase + (int64_t)key0 * c.v_st_b;
+  if (key0 + BN <= c.sk) {
 #pragma unroll
-  for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) {
-    int off = c.koff[i];
-    if (tail) {
-      int r = c.krow[i];
-      int rr = min(key0 + r, c.sk - 1) - key0;  // clamp to a real row; masked later
-      off += (rr - r) * (int)c.k_st;
-    }
-    g2lds16(kb + off, st.k + (c.wave * K_CHUNKS_PER_WAVE + i) * 1024);
-  }
+    for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) g2lds16(kb + c.koff[i], kst + c.kdst + i * 1024);
 #pragma unroll
-  for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) {
-    int off = c.voff[i];
-    if (tail) {
-      int r = c.vrow[i];
-      int rr = min(key0 + r, c.sk - 1) - key0;
-      off += (rr - r) * (int)c.v_st;
+    for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) g2lds16(vb + c.voff[i], vst + c.vdst + i * 1024);
+  } else {
+    // tail block: rows past the sequence re-read its last key (finite values, masked later)
+    const int last = c.sk - 1 - key0;
+#pragma unroll
+    for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) {
+      const int r = k_slot_row(c, i);
+      const int shift = (min(r, last) - r) * c.k_st_b;
+      g2lds16(kb + (uint32_t)((int)c.koff[i] + shift), kst + c.kdst + i * 1024);
     }
-    g2lds16(vb + off, st.v + (c.wave * V_CHUNKS_PER_WAVE + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) {
+      const int r = v_slot_row(c, i);
+      const int shift = (min(r, last) - r) * c.v_st_b;
+      g2lds16(vb + (uint32_t)((int)c.voff[i] + shift), vst + c.vdst + i * 1024);
+    }
   }
 }
 
@@ -92,20 +103,30 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
                                               float (&m_run)[NQ], float (&l_run)[NQ],
                                               f32x16 (&o)[NQ][DV / 32], float scale_log2,
                                               bool causal) {
-  // ---- S^T = K_blk * Q^T
+  // ---- S^T = K_blk * Q^T: the two 32-key tiles are independent accumulator chains, issued
+  // alternately, with the K fragments read from LDS PF steps ahead of their MFMA.
   f32x16 s[NQ][2];
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt) {
+  for (int nq = 0; nq < NQ; ++nq) s[nq][0] = s[nq][1] = f32x16{};
+  {
+    constexpr int NSTEP = 2 * (DQK / 16);  // 24 (kk, mt) steps
+    constexpr int PF = 4;
+    bf16x8 a[NSTEP];
 #pragma unroll
-    for (int nq = 0; nq < NQ; ++nq) s[nq][mt] = f32x16{};
-    const int row = mt * 32 + c.l32;
-    const char* rbase = ks + row * (DQK * 2);
+    for (int st = 0; st < PF; ++st) {
+      const int kk = st >> 1, mt = st & 1;
+      a[st] = lds_read_b128(ks + c.ka[kk & 3] + (kk >> 2) * 128 + mt * 32 * (DQK * 2));
+    }
 #pragma unroll
-    for (int kk = 0; kk < DQK / 16; ++kk) {
-      const int ch = (kk * 2 + c.hl) ^ (row & 7);
-      bf16x8 a = lds_read_b128(rbase + ch * 16);
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + PF < NSTEP) {
+        const int kk2 = (st + PF) >> 1, mt2 = (st + PF) & 1;
+        a[st + PF] = lds_read_b128(ks + c.ka[kk2 & 3] + (kk2 >> 2) * 128 + mt2 * 32 * (DQK * 2));
+      }
+      const int kk = st >> 1, mt = st & 1;
 #pragma unroll
-      for (int nq = 0; nq < NQ; ++nq) s[nq][mt] = mfma32(a, qf[nq][kk], s[nq][mt]);
+      for (int nq = 0; nq < NQ; ++nq) s[nq][mt] = mfma32(a[st], qf[nq][kk], s[nq][mt]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the read PF steps ahead of its MFMA
     }
   }
   // ---- mask (diagonal and tail blocks only; wave-uniform test)
@@ -117,71 +138,78 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       const int qrow = qmin + nq * 32 + c.l32;
-      const int lim = causal ? min(c.sk - 1, qrow + diag) : (c.sk - 1);
+      const int lim = (causal ? min(c.sk - 1, qrow + diag) : (c.sk - 1)) - key0 - 4 * c.hl;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          const int key = key0 + mt * 32 + 8 * (i >> 2) + 4 * c.hl + (i & 3);
-          if (key > lim) s[nq][mt][i] = -INFINITY;
+          const int kofs = mt * 32 + 8 * (i >> 2) + (i & 3);
+          if (kofs > lim) s[nq][mt][i] = -INFINITY;
         }
     }
   }
-  // ---- online softmax (per lane = per query; halves l and l^32 share a query)
+  // ---- online softmax (per lane = per query; halves l and l^32 share a query), lazy rescale
   bf16x8 pf[NQ][2][2];
+  const float tau_raw = kRescaleLog2 / scale_log2;
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
     float mx = s[nq][0][0];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[nq][mt][i]);
+      for (int i = (mt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[nq][mt][i]);
     mx = xhalf_max(mx);
     const float m_new = fmaxf(m_run[nq], mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2((m_run[nq] - m_use) * scale_log2);
-    const float mc = m_use * scale_log2;
-    float rs = 0.f;
+    if (__ballot(m_new > m_run[nq] + tau_raw) != 0ull) {
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = fast_exp2((m_run[nq] - m_use) * scale_log2);
+      l_run[nq] *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(fmaf(s[nq][mt][i], scale_log2, -mc));
-        s[nq][mt][i] = pv;
-        rs += pv;
-      }
-    l_run[nq] = l_run[nq] * alpha + rs;
-    m_run[nq] = m_new;
-#pragma unroll
-    for (int dt = 0; dt < DV / 32; ++dt) o[nq][dt] *= alpha;
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) pf[nq][mt][cc][e] = (__bf16)s[nq][mt][cc * 8 + e];
-  }
-  // ---- O^T += V_blk^T * P^T
-  const int g = c.lane >> 4;          // 16-lane group
-  const int r = c.lane & 15;          // lane within the group
-  const int dv_lane = (g & 1) * 16 + 4 * (r & 3);
-#pragma unroll
-  for (int dt = 0; dt < DV / 32; ++dt) {
-    const int dv = dt * 32 + dv_lane;
+      for (int dt = 0; dt < DV / 32; ++dt) o[nq][dt] *= alpha;
+      m_run[nq] = m_new;
+    }
+    const float mc = ((m_run[nq] == -INFINITY) ? 0.f : m_run[nq]) * scale_log2;
+    float rs = l_run[nq];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
-        const int k0 = mt * 32 + cc * 16 + 4 * c.hl + (r >> 2);
-        const int k1 = k0 + 8;
-        const int ch = dv >> 3;
-        const int sub = (dv & 7) * 2;
-        const char* p0 = vs + k0 * (DV * 2) + ((ch ^ ((k0 & 3) << 1)) * 16) + sub;
-        const char* p1 = vs + k1 * (DV * 2) + ((ch ^ ((k1 & 3) << 1)) * 16) + sub;
-        bf16x8 a = join(lds_read_tr16(p0), lds_read_tr16(p1));
+        u32x4 packed;
 #pragma unroll
-        for (int nq = 0; nq < NQ; ++nq) o[nq][dt] = mfma32(a, pf[nq][mt][cc], o[nq][dt]);
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = fast_exp2(fmaf(s[nq][mt][cc * 8 + 2 * e], scale_log2, -mc));
+          const float p1 = fast_exp2(fmaf(s[nq][mt][cc * 8 + 2 * e + 1], scale_log2, -mc));
+          packed[e] = pack_bf16x2(p0, p1);
+          rs += p0 + p1;
+        }
+        pf[nq][mt][cc] = __builtin_bit_cast(bf16x8, packed);
       }
+    l_run[nq] = rs;
+  }
+  // ---- O^T += V_blk^T * P^T: the four dv tiles are independent chains; the transposed V reads
+  // run PF steps ahead of their MFMA.
+  {
+    constexpr int NSTEP = 4 * (DV / 32);   // (mt, cc) x dt
+    constexpr int PF = 4;
+    bf16x8 a[NSTEP];
+#pragma unroll
+    for (int st = 0; st < PF; ++st) {
+      const int q4 = st / (DV / 32), dt = st % (DV / 32);
+      const char* p0 = vs + c.va[dt] + ((q4 >> 1) * 32 + (q4 & 1) * 16) * (DV * 2);
+      a[st] = join(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * (DV * 2)));
+    }
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st) {
+      if (st + PF < NSTEP) {
+        const int q4 = (st + PF) / (DV / 32), dt = (st + PF) % (DV / 32);
+        const char* p0 = vs + c.va[dt] + ((q4 >> 1) * 32 + (q4 & 1) * 16) * (DV * 2);
+        a[st + PF] = join(lds_read_tr16(p0), lds_read_tr16(p0 + 8 * (DV * 2)));
+      }
+      const int q4 = st / (DV / 32), dt = st % (DV / 32);
+#pragma unroll
+      for (int nq = 0; nq < NQ; ++nq) o[nq][dt] = mfma32(a[st], pf[nq][q4 >> 1][q4 & 1], o[nq][dt]);
+      __builtin_amdgcn_sched_barrier(0);  // keep the reads PF steps ahead of their MFMA
+    }
   }
 }
 
@@ -198,7 +226,7 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
   // ---- XCD-aware work mapping: blocks are dealt round-robin to the 8 XCDs, so give each XCD a
   // contiguous, head-major range of work items (tiles of one head share K/V in that XCD's L2).
   const int x = blockIdx.x;
-  const int w = (x & 7) * p.per_xcd + (x >> 3);
+  const int w = p.xcd_remap ? (x & 7) * p.per_xcd + (x >> 3) : x;
   if (w >= p.total_work) return;
   const int split = w % p.num_splits;
   const int t = w / p.num_splits;
@@ -217,31 +245,45 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
 
   DenseCtx<NQ> c;
   c.lane = threadIdx.x & 63;
-  c.wave = threadIdx.x >> 6;
+  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   c.l32 = c.lane & 31;
   c.hl = c.lane >> 5;
-  c.kbase = p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh;
-  c.vbase = p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh;
-  c.k_st = p.k_st;
-  c.v_st = p.v_st;
+  c.kbase = reinterpret_cast<const char*>(p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh);
+  c.vbase = reinterpret_cast<const char*>(p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh);
+  c.k_st_b = (int)(p.k_st * 2);
+  c.v_st_b = (int)(p.v_st * 2);
   c.sk = sk;
   c.sq = sq;
   c.row0 = row0;
+  c.kdst = c.wave * K_CHUNKS_PER_WAVE * 1024;
+  c.vdst = c.wave * V_CHUNKS_PER_WAVE * 1024;
 #pragma unroll
   for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) {
     const int pch = (c.wave * K_CHUNKS_PER_WAVE + i) * 64 + c.lane;
     const int row = pch / 24, pc = pch % 24;
-    const int lc = pc ^ (row & 7);
-    c.krow[i] = row;
-    c.koff[i] = row * (int)p.k_st + lc * 8;
+    c.koff[i] = (uint32_t)(row * c.k_st_b + ((pc ^ row_swz(row)) * 16));
   }
 #pragma unroll
   for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) {
     const int pch = (c.wave * V_CHUNKS_PER_WAVE + i) * 64 + c.lane;
     const int row = pch >> 4, pc = pch & 15;
-    const int lc = pc ^ ((row & 3) << 1);
-    c.vrow[i] = row;
-    c.voff[i] = row * (int)p.v_st + lc * 8;
+    c.voff[i] = (uint32_t)(row * c.v_st_b + ((pc ^ ((row & 3) << 2)) * 16));
+  }
+  // K operand rows: lane reads row (mt*32 + l32), chunk (kk*2 + hl) stored at chunk ^ row_swz(row)
+  // (row_swz(mt*32 + l32) == row_swz(l32)); for kk = 4g + u this is byte
+  // row*384 + g*128 + (((2u + hl) ^ row_swz(l32)) * 16).
+#pragma unroll
+  for (int u = 0; u < 4; ++u) c.ka[u] = c.l32 * (DQK * 2) + (((2 * u + c.hl) ^ row_swz(c.l32)) * 16);
+  // V^T operand: 16-lane group g reads rows k0..k0+3 (k0 = 4*hl + (r >> 2) + step offset) at
+  // columns dt*32 + (g & 1)*16 + 4*(r & 3); row k0 & 3 == (r >> 2) & 3 fixes the swizzle per lane.
+  {
+    const int g = c.lane >> 4, r = c.lane & 15;
+    const int krel = 4 * c.hl + (r >> 2);
+#pragma unroll
+    for (int dt = 0; dt < DV / 32; ++dt) {
+      const int dv = dt * 32 + (g & 1) * 16 + 4 * (r & 3);
+      c.va[dt] = krel * (DV * 2) + (((dv >> 3) ^ ((krel & 3) << 2)) * 16) + (dv & 7) * 2;
+    }
   }
 
   // ---- Q^T fragments for this wave's query columns (zero beyond the sequence)
@@ -269,18 +311,17 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
   }
 
   const bool causal = p.causal != 0;
-  const Stage st0{lds_k0, lds_v0}, st1{lds_k1, lds_v1};
-  if (blo < bhi) issue_block_load(c, blo, st0);
+  if (blo < bhi) issue_block_load(c, blo, lds_k0, lds_v0);
   wait_vmem();
   __syncthreads();
   // Two blocks per trip so each stage is a distinct LDS object at compile time.
   for (int j = blo; j < bhi; j += 2) {
-    if (j + 1 < bhi) issue_block_load(c, j + 1, st1);
+    if (j + 1 < bhi) issue_block_load(c, j + 1, lds_k1, lds_v1);
     compute_block<NQ>(c, j, lds_k0, lds_v0, qf, m_run, l_run, o, p.scale_log2, causal);
     wait_vmem();
     __syncthreads();
     if (j + 1 >= bhi) break;
-    if (j + 2 < bhi) issue_block_load(c, j + 2, st0);
+    if (j + 2 < bhi) issue_block_load(c, j + 2, lds_k0, lds_v0);
     compute_block<NQ>(c, j + 1, lds_k1, lds_v1, qf, m_run, l_run, o, p.scale_log2, causal);
     wait_vmem();
     __syncthreads();

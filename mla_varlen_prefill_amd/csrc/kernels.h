@@ -42,6 +42,7 @@ struct DenseParams {
   int32_t total_q;
   int32_t per_xcd;       // ceil(total_work / 8)
   int32_t total_work;    // n_slots * H * S
+  int32_t xcd_remap;     // 1: deal contiguous work ranges to XCDs; 0: dispatch order
 };
 
 struct SparseParams {

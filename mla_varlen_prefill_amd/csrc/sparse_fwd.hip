@@ -7,27 +7,29 @@
 // as in page "mla_prefill_branch_sparse_fp8". The 576 columns are 512 latent then 64 rope; the
 // value vector is the first 512 columns of the same row.
 //
-// Work decomposition: one work-group (4 waves, one per SIMD) per query token. All heads of a
-// token read the same gathered rows, so the heads form the matrix-core N dimension (wave w owns
-// heads [32w, 32w+32)) and every latent row is gathered once per token:
-//   1. Q is split along its 576 columns: columns [0, 288) of all heads are staged in LDS once,
-//      columns [288, 576) stay in registers (72 per lane), which leaves room for the 256-register
-//      O^T accumulator without spilling;
-//   2. blocks of 32 index slots are processed in slot order: their latent rows are copied
-//      global -> LDS directly (double-buffered) and a 32-bit validity mask (-1, out of range, or
-//      at/after topk_length) is kept next to them;
-//   3. S^T (32 keys x 32 heads) = K~ (A, LDS) * Q^T (B, LDS then registers), 576 deep;
-//   4. online softmax per head (one lane pair per head) against a reference max fixed by the
-//      first block with a visible key, so the O^T accumulator is never rescaled (P may reach
-//      2^32, well inside fp32/bf16 range). The exact running max is tracked as well; if any
-//      head's max exceeds its reference by more than 2^32, the work-group runs the slots a
-//      second time with the exact max as the reference (rare; never for data whose logits span
-//      less than about 22 nats within a row);
-//   5. O^T (512 x 32 heads) += V~^T (A, transposed LDS reads of the same rows) * P^T (B).
-// Gathered rows are 72 chunks of 16 bytes; chunk c of row r sits at c ^ f(r) with
-// f(r) = ((r & 3) << 1) | ((r >> 2) & 1), which keeps both the row-wise K~ reads (8 consecutive
-// rows) and the transposed V~ reads (4 consecutive rows, 32 bytes each) free of bank conflicts.
-// Q rows in LDS are padded to 592 bytes so 8 consecutive heads start on distinct banks.
+// Work decomposition: one work-group of 8 waves (two per SIMD) per query token. All heads of a
+// token read the same gathered rows, so the heads form the matrix-core N dimension: wave w owns
+// heads [16w, 16w+16) and every latent row is gathered once per token.
+//   * Q^T of the wave's 16 heads (576 deep) stays in registers (72 per lane); the 16x16 O^T tiles
+//     (512 x 16 heads) take 128.
+//   * The token's index slots are staged in LDS (2048 at a time), so gather addresses never wait
+//     on a global load. Blocks of 32 slots are processed in slot order; their latent rows are
+//     copied global -> LDS directly into a 4-deep ring, three blocks ahead of the compute, with a
+//     32-bit validity mask per block (-1, out of range, or at/after topk_length).
+//   * Per block: S^T (32 keys x 16 heads) = K~ (A, LDS) * Q^T (B, registers) with 16x16x32 bf16
+//     MFMA (two 16-key tiles, 18 steps each); online softmax per head across the four lanes that
+//     hold a head column; O^T (512 x 16) += V~^T (A, transposed LDS reads of the same rows) * P^T
+//     (B, the S^T registers converted to bf16 in place).
+//   * The reference max of a head is fixed by the first block with a visible key, so the
+//     accumulator is never rescaled (P may reach 2^32, well inside fp32/bf16 range). The exact
+//     running max is tracked too; if any head's max exceeds its reference by more than 2^32, the
+//     work-group runs the slots a second time with the exact max (rare; never for rows whose
+//     logits span less than about 22 nats).
+// LDS layout of a gathered block: rows padded to 73 chunks of 16 bytes (1168 B), so 16
+// consecutive rows start on 16 distinct bank groups; key k of each 16-key group sits in row
+// pi(k) = ((k & 7) << 1) | (k >> 3), so the 8 keys of one transposed read occupy alternating rows
+// whose 32-byte segments tile the 256-byte bank window exactly. No XOR swizzle is needed, so every
+// operand read is a per-lane base plus an immediate offset.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,213 +40,256 @@ namespace {
 constexpr int D = 576;
 constexpr int DVS = 512;
 constexpr int BNS = 32;
-constexpr int ROW_BYTES = D * 2;                        // 1152
-constexpr int CHUNKS = D / 8;                           // 72
-constexpr int STAGE_BYTES = BNS * ROW_BYTES;            // 36864
-constexpr int CHUNKS_PER_WAVE = BNS * CHUNKS / 256;     // 9 wave-wide 1 KiB copies per block
-constexpr int MAX_HEADS = 128;
-constexpr int KK_LDS = 18;                              // 16-deep steps of Q staged in LDS
-constexpr int KK_REG = D / 16 - KK_LDS;                 // 18 steps held in registers
-constexpr int QROW_BYTES = KK_LDS * 32 + 16;            // 592: 288 columns + 16-byte pad
-constexpr float kFlushLog2 = 32.f;                      // P may grow to 2^32 before a flush
+constexpr int CHUNKS = D / 8;                           // 72 data chunks of 16 bytes per row
+constexpr int ROW_CHUNKS = CHUNKS + 1;                  // 73: one pad chunk per row
+constexpr int ROW_BYTES = ROW_CHUNKS * 16;              // 1168
+constexpr int COPIES = (BNS * ROW_CHUNKS + 63) / 64;    // 37 wave-wide 1 KiB copies per block
+constexpr int STAGE_BYTES = COPIES * 1024;              // 37888 (whole copies; the tail is scratch)
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = NWAVES * 64;
+constexpr int COPIES_PER_WAVE = (COPIES + NWAVES - 1) / NWAVES;  // 5 (extra slots repeat copy 36)
+constexpr int KSTEPS = D / 32;                          // 18 MFMA steps of depth 32
+constexpr int DTILES = DVS / 16;                        // 32 output tiles of 16 columns
+constexpr int IDX_WIN = 2048;                           // index slots staged in LDS at a time
+constexpr float kFlushLog2 = 32.f;                      // P may grow to 2^32 (see the second pass)
 
-__device__ __forceinline__ int row_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+// LDS row of key k within a block, and its inverse.
+__device__ __forceinline__ int key_row(int k) { return (k & ~15) | ((k & 7) << 1) | ((k >> 3) & 1); }
+__device__ __forceinline__ int row_key(int r) { return (r & ~15) | ((r & 15) >> 1) | ((r & 1) << 3); }
 
 struct SparseCtx {
-  int lane, wave, l32, hl;
+  int lane, wave, l16, g;  // g = lane / 16
   int len;                 // slots considered: [0, len)
   const int32_t* irow;     // this token's index row
-  bool hok;                // this lane's head exists
-  float scale;
-  __bf16* orow;            // this lane's head row of the output
+  int win0;                // first slot of the staged index window
+  int* idx;                // LDS index window
 };
 
+// Stage index slots [win0, win0 + IDX_WIN) of this token in LDS (entries past `len` read as -1).
+__device__ __forceinline__ void stage_indices(const SparseCtx& c, int tid) {
+  for (int e = tid; e < IDX_WIN; e += NTHREADS) {
+    const int slot = c.win0 + e;
+    c.idx[e] = (slot < c.len) ? c.irow[slot] : -1;
+  }
+}
+
 // Copy the latent rows of slots [32j, 32j+32) into `stage`; invalid slots copy row 0 (finite,
-// in bounds) and are masked. Wave 0 also publishes the block's validity mask.
+// in bounds) and are masked. Every wave issues exactly COPIES_PER_WAVE copies (slots past the
+// last copy repeat it; identical bytes), so the vector-memory counter advances uniformly per
+// block. Pad chunks and the stage tail receive harmless copies of chunk 0 of a valid row.
+// Wave 0 also publishes the block's validity mask (bit k = key k).
 __device__ __forceinline__ void issue_gather(const SparseParams& p, const SparseCtx& c, int j,
                                              char* stage, uint32_t* mask_slot) {
+  const int base = j * BNS - c.win0;
+  // The per-copy row/chunk arithmetic is a handful of integer ops; an opaque copy of the lane id
+  // keeps the compiler from hoisting it out of the block loop into registers it would spill.
+  int lane = c.lane;
+  asm volatile("" : "+v"(lane));
 #pragma unroll
-  for (int i = 0; i < CHUNKS_PER_WAVE; ++i) {
-    const int pch = (c.wave * CHUNKS_PER_WAVE + i) * 64 + c.lane;
-    const int row = pch / CHUNKS;
-    const int pc = pch - row * CHUNKS;
-    const int lc = pc ^ row_swz(row);
-    const int slot = j * BNS + row;
-    int rid = (slot < c.len) ? c.irow[slot] : -1;
+  for (int i = 0; i < COPIES_PER_WAVE; ++i) {
+    const int q = min(c.wave + NWAVES * i, COPIES - 1);
+    const int slot = q * 64 + lane;
+    const int row = min(slot / ROW_CHUNKS, BNS - 1);
+    int chunk = slot - (slot / ROW_CHUNKS) * ROW_CHUNKS;
+    chunk = (slot / ROW_CHUNKS >= BNS || chunk >= CHUNKS) ? 0 : chunk;
+    int rid = c.idx[base + row_key(row)];
     rid = (rid >= 0 && (int64_t)rid < p.n_kv) ? rid : 0;
-    g2lds16(p.kv + (int64_t)rid * p.kv_st + lc * 8, stage + (c.wave * CHUNKS_PER_WAVE + i) * 1024);
+    g2lds16(p.kv + (int64_t)rid * p.kv_st + chunk * 8, stage + q * 1024);
   }
   if (c.wave == 0) {
-    const int slot = j * BNS + c.l32;
-    const int rid = (slot < c.len) ? c.irow[slot] : -1;
-    const bool ok = c.hl == 0 && rid >= 0 && (int64_t)rid < p.n_kv;
+    const int rid = c.idx[base + (c.lane & 31)];
+    const bool ok = c.lane < 32 && rid >= 0 && (int64_t)rid < p.n_kv;
     const uint64_t b = __ballot(ok);
     if (c.lane == 0) *mask_slot = (uint32_t)b;
   }
 }
 
-__device__ __forceinline__ void compute_block(const SparseCtx& c, const char* stage,
-                                              uint32_t valid, const char* qlds,
-                                              const bf16x8 (&qf)[KK_REG], float& m_ref,
-                                              float& l_run, f32x16 (&o)[DVS / 32],
-                                              float scale_log2, float flush_raw, float& m_true,
-                                              bool& overflow) {
-  // ---- S^T = K~ * Q^T
-  f32x16 s = f32x16{};
-  {
-    const int row = c.l32;
-    const char* rb = stage + row * ROW_BYTES;
-    const int sw = row_swz(row);
-    const char* qb = qlds + (c.wave * 32 + c.l32) * QROW_BYTES + c.hl * 16;
-#pragma unroll
-    for (int kk = 0; kk < KK_LDS; ++kk) {
-      bf16x8 a = lds_read_b128(rb + (((kk * 2 + c.hl) ^ sw) * 16));
-      bf16x8 b = lds_read_b128(qb + kk * 32);
-      s = mfma32(a, b, s);
-    }
-#pragma unroll
-    for (int kk = KK_LDS; kk < D / 16; ++kk) {
-      bf16x8 a = lds_read_b128(rb + (((kk * 2 + c.hl) ^ sw) * 16));
-      s = mfma32(a, qf[kk - KK_LDS], s);
-    }
+// Wait until this wave's copies of the next block have landed, leaving `newer` later blocks'
+// copies in flight.
+__device__ __forceinline__ void wait_gather(int newer) {
+  if (newer >= 2) {
+    asm volatile("s_waitcnt vmcnt(10)" ::: "memory");
+  } else if (newer == 1) {
+    asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+  } else {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  // ---- invalid slots
+}
+
+__device__ __forceinline__ void compute_block(const SparseCtx& c, const char* stage, uint32_t valid,
+                                              const bf16x8 (&qf)[KSTEPS], float& m_ref,
+                                              float& l_run, f32x4 (&o)[DTILES], float scale_log2,
+                                              float flush_raw, float& m_true, bool& overflow) {
+  // ---- S^T = K~ * Q^T: two 16-key tiles (independent chains), K~ fragments read from LDS a
+  // few steps ahead of their MFMA.
+  constexpr int NST = 2 * KSTEPS;  // (kk, mt)
+  constexpr int PF = 3;
+  // lane reads key 16*mt + l16 (row key_row of it), chunk 4*kk + g
+  const char* rb = stage + key_row(c.l16) * ROW_BYTES + c.g * 16;
+  f32x4 s[2] = {f32x4{}, f32x4{}};
+  bf16x8 ka[NST];
+  auto rd = [&](int st) {
+    const int kk = st >> 1, mt = st & 1;
+    ka[st] = lds_read_b128(rb + mt * 16 * ROW_BYTES + kk * 64);
+  };
+#pragma unroll
+  for (int st = 0; st < PF; ++st) rd(st);
+#pragma unroll
+  for (int st = 0; st < NST; ++st) {
+    if (st + PF < NST) rd(st + PF);
+    s[st & 1] = mfma16(ka[st], qf[st >> 1], s[st & 1]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  // ---- invalid slots: this lane holds keys 16*mt + 4*g + i
   if (valid != 0xFFFFFFFFu) {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int key = 8 * (i >> 2) + 4 * c.hl + (i & 3);
-      if (((valid >> key) & 1u) == 0u) s[i] = -INFINITY;
-    }
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (((valid >> (16 * mt + 4 * c.g + i)) & 1u) == 0u) s[mt][i] = -INFINITY;
   }
   // ---- online softmax against the reference max (fixed once the head holds any mass)
-  float mx = s[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) mx = fmaxf(mx, s[i]);
-  mx = xhalf_max(mx);
+  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+  mx = xquad_max(mx);
   m_true = fmaxf(m_true, mx);
-  if (m_ref == -INFINITY) m_ref = mx;  // first visible key of this head (same in both halves)
+  if (m_ref == -INFINITY) m_ref = mx;  // first visible key of this head (same in all 4 lanes)
   overflow = overflow || (mx > m_ref + flush_raw);
   const float mc = ((m_ref == -INFINITY) ? 0.f : m_ref) * scale_log2;
-  bf16x8 pf[2];
+  u32x4 packed;
   float rs = 0.f;
 #pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    const float pv = fast_exp2(fmaf(s[i], scale_log2, -mc));
-    rs += pv;
-    pf[i >> 3][i & 7] = (__bf16)pv;
+  for (int e = 0; e < 4; ++e) {
+    const float p0 = fast_exp2(fmaf(s[e >> 1][2 * (e & 1)], scale_log2, -mc));
+    const float p1 = fast_exp2(fmaf(s[e >> 1][2 * (e & 1) + 1], scale_log2, -mc));
+    packed[e] = pack_bf16x2(p0, p1);
+    rs += p0 + p1;
   }
   l_run += rs;
-  // ---- O^T += V~^T * P^T (V~ = first 512 columns of the same LDS rows, read transposed)
-  const int g = c.lane >> 4;
-  const int r = c.lane & 15;
-  const int dv_lane = (g & 1) * 16 + 4 * (r & 3);
+  // P^T operand: k-slot 8*g + j holds key 4g + j (j < 4) or 16 + 4g + (j - 4) (j >= 4).
+  const bf16x8 pf = __builtin_bit_cast(bf16x8, packed);
+  // ---- O^T += V~^T * P^T: V~ = first 512 columns of the same rows, read transposed with the
+  // same key order; 32 independent 16-column tiles, reads a few tiles ahead.
+  {
+    // group lane r supplies row key 4g + r/4 (and +16), columns 16*dt + 4*(r & 3)
+    const int k0 = 4 * c.g + (c.l16 >> 2);
+    const char* r0 = stage + key_row(k0) * ROW_BYTES + 8 * (c.l16 & 3);
+    const char* r1 = r0 + 16 * ROW_BYTES;  // key k0 + 16 sits 16 rows further
+    constexpr int PFV = 3;
+    bf16x8 va[DTILES];
+    auto vr = [&](int dt) { va[dt] = join(lds_read_tr16(r0 + dt * 32), lds_read_tr16(r1 + dt * 32)); };
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc) {
-    const int k0 = cc * 16 + 4 * c.hl + (r >> 2);
-    const int k1 = k0 + 8;
-    const char* r0 = stage + k0 * ROW_BYTES;
-    const char* r1 = stage + k1 * ROW_BYTES;
-    const int sw0 = row_swz(k0), sw1 = row_swz(k1);
+    for (int dt = 0; dt < PFV; ++dt) vr(dt);
 #pragma unroll
-    for (int dt = 0; dt < DVS / 32; ++dt) {
-      const int dv = dt * 32 + dv_lane;
-      const int ch = dv >> 3, sub = (dv & 7) * 2;
-      bf16x8 a = join(lds_read_tr16(r0 + ((ch ^ sw0) * 16) + sub),
-                      lds_read_tr16(r1 + ((ch ^ sw1) * 16) + sub));
-      o[dt] = mfma32(a, pf[cc], o[dt]);
+    for (int dt = 0; dt < DTILES; ++dt) {
+      if (dt + PFV < DTILES) vr(dt + PFV);
+      o[dt] = mfma16(va[dt], pf, o[dt]);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(SparseParams p) {
+__global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p) {
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char qlds[MAX_HEADS * QROW_BYTES];
-  __shared__ uint32_t valid_mask[2];
+  __shared__ __attribute__((aligned(1024))) char stage2[STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char stage3[STAGE_BYTES];
+  __shared__ int idx_lds[IDX_WIN];
+  __shared__ uint32_t valid_mask[4];
   __shared__ int redo_flag;
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   SparseCtx c;
   c.lane = tid & 63;
-  c.wave = tid >> 6;
-  c.l32 = c.lane & 31;
-  c.hl = c.lane >> 5;
+  c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  c.l16 = c.lane & 15;
+  c.g = c.lane >> 4;
   c.len = p.topk;
   if (p.topk_length != nullptr) c.len = min(max(p.topk_length[t], 0), p.topk);
   if (p.n_kv <= 0) c.len = 0;  // an empty pool has no valid slot (and no row to read)
   c.irow = p.idx + (int64_t)t * p.idx_st;
-
+  c.win0 = 0;
+  c.idx = idx_lds;
   const int nblk = (c.len + BNS - 1) / BNS;
-  if (nblk > 0) issue_gather(p, c, 0, stage0, &valid_mask[0]);
 
-  // ---- Q columns [0, 288) of every head -> LDS (zero rows for heads >= H)
-  const __bf16* qt = p.q + (int64_t)t * p.q_st;
-  for (int e = tid; e < MAX_HEADS * (KK_LDS * 2); e += 256) {
-    const int hrow = e / (KK_LDS * 2);
-    const int ch = e - hrow * (KK_LDS * 2);
-    bf16x8 v = bf16x8{};
-    if (hrow < p.num_heads) v = *reinterpret_cast<const bf16x8*>(qt + (int64_t)hrow * p.q_sh + ch * 8);
-    *reinterpret_cast<bf16x8*>(qlds + hrow * QROW_BYTES + ch * 16) = v;
-  }
-  // ---- Q columns [288, 576) of this lane's head -> registers
-  const int head = c.wave * 32 + c.l32;
-  c.hok = head < p.num_heads;
-  c.scale = p.scale;
-  c.orow = p.out + (int64_t)t * p.o_st + (int64_t)(c.hok ? head : 0) * p.o_sh;
-  const bool wave_active = c.wave * 32 < p.num_heads;
-  bf16x8 qf[KK_REG];
+  // ---- Q^T of this lane's head: 8 columns of each 32-deep step
+  const int head = c.wave * 16 + c.l16;
+  const bool hok = head < p.num_heads;
+  const bool wave_active = c.wave * 16 < p.num_heads;
+  bf16x8 qf[KSTEPS];
   {
-    const __bf16* qp = qt + (int64_t)(c.hok ? head : 0) * p.q_sh + c.hl * 8;
+    const __bf16* qp = p.q + (int64_t)t * p.q_st + (int64_t)(hok ? head : 0) * p.q_sh + c.g * 8;
 #pragma unroll
-    for (int kk = 0; kk < KK_REG; ++kk) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + (KK_LDS + kk) * 16);
-      qf[kk] = c.hok ? v : bf16x8{};
+    for (int kk = 0; kk < KSTEPS; ++kk) {
+      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kk * 32);
+      qf[kk] = hok ? v : bf16x8{};
     }
   }
-  f32x16 o[DVS / 32];
+
+  f32x4 o[DTILES];
   float m_ref = -INFINITY, l_run = 0.f, m_true = -INFINITY;
   const float flush_raw = kFlushLog2 / p.scale_log2;
+  char* stages[4] = {stage0, stage1, stage2, stage3};
 
-  wait_vmem();
-  __syncthreads();
   for (int pass = 0; pass < 2; ++pass) {
 #pragma unroll
-    for (int dt = 0; dt < DVS / 32; ++dt) o[dt] = f32x16{};
+    for (int dt = 0; dt < DTILES; ++dt) o[dt] = f32x4{};
     l_run = 0.f;
     if (pass == 1) m_ref = m_true;  // exact max: P <= 1 everywhere
     bool overflow = false;
-    for (int j = 0; j < nblk; j += 2) {
-      if (j + 1 < nblk) issue_gather(p, c, j + 1, stage1, &valid_mask[1]);
-      if (wave_active)
-        compute_block(c, stage0, valid_mask[0], qlds, qf, m_ref, l_run, o, p.scale_log2, flush_raw,
-                      m_true, overflow);
-      wait_vmem();
-      __syncthreads();
-      if (j + 1 >= nblk) break;
-      if (j + 2 < nblk) issue_gather(p, c, j + 2, stage0, &valid_mask[0]);
-      if (wave_active)
-        compute_block(c, stage1, valid_mask[1], qlds, qf, m_ref, l_run, o, p.scale_log2, flush_raw,
-                      m_true, overflow);
-      wait_vmem();
-      __syncthreads();
+
+    // prologue: index window 0, then the first three blocks in flight
+    c.win0 = 0;
+    stage_indices(c, tid);
+    __syncthreads();
+#pragma unroll
+    for (int b = 0; b < 3; ++b)
+      if (b < nblk) issue_gather(p, c, b, stages[b], &valid_mask[b]);
+    wait_gather(min(nblk, 3) - 1);
+    __syncthreads();
+
+    // Steady state, unrolled by four so that each ring slot is a distinct LDS object.
+#define MLA_SPARSE_STEP(K, CUR, NEXT)                                                            \
+    {                                                                                             \
+      const int jj = j + (K);                                                                     \
+      if (jj >= nblk) break;                                                                      \
+      if (jj + 3 < nblk) {                                                                        \
+        if ((jj + 3) * BNS - c.win0 >= IDX_WIN) {                                                 \
+          /* every copy from the old window has been issued and its indices consumed */          \
+          c.win0 += IDX_WIN;                                                                      \
+          stage_indices(c, tid);                                                                  \
+          __syncthreads();                                                                        \
+        }                                                                                         \
+        issue_gather(p, c, jj + 3, NEXT, &valid_mask[((K) + 3) & 3]);                            \
+      }                                                                                           \
+      if (wave_active)                                                                            \
+        compute_block(c, CUR, valid_mask[(K)], qf, m_ref, l_run, o, p.scale_log2, flush_raw,      \
+                      m_true, overflow);                                                          \
+      wait_gather(min(nblk - 1, jj + 3) - (jj + 1));                                              \
+      __syncthreads();                                                                            \
     }
+    for (int j = 0; j < nblk; j += 4) {
+      MLA_SPARSE_STEP(0, stage0, stage3)
+      MLA_SPARSE_STEP(1, stage1, stage0)
+      MLA_SPARSE_STEP(2, stage2, stage1)
+      MLA_SPARSE_STEP(3, stage3, stage2)
+    }
+#undef MLA_SPARSE_STEP
+
     if (pass == 1) break;
     if (tid == 0) redo_flag = 0;
     __syncthreads();
     if (__ballot(overflow) != 0ull && c.lane == 0) redo_flag = 1;
     __syncthreads();
     if (redo_flag == 0) break;
-    if (nblk > 0) issue_gather(p, c, 0, stage0, &valid_mask[0]);
-    wait_vmem();
-    __syncthreads();
   }
 
   // ---- epilogue: normalise, fold in the sink logit, write O and LSE
-  const float l_tot = xhalf_sum(l_run);
-  const float sink_v = (p.sink != nullptr && c.hok) ? p.sink[head] : -INFINITY;
+  const float l_tot = xquad_sum(l_run);
+  const float sink_v = (p.sink != nullptr && hok) ? p.sink[head] : -INFINITY;
   float inv, lse_v;
   if (l_tot == 0.f) {
     inv = 0.f;
@@ -262,24 +307,20 @@ __global__ __launch_bounds__(256, 1) void sparse_fwd_kernel(SparseParams p) {
       lse_v = mxs + __logf(z);
     }
   }
-  if (c.hok) {
-    __bf16* op = c.orow;
+  if (hok) {
+    __bf16* op = p.out + (int64_t)t * p.o_st + (int64_t)head * p.o_sh + 4 * c.g;
 #pragma unroll
-    for (int dt = 0; dt < DVS / 32; ++dt)
-#pragma unroll
-      for (int g4 = 0; g4 < 4; ++g4) {
-        const int dv = dt * 32 + 8 * g4 + 4 * c.hl;
-        u32x2 v = {pack_bf16x2(o[dt][g4 * 4 + 0] * inv, o[dt][g4 * 4 + 1] * inv),
-                   pack_bf16x2(o[dt][g4 * 4 + 2] * inv, o[dt][g4 * 4 + 3] * inv)};
-        *reinterpret_cast<u32x2*>(op + dv) = v;
-      }
-    if (p.lse != nullptr && c.hl == 0) p.lse[(int64_t)t * p.l_st + (int64_t)head * p.l_sh] = lse_v;
+    for (int dt = 0; dt < DTILES; ++dt) {
+      u32x2 v = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(op + dt * 16) = v;
+    }
+    if (p.lse != nullptr && c.g == 0) p.lse[(int64_t)t * p.l_st + (int64_t)head * p.l_sh] = lse_v;
   }
 }
 
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sparse_fwd_kernel, dim3(p.num_tokens), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(sparse_fwd_kernel, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
