@@ -59,14 +59,11 @@ struct DenseCtx {
   int va[DV / 32];                   // V rows: + (mt*32 + cc*16 [+8]) * 256 per step
 };
 
-// Row of the block that slot i of this lane's K (or V) copies holds.
-template <int NQ>
-__device__ __forceinline__ int k_slot_row(const DenseCtx<NQ>& c, int i) {
-  return ((c.wave * K_CHUNKS_PER_WAVE + i) * 64 + c.lane) / 24;
-}
-template <int NQ>
-__device__ __forceinline__ int v_slot_row(const DenseCtx<NQ>& c, int i) {
-  return ((c.wave * V_CHUNKS_PER_WAVE + i) * 64 + c.lane) >> 4;
+// 32-bit value the optimiser must treat as opaque (keeps precomputed offsets 32-bit at their use
+// and per-lane arithmetic from being hoisted into long-lived registers).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+v"(x));
+  return x;
 }
 
 template <int NQ>
@@ -76,71 +73,80 @@ __device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, int j, c
   const char* vb = c.vbase + (int64_t)key0 * c.v_st_b;
   if (key0 + BN <= c.sk) {
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) g2lds16(kb + c.koff[i], kst + c.kdst + i * 1024);
+    for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) g2lds16(kb + opaque(c.koff[i]), kst + c.kdst + i * 1024);
 #pragma unroll
-    for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) g2lds16(vb + c.voff[i], vst + c.vdst + i * 1024);
+    for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) g2lds16(vb + opaque(c.voff[i]), vst + c.vdst + i * 1024);
   } else {
     // tail block: rows past the sequence re-read its last key (finite values, masked later)
     const int last = c.sk - 1 - key0;
+    const int lane = (int)opaque((uint32_t)c.lane);
 #pragma unroll
     for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) {
-      const int r = k_slot_row(c, i);
+      const int r = ((c.wave * K_CHUNKS_PER_WAVE + i) * 64 + lane) / 24;
       const int shift = (min(r, last) - r) * c.k_st_b;
       g2lds16(kb + (uint32_t)((int)c.koff[i] + shift), kst + c.kdst + i * 1024);
     }
 #pragma unroll
     for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) {
-      const int r = v_slot_row(c, i);
+      const int r = ((c.wave * V_CHUNKS_PER_WAVE + i) * 64 + lane) >> 4;
       const int shift = (min(r, last) - r) * c.v_st_b;
       g2lds16(vb + (uint32_t)((int)c.voff[i] + shift), vst + c.vdst + i * 1024);
     }
   }
 }
 
-template <int NQ>
+// NMT: how many of the block's two 32-key tiles this wave computes (2, or 1 when the second tile
+// is entirely masked for every row of the wave; a wave with both tiles masked skips the block).
+template <int NQ, int NMT, bool MASK>
 __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, const char* ks,
                                               const char* vs, const bf16x8 (&qf)[NQ][DQK / 16],
                                               float (&m_run)[NQ], float (&l_run)[NQ],
                                               f32x16 (&o)[NQ][DV / 32], float scale_log2,
                                               bool causal) {
-  // ---- S^T = K_blk * Q^T: the two 32-key tiles are independent accumulator chains, issued
+  // ---- S^T = K_blk * Q^T: the 32-key tiles are independent accumulator chains, issued
   // alternately, with the K fragments read from LDS PF steps ahead of their MFMA.
   f32x16 s[NQ][2];
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) s[nq][0] = s[nq][1] = f32x16{};
   {
-    constexpr int NSTEP = 2 * (DQK / 16);  // 24 (kk, mt) steps
+    constexpr int NSTEP = NMT * (DQK / 16);  // (kk, mt) steps
     constexpr int PF = 4;
     bf16x8 a[NSTEP];
 #pragma unroll
     for (int st = 0; st < PF; ++st) {
-      const int kk = st >> 1, mt = st & 1;
+      const int kk = st / NMT, mt = st % NMT;
       a[st] = lds_read_b128(ks + c.ka[kk & 3] + (kk >> 2) * 128 + mt * 32 * (DQK * 2));
     }
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       if (st + PF < NSTEP) {
-        const int kk2 = (st + PF) >> 1, mt2 = (st + PF) & 1;
+        const int kk2 = (st + PF) / NMT, mt2 = (st + PF) % NMT;
         a[st + PF] = lds_read_b128(ks + c.ka[kk2 & 3] + (kk2 >> 2) * 128 + mt2 * 32 * (DQK * 2));
       }
-      const int kk = st >> 1, mt = st & 1;
+      const int kk = st / NMT, mt = st % NMT;
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) s[nq][mt] = mfma32(a[st], qf[nq][kk], s[nq][mt]);
       __builtin_amdgcn_sched_barrier(0);  // keep the read PF steps ahead of its MFMA
     }
   }
+  if (NMT == 1) {
+#pragma unroll
+    for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) s[nq][1][i] = -INFINITY;
+  }
   // ---- mask (diagonal and tail blocks only; wave-uniform test)
   const int key0 = j * BN;
   const int qmin = c.row0 + c.wave * 32 * NQ;  // smallest local query row of this wave
   const int diag = c.sk - c.sq;                // bottom-right alignment offset
-  const bool need_mask = (key0 + BN > c.sk) || (causal && key0 + BN - 1 > qmin + diag);
+  const bool need_mask = MASK && ((key0 + BN > c.sk) || (causal && key0 + BN - 1 > qmin + diag));
   if (need_mask) {
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       const int qrow = qmin + nq * 32 + c.l32;
       const int lim = (causal ? min(c.sk - 1, qrow + diag) : (c.sk - 1)) - key0 - 4 * c.hl;
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kofs = mt * 32 + 8 * (i >> 2) + (i & 3);
@@ -155,7 +161,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
   for (int nq = 0; nq < NQ; ++nq) {
     float mx = s[nq][0][0];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int i = (mt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[nq][mt][i]);
     mx = xhalf_max(mx);
@@ -171,7 +177,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
     const float mc = ((m_run[nq] == -INFINITY) ? 0.f : m_run[nq]) * scale_log2;
     float rs = l_run[nq];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
       for (int cc = 0; cc < 2; ++cc) {
         u32x4 packed;
@@ -189,7 +195,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
   // ---- O^T += V_blk^T * P^T: the four dv tiles are independent chains; the transposed V reads
   // run PF steps ahead of their MFMA.
   {
-    constexpr int NSTEP = 4 * (DV / 32);   // (mt, cc) x dt
+    constexpr int NSTEP = 2 * NMT * (DV / 32);   // (mt, cc) x dt
     constexpr int PF = 4;
     bf16x8 a[NSTEP];
 #pragma unroll
@@ -314,15 +320,43 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
   if (blo < bhi) issue_block_load(c, blo, lds_k0, lds_v0);
   wait_vmem();
   __syncthreads();
-  // Two blocks per trip so each stage is a distinct LDS object at compile time.
-  for (int j = blo; j < bhi; j += 2) {
-    if (j + 1 < bhi) issue_block_load(c, j + 1, lds_k1, lds_v1);
-    compute_block<NQ>(c, j, lds_k0, lds_v0, qf, m_run, l_run, o, p.scale_log2, causal);
+  // Blocks [blo, jd) need no mask for any row of the tile: they hold no key past the sequence
+  // end and, when causal, none past the bottom-right diagonal of the tile's first row.
+  const int diag = sk - sq;  // bottom-right alignment offset
+  int jd = sk / BN;
+  if (causal) {
+    const int x = row0 + diag - (BN - 1);
+    jd = min(jd, x < 0 ? 0 : x / BN + 1);
+  }
+  const int jm = max(blo, min(jd, bhi));
+  int j = blo;
+  // Two unmasked blocks per trip so each stage is a distinct LDS object at compile time.
+  for (; j + 1 < jm; j += 2) {
+    issue_block_load(c, j + 1, lds_k1, lds_v1);
+    compute_block<NQ, 2, false>(c, j, lds_k0, lds_v0, qf, m_run, l_run, o, p.scale_log2, causal);
     wait_vmem();
     __syncthreads();
-    if (j + 1 >= bhi) break;
     if (j + 2 < bhi) issue_block_load(c, j + 2, lds_k0, lds_v0);
-    compute_block<NQ>(c, j + 1, lds_k1, lds_v1, qf, m_run, l_run, o, p.scale_log2, causal);
+    compute_block<NQ, 2, false>(c, j + 1, lds_k1, lds_v1, qf, m_run, l_run, o, p.scale_log2, causal);
+    wait_vmem();
+    __syncthreads();
+  }
+  // The rest (at most one unmasked block plus the diagonal and tail blocks), block j in stage 0
+  // on entry. Per wave and block, only the leading 32-key tiles that hold a key visible to some
+  // row of the wave are computed (0, 1 or 2; wave-uniform).
+  const int qmax = row0 + c.wave * 32 * NQ + 32 * NQ - 1;  // largest local query row of the wave
+  const int vis_end = min(sk, causal ? qmax + diag + 1 : sk);  // keys [0, vis_end) visible to the wave
+  for (int st = 0; j < bhi; ++j, st ^= 1) {
+    char* kcur = st ? lds_k1 : lds_k0;
+    char* vcur = st ? lds_v1 : lds_v0;
+    if (j + 1 < bhi) issue_block_load(c, j + 1, st ? lds_k0 : lds_k1, st ? lds_v0 : lds_v1);
+    const int rem = vis_end - j * BN;
+    // The one-tile body exists only for one query tile per wave (with two, a second copy of the
+    // body does not fit the register file).
+    if (rem > 32 || (NQ > 1 && rem > 0))
+      compute_block<NQ, 2, true>(c, j, kcur, vcur, qf, m_run, l_run, o, p.scale_log2, causal);
+    else if (NQ == 1 && rem > 0)
+      compute_block<NQ, 1, true>(c, j, kcur, vcur, qf, m_run, l_run, o, p.scale_log2, causal);
     wait_vmem();
     __syncthreads();
   }
