@@ -105,6 +105,13 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
  *   lse  : nullable float32 [total_q, H], strides (lse_stride_tok, lse_stride_head), written.
  *   workspace : device memory of at least mla_prefill_varlen_workspace_size(...) bytes with the
  *         same batch/total_q/max_seqlen/H/num_splits; scratch only, contents undefined after.
+ *         It holds the plan and the work-ticket counters of the call: calls that may overlap in
+ *         time (other streams) must not share a workspace.
+ * Tuning (environment, read by the library): MLA_DENSE_NQ=2 selects 256-row query tiles (one
+ * work-group per CU); MLA_DENSE_GROUP=n schedules n (head, split) units per XCD at a time
+ * (default 1); MLA_DENSE_WGS_PER_XCD=n caps the persistent grid at 8*n work-groups (default: all
+ * resident slots). The last two leave results bitwise unchanged (each work item is computed the
+ * same way whichever work-group runs it); the tile height may change them within rounding.
  * With num_splits == 1 a sequence's result does not depend on the other sequences in the batch,
  * and repeated calls are bitwise identical.
  * Errors: INVALID_ARG (null q/k/v/cu/out, sizes <= 0 where a count is required, strides smaller

@@ -101,13 +101,15 @@ int dense_nq() {
 }
 int dense_bm() { return 128 * dense_nq(); }
 
-// XCD-aware work mapping (default on); MLA_XCD_REMAP=0 keeps plain dispatch order.
-bool xcd_remap_enabled() {
-  static bool on = []() {
-    const char* e = std::getenv("MLA_XCD_REMAP");
-    return !(e != nullptr && std::atoi(e) == 0);
+// Dense scheduling groups: each XCD works through `n` (head, split) units at a time (longest
+// item first within a group). MLA_DENSE_GROUP overrides the default.
+int dense_group_per_xcd() {
+  static int n = []() {
+    const char* e = std::getenv("MLA_DENSE_GROUP");
+    const int v = e != nullptr ? std::atoi(e) : 0;
+    return v > 0 ? v : 1;
   }();
-  return on;
+  return n;
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -117,7 +119,8 @@ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct VarlenLayout {
   int32_t bm, mt, n_slots, splits;
-  size_t off_count, off_plan, off_opart, off_lpart, total;
+  int32_t wgs_per_xcd;  // persistent dense grid: 8 * wgs_per_xcd work-groups
+  size_t off_count, off_tickets, off_plan, off_plan_ext, off_opart, off_lpart, total;
 };
 
 int32_t resolve_splits(int32_t batch, int32_t max_q, int32_t max_k, int32_t heads,
@@ -145,9 +148,23 @@ VarlenLayout varlen_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_
   L.mt = (int32_t)cdiv(std::max(max_q, 0), L.bm);
   L.n_slots = batch * L.mt;
   L.splits = resolve_splits(batch, max_q, max_k, heads, num_splits);
+  {
+    // Persistent dense grid: every resident work-group slot (two per CU with 128-row tiles), but
+    // no more work-groups than work items.
+    const DeviceInfo* di = device_info();
+    const int cus = (di != nullptr && di->cus > 0) ? di->cus : 256;
+    const int occ = dense_nq() == 1 ? 2 : 1;
+    const int64_t max_work = (int64_t)L.n_slots * heads * L.splits;
+    const int64_t per_xcd = std::max<int64_t>(1, (int64_t)(cus / 8) * occ);
+    int64_t want = per_xcd;
+    if (const char* e = std::getenv("MLA_DENSE_WGS_PER_XCD")) want = std::max(1, std::atoi(e));
+    L.wgs_per_xcd = (int32_t)std::max<int64_t>(1, std::min<int64_t>(want, cdiv(max_work, 8)));
+  }
   L.off_count = 0;
-  L.off_plan = 256;
-  size_t off = align256(L.off_plan + (size_t)L.n_slots * 16);
+  L.off_tickets = 256;  // 8 per-XCD ticket counters, one 128-byte line each, zeroed by the plan kernel
+  L.off_plan = L.off_tickets + 8 * 128;
+  L.off_plan_ext = align256(L.off_plan + (size_t)L.n_slots * 16);
+  size_t off = align256(L.off_plan_ext + (size_t)L.n_slots * 16);
   L.off_opart = off;
   L.off_lpart = off;
   if (L.splits > 1) {
@@ -270,8 +287,10 @@ mla_status_t mla_prefill_varlen(
   int32_t* num_items = reinterpret_cast<int32_t*>(ws + L.off_count);
   int32_t* plan = reinterpret_cast<int32_t*>(ws + L.off_plan);
 
+  int32_t* tickets = reinterpret_cast<int32_t*>(ws + L.off_tickets);
+  int32_t* plan_ext = reinterpret_cast<int32_t*>(ws + L.off_plan_ext);
   mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, L.mt, L.bm, kDenseBN, causal ? 1 : 0,
-                     plan, L.n_slots, num_items};
+                     plan, L.n_slots, num_items, tickets, plan_ext};
   if (timed_launch(MLA_KERNEL_PLAN, stream, [&] { return mla::launch_plan(pp, stream); }) != hipSuccess)
     return MLA_ERR_HIP;
 
@@ -282,6 +301,7 @@ mla_status_t mla_prefill_varlen(
   dp.cu_q = cu_seqlens_q;
   dp.cu_k = cu_seqlens_k;
   dp.plan = plan;
+  dp.plan_ext = plan_ext;
   dp.num_items = num_items;
   dp.n_slots = L.n_slots;
   dp.num_heads = num_heads;
@@ -297,9 +317,13 @@ mla_status_t mla_prefill_varlen(
     dp.o_part = reinterpret_cast<float*>(ws + L.off_opart);
     dp.lse_part = reinterpret_cast<float*>(ws + L.off_lpart);
   }
-  dp.total_work = L.n_slots * num_heads * L.splits;
-  dp.per_xcd = (dp.total_work + 7) / 8;
-  dp.xcd_remap = xcd_remap_enabled() ? 1 : 0;
+  {
+    dp.wgs_per_xcd = L.wgs_per_xcd;
+    const int units = num_heads * L.splits;
+    const int gu = 8 * dense_group_per_xcd();
+    dp.group_units = (units % gu == 0) ? gu : units;
+    dp.counters = tickets;
+  }
   if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, dense_nq(), stream); }) !=
       hipSuccess)
     return MLA_ERR_HIP;

@@ -6,10 +6,10 @@
 // run_prefill_new_tokens, run_prefill_context_chunk); the softmax is accumulated online in the
 // manner the "Mojo module mla" page names as the Flash attention v2 algorithm.
 //
-// Work decomposition. One work-group (4 waves) owns one (query tile, head, key split). The
-// query tile has BM = 128*NQ rows; wave w owns rows [w*32*NQ, (w+1)*32*NQ). Keys stream in
-// blocks of BN = 64 through LDS, double-buffered, copied straight from global memory into LDS
-// (no register staging). Per block and wave:
+// Work decomposition. A work item is one (query tile, head, key split); its work-group has 4
+// waves. The query tile has BM = 128*NQ rows; wave w owns rows [w*32*NQ, (w+1)*32*NQ). Keys
+// stream in blocks of BN = 64 through LDS, double-buffered, copied straight from global memory
+// into LDS (no register staging). Per block and wave:
 //   S^T (keys x queries) = K_blk (A, from LDS) * Q^T (B, registers)       32x32x16 bf16 MFMA
 //   each lane owns one query column, so the row max needs one cross-half swap and the row sum
 //   stays lane-local until the end;
@@ -18,6 +18,15 @@
 // The key order inside every 16-key MFMA step is the one the S^T accumulator layout gives each
 // lane (keys {4h..4h+3, 8+4h..8+4h+3} for lane half h); the V^T operand is read in the same
 // order with two ds_read_b64_tr_b16 of four consecutive keys each.
+//
+// Scheduling. The grid is persistent: as many work-groups as stay resident (two per CU at
+// NQ = 1), each running work item after work item. Work items are dealt to the 8 XCDs by (head,
+// split) unit, so every K/V row a unit reads stays in one XCD's L2, and listed inside an XCD
+// longest first (the plan's order) within groups of units; an XCD's work-groups take positions
+// of that list from a ticket counter, each shortly before starting the item. The item stream is
+// pipelined: the last block of an item issues the copy of the next item's first key block and,
+// as its own Q^T fragments die (after the S^T products), the loads of the next item's.
+// The epilogue turns each wave's output tile around in LDS and writes whole row segments.
 //
 // LDS layout per stage (16-byte chunks, XOR-swizzled so every MFMA operand read is free of bank
 // conflicts on the 64-bank LDS while each wave's copy still writes 1 KiB contiguous):
@@ -41,22 +50,29 @@ constexpr int K_CHUNKS_PER_WAVE = BN * (DQK / 8) / 256;  // 6 wave-wide 1 KiB co
 constexpr int V_CHUNKS_PER_WAVE = BN * (DV / 8) / 256;   // 4
 
 constexpr float kRescaleLog2 = 8.f;  // rescale O only when a row max grows by more than 2^8
+// Bytes of a wave's K copy region used by the epilogue's output turn-around (32 rows x 128 B);
+// the rest of the region holds the work ticket handed between waves.
+constexpr int kEpilogueBytes = 32 * 128;
+static_assert(kEpilogueBytes + 4 <= K_CHUNKS_PER_WAVE * 1024, "ticket slot past the region");
 
+// Per-lane constants of a work-group (the same for every work item it runs).
 template <int NQ>
 struct DenseCtx {
-  // per-lane constants
   int lane, wave, l32, hl;
-  // problem
-  const char* kbase;   // K of this sequence/head at key 0 (bytes)
-  const char* vbase;
   int k_st_b, v_st_b;  // token strides in bytes (validated to keep 64-row offsets in 31 bits)
-  int sk, sq, row0;
   uint32_t koff[K_CHUNKS_PER_WAVE];  // byte offset of this lane's 16-byte chunk inside a block
   uint32_t voff[V_CHUNKS_PER_WAVE];
   int kdst, vdst;                    // this wave's first 1 KiB slot in a stage (bytes)
   // LDS operand addresses (bytes, relative to a stage)
   int ka[4];                         // K rows: + g*128 + mt*32*384 per 4-step group g
   int va[DV / 32];                   // V rows: + (mt*32 + cc*16 [+8]) * 256 per step
+};
+
+// One work item (wave-uniform): query tile `row0` of sequence b, head h, key blocks [blo, bhi).
+struct Item {
+  const char* kbase;  // K of this sequence/head at key 0 (bytes)
+  const char* vbase;
+  int cq0, sq, sk, row0, rows, blo, bhi, h, split;
 };
 
 // 32-bit value the optimiser must treat as opaque (keeps precomputed offsets 32-bit at their use
@@ -67,18 +83,19 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
 }
 
 template <int NQ>
-__device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, int j, char* kst, char* vst) {
+__device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, const Item& it, int j, char* kst,
+                                                 char* vst) {
   const int key0 = j * BN;
-  const char* kb = c.kbase + (int64_t)key0 * c.k_st_b;
-  const char* vb = c.vbase + (int64_t)key0 * c.v_st_b;
-  if (key0 + BN <= c.sk) {
+  const char* kb = it.kbase + (int64_t)key0 * c.k_st_b;
+  const char* vb = it.vbase + (int64_t)key0 * c.v_st_b;
+  if (key0 + BN <= it.sk) {
 #pragma unroll
     for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) g2lds16(kb + opaque(c.koff[i]), kst + c.kdst + i * 1024);
 #pragma unroll
     for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) g2lds16(vb + opaque(c.voff[i]), vst + c.vdst + i * 1024);
   } else {
     // tail block: rows past the sequence re-read its last key (finite values, masked later)
-    const int last = c.sk - 1 - key0;
+    const int last = it.sk - 1 - key0;
     const int lane = (int)opaque((uint32_t)c.lane);
 #pragma unroll
     for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) {
@@ -97,12 +114,13 @@ __device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, int j, c
 
 // NMT: how many of the block's two 32-key tiles this wave computes (2, or 1 when the second tile
 // is entirely masked for every row of the wave; a wave with both tiles masked skips the block).
-template <int NQ, int NMT, bool MASK>
-__device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, const char* ks,
-                                              const char* vs, const bf16x8 (&qf)[NQ][DQK / 16],
-                                              float (&m_run)[NQ], float (&l_run)[NQ],
-                                              f32x16 (&o)[NQ][DV / 32], float scale_log2,
-                                              bool causal) {
+// q_done(kk) runs right after the last product that reads the Q^T fragments qf[.][kk].
+template <int NQ, int NMT, bool MASK, class QDone>
+__device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item& it, int j,
+                                              const char* ks, const char* vs,
+                                              bf16x8 (&qf)[NQ][DQK / 16], float (&m_run)[NQ],
+                                              float (&l_run)[NQ], f32x16 (&o)[NQ][DV / 32],
+                                              float scale_log2, bool causal, QDone&& q_done) {
   // ---- S^T = K_blk * Q^T: the 32-key tiles are independent accumulator chains, issued
   // alternately, with the K fragments read from LDS PF steps ahead of their MFMA.
   f32x16 s[NQ][2];
@@ -126,6 +144,10 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
       const int kk = st / NMT, mt = st % NMT;
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) s[nq][mt] = mfma32(a[st], qf[nq][kk], s[nq][mt]);
+      if (mt == NMT - 1) {
+        __builtin_amdgcn_sched_barrier(0);  // the old fragments are read before q_done replaces them
+        q_done(kk);
+      }
       __builtin_amdgcn_sched_barrier(0);  // keep the read PF steps ahead of its MFMA
     }
   }
@@ -137,14 +159,14 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
   }
   // ---- mask (diagonal and tail blocks only; wave-uniform test)
   const int key0 = j * BN;
-  const int qmin = c.row0 + c.wave * 32 * NQ;  // smallest local query row of this wave
-  const int diag = c.sk - c.sq;                // bottom-right alignment offset
-  const bool need_mask = MASK && ((key0 + BN > c.sk) || (causal && key0 + BN - 1 > qmin + diag));
+  const int qmin = it.row0 + c.wave * 32 * NQ;  // smallest local query row of this wave
+  const int diag = it.sk - it.sq;                // bottom-right alignment offset
+  const bool need_mask = MASK && ((key0 + BN > it.sk) || (causal && key0 + BN - 1 > qmin + diag));
   if (need_mask) {
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       const int qrow = qmin + nq * 32 + c.l32;
-      const int lim = (causal ? min(c.sk - 1, qrow + diag) : (c.sk - 1)) - key0 - 4 * c.hl;
+      const int lim = (causal ? min(it.sk - 1, qrow + diag) : (it.sk - 1)) - key0 - 4 * (int)(opaque(c.lane) >> 5);
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
@@ -219,48 +241,271 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, int j, cons
   }
 }
 
+// One key block: optionally issue the copy of block ld_j of item ld into the other stage, then
+// compute block j of item it from the current stage. The stage pointers are restrict-qualified:
+// the two stages never overlap, and saying so lets the compiler order the operand reads of the
+// current stage freely against the copy in flight into the other one.
+template <int NQ, int NMT, bool MASK, class QDone>
+__device__ __forceinline__ void block_step(const DenseCtx<NQ>& c, const Item& it, int j, const Item& ld,
+                                           int ld_j, bool do_load, char* __restrict__ kn,
+                                           char* __restrict__ vn, const char* __restrict__ kc,
+                                           const char* __restrict__ vc, bf16x8 (&qf)[NQ][DQK / 16],
+                                           float (&m_run)[NQ], float (&l_run)[NQ],
+                                           f32x16 (&o)[NQ][DV / 32], float scale_log2, bool causal,
+                                           QDone&& q_done) {
+  if (do_load) issue_block_load(c, ld, ld_j, kn, vn);
+  compute_block<NQ, NMT, MASK>(c, it, j, kc, vc, qf, m_run, l_run, o, scale_log2, causal, q_done);
+}
+
+// Read-only metadata (plan, cu_seqlens, sink, item count) is read through the constant address
+// space: those loads are scalar, so they never hold a vector-memory counter slot that the
+// compiler would make a later block wait for, and their results are wave-uniform registers.
+template <class T>
+__device__ __forceinline__ T ld_const(const T* ptr, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)ptr)[i];
+}
+
+// The kernel's arguments, re-read from the kernel-argument segment at each use: values needed
+// only once per work item are loaded there instead of being held in scalar registers for the
+// whole kernel (the optimiser cannot see through the empty asm, so it cannot hoist the loads).
+__device__ __forceinline__ const DenseParams& kargs() {
+  auto kp = (const __attribute__((address_space(4))) DenseParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return *(const DenseParams*)kp;
+}
+
+// Decodes position i of the work list of XCD `xcd` (the positions are handed out by that XCD's
+// ticket counter). The list holds the work items t = 8*i + xcd of one global order: units
+// u = h * num_splits + split in groups of group_units, group-major, then plan item (longest
+// first), then unit within the group. Returns false past the end of the list.
+__device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& item, int& h, int& split) {
+  const DenseParams& p = kargs();
+  const int units = p.num_heads * p.num_splits;
+  const int total = n_items * units;
+  const int n_x = total > xcd ? (total - xcd + 7) / 8 : 0;
+  if (i < 0 || i >= n_x) return false;
+  const int t = 8 * i + xcd;
+  const int gu = p.group_units;
+  const int per_group = n_items * gu;
+  const int grp = t / per_group;
+  const int r = t - grp * per_group;
+  item = r / gu;
+  const int u = grp * gu + (r - item * gu);
+  h = u / p.num_splits;
+  split = u - h * p.num_splits;
+  return true;
+}
+
+template <int NQ>
+__device__ __forceinline__ Item make_item(int item, int h, int split) {
+  const DenseParams& p = kargs();
+  Item it;
+  // two independent loads: the plan entry and the sequence's row ranges the planner stored beside it
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 e = ld_const(reinterpret_cast<const i32x4*>(p.plan), item);
+  const i32x4 f = ld_const(reinterpret_cast<const i32x4*>(p.plan_ext), item);
+  const int m = e[1], nb = e[2];
+  it.cq0 = f[0];
+  it.sq = f[1];
+  const int ck0 = f[2];
+  it.sk = f[3];
+  it.row0 = m * 128 * NQ;
+  it.rows = min(128 * NQ, it.sq - it.row0);
+  it.blo = (int)(((int64_t)split * nb) / p.num_splits);
+  it.bhi = (int)(((int64_t)(split + 1) * nb) / p.num_splits);
+  it.h = h;
+  it.split = split;
+  it.kbase = reinterpret_cast<const char*>(p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh);
+  it.vbase = reinterpret_cast<const char*>(p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh);
+  return it;
+}
+
+// Q^T fragments of this wave's query columns. Rows past the tile re-read its last row: their
+// scores stay finite and their outputs are never stored, so no zeroing (and no wait) is needed.
+template <int NQ>
+__device__ __forceinline__ void q_rows(const DenseCtx<NQ>& c, const Item& it, const __bf16* (&qp)[NQ]) {
+  const DenseParams& p = kargs();
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) {
+    const int lane = (int)opaque((uint32_t)c.lane);
+    const int r = min(c.wave * 32 * NQ + nq * 32 + (lane & 31), it.rows - 1);
+    qp[nq] = p.q + (int64_t)(it.cq0 + it.row0 + r) * p.q_st + (int64_t)it.h * p.q_sh + (lane >> 5) * 8;
+  }
+}
+
+template <int NQ>
+__device__ __forceinline__ void load_q(const DenseCtx<NQ>& c, const Item& it, bf16x8 (&qf)[NQ][DQK / 16]) {
+  const __bf16* qp[NQ];
+  q_rows(c, it, qp);
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq)
+#pragma unroll
+    for (int kk = 0; kk < DQK / 16; ++kk) qf[nq][kk] = *reinterpret_cast<const bf16x8*>(qp[nq] + kk * 16);
+}
+
+// Pulls an item's Q tile into L2 ahead of its loads: the tile's rows are 384-byte runs (3
+// cache lines of 128 bytes); each thread touches 2 of its 3*BM lines. The two values must be
+// passed to touch_done() once they may have arrived (it makes no wait of its own after a
+// wait_vmem()).
+template <int NQ>
+__device__ __forceinline__ void touch_q(const Item& it, int (&t)[2]) {
+  const DenseParams& p = kargs();
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int line = (int)opaque(threadIdx.x) + i * 256;  // 0 .. 3*128*NQ-1 (NQ = 1), beyond: repeat
+    const int r = min((line / 3) % (128 * NQ), it.rows - 1);
+    const __bf16* qp = p.q + (int64_t)(it.cq0 + it.row0 + r) * p.q_st + (int64_t)it.h * p.q_sh + (line % 3) * 64;
+    t[i] = *reinterpret_cast<const int*>(qp);
+  }
+}
+__device__ __forceinline__ void touch_done(const int (&t)[2]) { asm volatile("" ::"v"(t[0]), "v"(t[1])); }
+
+template <int NQ>
+__device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it, const float (&m_run)[NQ],
+                                           const float (&l_run)[NQ], const f32x16 (&o)[NQ][DV / 32],
+                                           char* stage) {
+  // The arguments are read once, before any store (a store could otherwise be taken to change them).
+  const DenseParams& p = kargs();
+  const int h = it.h;
+  const float scale = p.scale;
+  float* const o_part = p.o_part;
+  float* const lse_part = p.lse_part;
+  const int64_t part_row = (int64_t)it.split * p.total_q;  // split-mode row base
+  const int num_heads = p.num_heads;
+  __bf16* const out_h = p.out + (int64_t)h * p.o_sh;
+  const int64_t o_st = p.o_st;
+  float* const lse = p.lse;
+  const int64_t l_st = p.l_st, l_sh = p.l_sh;
+  const float sink_v = (p.sink != nullptr && o_part == nullptr) ? ld_const(p.sink, h) : -INFINITY;
+#pragma unroll
+  for (int nq = 0; nq < NQ; ++nq) {
+    const float l_tot = xhalf_sum(l_run[nq]);
+    const int r = c.wave * 32 * NQ + nq * 32 + (int)(opaque((uint32_t)c.lane) & 31);
+    float inv, lse_v;
+    if (l_tot == 0.f) {
+      inv = 0.f;
+      lse_v = sink_v;  // -inf without a sink
+    } else {
+      const float mm = m_run[nq] * scale;  // natural-log units
+      if (sink_v == -INFINITY) {
+        inv = 1.f / l_tot;
+        lse_v = mm + __logf(l_tot);
+      } else {
+        const float mx = fmaxf(mm, sink_v);
+        const float a = __expf(mm - mx);
+        const float z = l_tot * a + __expf(sink_v - mx);
+        inv = a / z;
+        lse_v = mx + __logf(z);
+      }
+    }
+    if (r < it.rows) {
+      const int tok = it.cq0 + it.row0 + r;
+      if (o_part != nullptr) {
+        float* op = o_part + ((part_row + tok) * num_heads + h) * DV;
+#pragma unroll
+        for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int dv = dt * 32 + 8 * g4 + 4 * c.hl;
+            f32x4 v = {o[nq][dt][g4 * 4 + 0] * inv, o[nq][dt][g4 * 4 + 1] * inv,
+                       o[nq][dt][g4 * 4 + 2] * inv, o[nq][dt][g4 * 4 + 3] * inv};
+            *reinterpret_cast<f32x4*>(op + dv) = v;
+          }
+        if (c.hl == 0) lse_part[(part_row + tok) * num_heads + h] = lse_v;
+      } else if (lse != nullptr && c.hl == 0) {
+        lse[(int64_t)tok * l_st + (int64_t)h * l_sh] = lse_v;
+      }
+    }
+    if (o_part == nullptr) {
+      // bf16 output through LDS: the lane layout holds 8-byte pieces of a row, so the tile is
+      // turned around in this wave's own copy region of a free stage (rows of 64 dv, 16-byte
+      // chunks XOR-swizzled by row) and written as whole 128-byte row segments.
+      char* buf = stage + c.kdst;
+      const int r0 = c.wave * 32 * NQ + nq * 32;  // first tile row of this 32-row slab
+      // lane-derived addresses are computed here, not hoisted into long-lived registers
+      const int lane = (int)opaque((uint32_t)c.lane), l32 = lane & 31, hl = lane >> 5;
+      const int cc = lane & 7;
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+#pragma unroll
+        for (int dd = 0; dd < 2; ++dd) {
+          const int dt = half * 2 + dd;
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const int chunk = dd * 4 + g4;  // 16-byte chunk of the 64-dv row segment
+            u32x2 v = {pack_bf16x2(o[nq][dt][g4 * 4 + 0] * inv, o[nq][dt][g4 * 4 + 1] * inv),
+                       pack_bf16x2(o[nq][dt][g4 * 4 + 2] * inv, o[nq][dt][g4 * 4 + 3] * inv)};
+            *reinterpret_cast<u32x2*>(buf + l32 * 128 + ((chunk ^ (l32 & 7)) * 16) + hl * 8) = v;
+          }
+        }
+        u32x4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = i * 8 + (lane >> 3);
+          v[i] = *reinterpret_cast<const u32x4*>(buf + rr * 128 + ((cc ^ (rr & 7)) * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int rr = i * 8 + (lane >> 3);
+          if (r0 + rr < it.rows)
+            *reinterpret_cast<u32x4*>(out_h + (int64_t)(it.cq0 + it.row0 + r0 + rr) * o_st + half * 64 + cc * 8) = v[i];
+        }
+      }
+    }
+  }
+}
+
 }  // namespace
 
 template <int NQ>
 __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(DenseParams p) {
-  constexpr int BM = 128 * NQ;
   __shared__ __attribute__((aligned(1024))) char lds_k0[K_STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char lds_v0[V_STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char lds_k1[K_STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char lds_v1[V_STAGE_BYTES];
 
-  // ---- XCD-aware work mapping: blocks are dealt round-robin to the 8 XCDs, so give each XCD a
-  // contiguous, head-major range of work items (tiles of one head share K/V in that XCD's L2).
-  const int x = blockIdx.x;
-  const int w = p.xcd_remap ? (x & 7) * p.per_xcd + (x >> 3) : x;
-  if (w >= p.total_work) return;
-  const int split = w % p.num_splits;
-  const int t = w / p.num_splits;
-  const int item = t % p.n_slots;
-  const int h = t / p.n_slots;
-  if (item >= *p.num_items) return;
-  const int4 it = reinterpret_cast<const int4*>(p.plan)[item];
-  const int b = it.x, m = it.y, nb = it.z;
-
-  const int cq0 = p.cu_q[b], sq = p.cu_q[b + 1] - cq0;
-  const int ck0 = p.cu_k[b], sk = p.cu_k[b + 1] - ck0;
-  const int row0 = m * BM;
-  const int rows = min(BM, sq - row0);
-  const int blo = (int)(((int64_t)split * nb) / p.num_splits);
-  const int bhi = (int)(((int64_t)(split + 1) * nb) / p.num_splits);
+  // Work-groups are dispatched to the XCDs round-robin (work-group x runs on XCD x % 8). The
+  // work-groups of one XCD take the positions of its list from a ticket counter, each ticket
+  // shortly before the item it names starts (about two key blocks ahead, to hide the atomic's
+  // latency). The items in flight on an XCD thus always form a short window of its list, as in
+  // the dispatch order of a non-persistent grid, and their K/V rows are shared in that XCD's L2.
+  const int xcd = blockIdx.x & 7;
+  int* const counter = p.counters + xcd * 32;  // one 128-byte line per counter
+  const int n_items = min(ld_const(p.num_items, 0), p.n_slots);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // Thread 0 hands a ticket to every wave through a K stage that is free at that moment: one
+  // copy in each wave's own copy region, which only that wave's next block copy overwrites (after
+  // the wave has read it). The copy sits past the first kEpilogueBytes of the region, which the
+  // epilogue of the previous item may still be using in that stage (a wave can still be turning
+  // its output around there while thread 0 shares the ticket of the next item).
+  auto share_ticket = [&](char* kfree, int tk) -> int {
+    if (threadIdx.x == 0) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        *reinterpret_cast<int*>(kfree + w * K_CHUNKS_PER_WAVE * 1024 + kEpilogueBytes) = tk;
+    }
+    __syncthreads();
+    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int*>(
+        kfree + wave * K_CHUNKS_PER_WAVE * 1024 + kEpilogueBytes));
+  };
+  int fetched = 0;
+  auto fetch = [&] {
+    // The zero offset the optimiser cannot see through keeps this a plain per-lane atomic: at a
+    // provably uniform address it would be rewritten into a wave-level form that reads its result
+    // at once, waiting for the round trip here instead of where the ticket is shared.
+    if (threadIdx.x == 0) fetched = atomicAdd(counter + (int)opaque(0u), 1);
+  };
+  fetch();
+  int wi, wh, wsplit;
+  if (!decode_pos(n_items, xcd, share_ticket(lds_k1, fetched), wi, wh, wsplit)) return;
 
   DenseCtx<NQ> c;
   c.lane = threadIdx.x & 63;
-  c.wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  c.wave = wave;
   c.l32 = c.lane & 31;
   c.hl = c.lane >> 5;
-  c.kbase = reinterpret_cast<const char*>(p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh);
-  c.vbase = reinterpret_cast<const char*>(p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh);
   c.k_st_b = (int)(p.k_st * 2);
   c.v_st_b = (int)(p.v_st * 2);
-  c.sk = sk;
-  c.sq = sq;
-  c.row0 = row0;
   c.kdst = c.wave * K_CHUNKS_PER_WAVE * 1024;
   c.vdst = c.wave * V_CHUNKS_PER_WAVE * 1024;
 #pragma unroll
@@ -280,137 +525,138 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
   // row*384 + g*128 + (((2u + hl) ^ row_swz(l32)) * 16).
 #pragma unroll
   for (int u = 0; u < 4; ++u) c.ka[u] = c.l32 * (DQK * 2) + (((2 * u + c.hl) ^ row_swz(c.l32)) * 16);
-  // V^T operand: 16-lane group g reads rows k0..k0+3 (k0 = 4*hl + (r >> 2) + step offset) at
-  // columns dt*32 + (g & 1)*16 + 4*(r & 3); row k0 & 3 == (r >> 2) & 3 fixes the swizzle per lane.
+  // V^T operand: 16-lane group gg reads rows k0..k0+3 (k0 = 4*hl + (r >> 2) + step offset) at
+  // columns dt*32 + (gg & 1)*16 + 4*(r & 3); row k0 & 3 == (r >> 2) & 3 fixes the swizzle per lane.
   {
-    const int g = c.lane >> 4, r = c.lane & 15;
+    const int gg = c.lane >> 4, r = c.lane & 15;
     const int krel = 4 * c.hl + (r >> 2);
 #pragma unroll
     for (int dt = 0; dt < DV / 32; ++dt) {
-      const int dv = dt * 32 + (g & 1) * 16 + 4 * (r & 3);
+      const int dv = dt * 32 + (gg & 1) * 16 + 4 * (r & 3);
       c.va[dt] = krel * (DV * 2) + (((dv >> 3) ^ ((krel & 3) << 2)) * 16) + (dv & 7) * 2;
     }
   }
+  const bool causal = p.causal != 0;
 
-  // ---- Q^T fragments for this wave's query columns (zero beyond the sequence)
   bf16x8 qf[NQ][DQK / 16];
-#pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    const int r = c.wave * 32 * NQ + nq * 32 + c.l32;
-    const bool ok = r < rows;
-    const __bf16* qp = p.q + (int64_t)(cq0 + row0 + (ok ? r : 0)) * p.q_st + (int64_t)h * p.q_sh + c.hl * 8;
-#pragma unroll
-    for (int kk = 0; kk < DQK / 16; ++kk) {
-      bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + kk * 16);
-      qf[nq][kk] = ok ? v : bf16x8{};
-    }
-  }
-
   float m_run[NQ], l_run[NQ];
   f32x16 o[NQ][DV / 32];
-#pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    m_run[nq] = -INFINITY;
-    l_run[nq] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DV / 32; ++dt) o[nq][dt] = f32x16{};
-  }
+  int st = 0;  // stage holding the next block to compute
+  auto stage_k = [&](int s) { return s ? lds_k1 : lds_k0; };
+  auto stage_v = [&](int s) { return s ? lds_v1 : lds_v0; };
 
-  const bool causal = p.causal != 0;
-  if (blo < bhi) issue_block_load(c, blo, lds_k0, lds_v0);
+  Item cur = make_item<NQ>(wi, wh, wsplit);
+  load_q(c, cur, qf);
+  if (cur.blo < cur.bhi) issue_block_load(c, cur, cur.blo, stage_k(st), stage_v(st));
   wait_vmem();
   __syncthreads();
-  // Blocks [blo, jd) need no mask for any row of the tile: they hold no key past the sequence
-  // end and, when causal, none past the bottom-right diagonal of the tile's first row.
-  const int diag = sk - sq;  // bottom-right alignment offset
-  int jd = sk / BN;
-  if (causal) {
-    const int x = row0 + diag - (BN - 1);
-    jd = min(jd, x < 0 ? 0 : x / BN + 1);
-  }
-  const int jm = max(blo, min(jd, bhi));
-  int j = blo;
-  // Two unmasked blocks per trip so each stage is a distinct LDS object at compile time.
-  for (; j + 1 < jm; j += 2) {
-    issue_block_load(c, j + 1, lds_k1, lds_v1);
-    compute_block<NQ, 2, false>(c, j, lds_k0, lds_v0, qf, m_run, l_run, o, p.scale_log2, causal);
-    wait_vmem();
-    __syncthreads();
-    if (j + 2 < bhi) issue_block_load(c, j + 2, lds_k0, lds_v0);
-    compute_block<NQ, 2, false>(c, j + 1, lds_k1, lds_v1, qf, m_run, l_run, o, p.scale_log2, causal);
-    wait_vmem();
-    __syncthreads();
-  }
-  // The rest (at most one unmasked block plus the diagonal and tail blocks), block j in stage 0
-  // on entry. Per wave and block, only the leading 32-key tiles that hold a key visible to some
-  // row of the wave are computed (0, 1 or 2; wave-uniform).
-  const int qmax = row0 + c.wave * 32 * NQ + 32 * NQ - 1;  // largest local query row of the wave
-  const int vis_end = min(sk, causal ? qmax + diag + 1 : sk);  // keys [0, vis_end) visible to the wave
-  for (int st = 0; j < bhi; ++j, st ^= 1) {
-    char* kcur = st ? lds_k1 : lds_k0;
-    char* vcur = st ? lds_v1 : lds_v0;
-    if (j + 1 < bhi) issue_block_load(c, j + 1, st ? lds_k0 : lds_k1, st ? lds_v0 : lds_v1);
-    const int rem = vis_end - j * BN;
-    // The one-tile body exists only for one query tile per wave (with two, a second copy of the
-    // body does not fit the register file).
-    if (rem > 32 || (NQ > 1 && rem > 0))
-      compute_block<NQ, 2, true>(c, j, kcur, vcur, qf, m_run, l_run, o, p.scale_log2, causal);
-    else if (NQ == 1 && rem > 0)
-      compute_block<NQ, 1, true>(c, j, kcur, vcur, qf, m_run, l_run, o, p.scale_log2, causal);
-    wait_vmem();
-    __syncthreads();
-  }
 
-  // ---- epilogue
-  const float sink_v = (p.sink != nullptr && p.o_part == nullptr) ? p.sink[h] : -INFINITY;
+  while (true) {
+    bool has_next = false;
 #pragma unroll
-  for (int nq = 0; nq < NQ; ++nq) {
-    const float l_tot = xhalf_sum(l_run[nq]);
-    const int r = c.wave * 32 * NQ + nq * 32 + c.l32;
-    float inv, lse_v;
-    if (l_tot == 0.f) {
-      inv = 0.f;
-      lse_v = sink_v;  // -inf without a sink
-    } else {
-      const float mm = m_run[nq] * p.scale;  // natural-log units
-      if (sink_v == -INFINITY) {
-        inv = 1.f / l_tot;
-        lse_v = mm + __logf(l_tot);
-      } else {
-        const float mx = fmaxf(mm, sink_v);
-        const float a = __expf(mm - mx);
-        const float z = l_tot * a + __expf(sink_v - mx);
-        inv = a / z;
-        lse_v = mx + __logf(z);
-      }
+    for (int nq = 0; nq < NQ; ++nq) {
+      m_run[nq] = -INFINITY;
+      l_run[nq] = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DV / 32; ++dt) o[nq][dt] = f32x16{};
     }
-    if (r < rows) {
-      const int tok = cq0 + row0 + r;
-      if (p.o_part != nullptr) {
-        float* op = p.o_part + (((int64_t)split * p.total_q + tok) * p.num_heads + h) * DV;
-#pragma unroll
-        for (int dt = 0; dt < DV / 32; ++dt)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dv = dt * 32 + 8 * g4 + 4 * c.hl;
-            f32x4 v = {o[nq][dt][g4 * 4 + 0] * inv, o[nq][dt][g4 * 4 + 1] * inv,
-                       o[nq][dt][g4 * 4 + 2] * inv, o[nq][dt][g4 * 4 + 3] * inv};
-            *reinterpret_cast<f32x4*>(op + dv) = v;
-          }
-        if (c.hl == 0) p.lse_part[((int64_t)split * p.total_q + tok) * p.num_heads + h] = lse_v;
-      } else {
-        __bf16* op = p.out + (int64_t)tok * p.o_st + (int64_t)h * p.o_sh;
-#pragma unroll
-        for (int dt = 0; dt < DV / 32; ++dt)
-#pragma unroll
-          for (int g4 = 0; g4 < 4; ++g4) {
-            const int dv = dt * 32 + 8 * g4 + 4 * c.hl;
-            u32x2 v = {pack_bf16x2(o[nq][dt][g4 * 4 + 0] * inv, o[nq][dt][g4 * 4 + 1] * inv),
-                       pack_bf16x2(o[nq][dt][g4 * 4 + 2] * inv, o[nq][dt][g4 * 4 + 3] * inv)};
-            *reinterpret_cast<u32x2*>(op + dv) = v;
-          }
-        if (p.lse != nullptr && c.hl == 0) p.lse[(int64_t)tok * p.l_st + (int64_t)h * p.l_sh] = lse_v;
+    const bool had_blocks = cur.blo < cur.bhi;
+    // Hand-over to the next item: its ticket is fetched at the start of block fetch_j, shared at
+    // the start of block share_j (where its descriptor is built and its Q tile pulled into L2),
+    // and the last block copies its first key block and loads its Q^T fragments. Sharing waits
+    // for the ticket, so it comes at least one block after the fetch whenever the item has two
+    // blocks or more.
+    const int fetch_j = max(cur.blo, cur.bhi - 4);
+    const int share_j = cur.bhi - cur.blo >= 3 ? cur.bhi - 2 : cur.bhi - 1;
+    Item nxt = cur;
+    if (had_blocks) {
+      // Blocks before jd need no mask for any row of the tile: they hold no key past the sequence
+      // end and, when causal, none past the bottom-right diagonal of the tile's first row. The
+      // last two blocks always run in the later loops, which prepare the hand-over.
+      const int diag = cur.sk - cur.sq;
+      int jd = cur.sk / BN;
+      if (causal) {
+        const int x = cur.row0 + diag - (BN - 1);
+        jd = min(jd, x < 0 ? 0 : x / BN + 1);
       }
+      const int jm = max(cur.blo, min(jd, cur.bhi - 2));
+      // Per wave, only the leading 32-key tiles holding a key visible to some row of the wave
+      // are computed (0, 1 or 2; wave-uniform).
+      const int qmax = cur.row0 + c.wave * 32 * NQ + 32 * NQ - 1;  // largest local query row
+      const int vis_end = min(cur.sk, causal ? qmax + diag + 1 : cur.sk);
+
+      auto no_q = [](int) {};
+      int touched[2] = {0, 0};
+      auto prepare = [&](int jj) {  // at the start of block jj, before its copy
+        if (jj == fetch_j) fetch();
+        if (jj == share_j) {
+          has_next = decode_pos(n_items, xcd, share_ticket(stage_k(st ^ 1), fetched), wi, wh, wsplit);
+          if (has_next) {
+            nxt = make_item<NQ>(wi, wh, wsplit);
+            // (in the last block itself the fragment loads follow at once: no use touching)
+            if (jj + 1 < cur.bhi) touch_q<NQ>(nxt, touched);
+          }
+        }
+      };
+      int j = cur.blo;
+      for (; j < jm; ++j, st ^= 1) {
+        if (j == fetch_j) fetch();
+        block_step<NQ, 2, false>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st), stage_v(st),
+                                 qf, m_run, l_run, o, p.scale_log2, causal, no_q);
+        wait_vmem();
+        __syncthreads();
+      }
+      // The one-tile body exists only for one query tile per wave (with two, a second copy of the
+      // body does not fit the register file). A wave with no visible key in the block only copies.
+      for (; j < cur.bhi - 1; ++j, st ^= 1) {
+        prepare(j);
+        const int rem = vis_end - j * BN;
+        if (rem > 32 || (NQ > 1 && rem > 0))
+          block_step<NQ, 2, true>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st), stage_v(st),
+                                  qf, m_run, l_run, o, p.scale_log2, causal, no_q);
+        else if (NQ == 1 && rem > 0)
+          block_step<NQ, 1, true>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st), stage_v(st),
+                                  qf, m_run, l_run, o, p.scale_log2, causal, no_q);
+        else
+          issue_block_load(c, cur, j + 1, stage_k(st ^ 1), stage_v(st ^ 1));
+        wait_vmem();
+        __syncthreads();
+        touch_done(touched);
+      }
+      // Last block: hand over to the next item. Its first key block is copied into the other
+      // stage, and each of its Q^T fragments is loaded as soon as the matching fragment of this
+      // item has been read for the last time (without a next item, Q is simply re-read). It
+      // always runs the two-tile body so that the new fragments have a single definition.
+      {
+        prepare(j);
+        const __bf16* qp[NQ];
+        q_rows(c, nxt, qp);
+        block_step<NQ, 2, true>(c, cur, j, nxt, nxt.blo, has_next && nxt.blo < nxt.bhi, stage_k(st ^ 1),
+                                stage_v(st ^ 1), stage_k(st), stage_v(st), qf, m_run, l_run, o, p.scale_log2, causal,
+                                [&](int kk) {
+#pragma unroll
+                                  for (int nq = 0; nq < NQ; ++nq)
+                                    qf[nq][kk] = *reinterpret_cast<const bf16x8*>(qp[nq] + kk * 16);
+                                });
+        wait_vmem();
+        __syncthreads();
+        touch_done(touched);
+        st ^= 1;
+      }
+    } else {
+      fetch();
+      has_next = decode_pos(n_items, xcd, share_ticket(stage_k(st ^ 1), fetched), wi, wh, wsplit);
+    }
+    // Free stage for the epilogue: the one the last block read (the next item's first block sits
+    // in the other), or, for an item without blocks, the one the next item will be copied into.
+    store_item(c, cur, m_run, l_run, o, had_blocks ? stage_k(st ^ 1) : stage_k(st));
+    if (!has_next) break;
+    cur = had_blocks ? nxt : make_item<NQ>(wi, wh, wsplit);
+    if (!had_blocks) {  // nothing was handed over: start the next item from scratch
+      load_q(c, cur, qf);
+      if (cur.blo < cur.bhi) issue_block_load(c, cur, cur.blo, stage_k(st), stage_v(st));
+      wait_vmem();
+      __syncthreads();
     }
   }
 }
@@ -419,7 +665,7 @@ template __global__ void dense_fwd_kernel<1>(DenseParams);
 template __global__ void dense_fwd_kernel<2>(DenseParams);
 
 hipError_t launch_dense_fwd(const DenseParams& p, int nq, hipStream_t stream) {
-  const int grid = 8 * p.per_xcd;
+  const int grid = 8 * p.wgs_per_xcd;
   if (grid <= 0) return hipSuccess;
   if (nq == 2) {
     hipLaunchKernelGGL(dense_fwd_kernel<2>, dim3(grid), dim3(256), 0, stream, p);

@@ -18,6 +18,8 @@ struct PlanParams {
   int32_t* plan;     // [capacity][4]
   int32_t capacity;
   int32_t* num_items;
+  int32_t* counters;  // nullable [8][32]: element 0 of each line zeroed (dense work tickets)
+  int32_t* plan_ext;  // nullable [capacity][4]: (cu_q[b], Sq, cu_k[b], Sk) of each valid entry
 };
 
 struct DenseParams {
@@ -27,6 +29,7 @@ struct DenseParams {
   const int32_t* cu_q;
   const int32_t* cu_k;
   const int32_t* plan;
+  const int32_t* plan_ext;   // [n_slots][4] (cu_q[b], Sq, cu_k[b], Sk) per valid plan entry
   const int32_t* num_items;
   int32_t n_slots;       // plan capacity (batch * Mt)
   int32_t num_heads;
@@ -40,9 +43,10 @@ struct DenseParams {
   float* o_part;         // split mode: [S][total_q][H][128] fp32, else null
   float* lse_part;       // split mode: [S][total_q][H]
   int32_t total_q;
-  int32_t per_xcd;       // ceil(total_work / 8)
-  int32_t total_work;    // n_slots * H * S
-  int32_t xcd_remap;     // 1: deal contiguous work ranges to XCDs; 0: dispatch order
+  int32_t wgs_per_xcd;   // persistent grid: 8 * wgs_per_xcd work-groups
+  int32_t group_units;   // (head, split) units per scheduling group; divides H * S
+  int32_t* counters;     // [8][32] work ticket counter per XCD list (element 0 of each
+                         // 128-byte line), zero at launch
 };
 
 struct SparseParams {

@@ -16,6 +16,7 @@ namespace {
 
 struct Item {
   int b, m, nb, kv_end;
+  int cq0, sq, ck0, sk;
   bool valid;
 };
 
@@ -23,8 +24,12 @@ __device__ __forceinline__ Item slot_item(const PlanParams& p, int s) {
   Item it;
   it.b = s / p.mt;
   it.m = s - it.b * p.mt;
-  const int sq = p.cu_q[it.b + 1] - p.cu_q[it.b];
-  const int sk = p.cu_k[it.b + 1] - p.cu_k[it.b];
+  it.cq0 = p.cu_q[it.b];
+  it.ck0 = p.cu_k[it.b];
+  const int sq = p.cu_q[it.b + 1] - it.cq0;
+  const int sk = p.cu_k[it.b + 1] - it.ck0;
+  it.sq = sq;
+  it.sk = sk;
   it.valid = it.m * p.bm < sq;
   int kv_end = sk;
   if (p.causal) {
@@ -36,8 +41,10 @@ __device__ __forceinline__ Item slot_item(const PlanParams& p, int s) {
   return it;
 }
 
-__device__ __forceinline__ void write_item(int32_t* plan, int i, const Item& it) {
-  reinterpret_cast<int4*>(plan)[i] = make_int4(it.b, it.m, it.nb, it.kv_end);
+// Entry i of the plan, and (for the dense kernel, when asked for) the sequence's row ranges.
+__device__ __forceinline__ void write_item(const PlanParams& p, int i, const Item& it) {
+  reinterpret_cast<int4*>(p.plan)[i] = make_int4(it.b, it.m, it.nb, it.kv_end);
+  if (p.plan_ext != nullptr) reinterpret_cast<int4*>(p.plan_ext)[i] = make_int4(it.cq0, it.sq, it.ck0, it.sk);
 }
 
 }  // namespace
@@ -48,6 +55,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
   __shared__ int count_sh;
   const int tid = threadIdx.x;
   const int n_slots = p.batch * p.mt;
+  if (p.counters != nullptr && tid < 8) p.counters[tid * 32] = 0;
 
   if (n_slots <= kPlanSortCapacity) {
     int P = 1;
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
     const int count = count_sh;
     for (int i = tid; i < p.capacity; i += 1024) {
       if (i < count) {
-        write_item(p.plan, i, slot_item(p, (int)(keys[i] & 0x3FFFu)));
+        write_item(p, i, slot_item(p, (int)(keys[i] & 0x3FFFu)));
       } else {
         reinterpret_cast<int4*>(p.plan)[i] = make_int4(-1, -1, -1, -1);
       }
@@ -115,7 +123,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
         if (wv < wave) off += wave_tot[wv];
         tot += wave_tot[wv];
       }
-      if (it.valid) write_item(p.plan, off + pre, it);
+      if (it.valid) write_item(p, off + pre, it);
       base += tot;
       __syncthreads();
     }

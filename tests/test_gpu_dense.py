@@ -175,3 +175,35 @@ def test_dense_chunked_prefill_sampled():
     cq = cu_from_lens([2048] * 4)
     tokens = [0, 2047, 2048, 3000, 4096, 6143, 6144, 8191]
     _full_size_sampled([2048] * 4, list(CHUNKED_SK), 128, 4, tokens, [1, 64, 126], 0)
+
+
+# The dense kernel keeps a fixed grid of work-groups that each run many work items in turn, handing
+# over from one item to the next inside the last key blocks. A tiny grid makes every work-group run
+# a long chain of items: items with zero, one, two and many key blocks, tail tiles, ties in the
+# longest-first order and split keys all follow one another.
+MANY_LENS_Q = [1, 64, 128, 129, 300, 700, 33, 256, 0, 190]
+MANY_LENS_K = [1, 64, 128, 129, 300, 1500, 20, 256, 9, 100]
+
+
+@pytest.mark.parametrize("wgs_per_xcd", [1, 3])
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_dense_persistent_item_chains(wgs_per_xcd, causal, num_splits, monkeypatch):
+    monkeypatch.setenv("MLA_DENSE_WGS_PER_XCD", str(wgs_per_xcd))
+    c = make_dense(f"chains_w{wgs_per_xcd}_c{int(causal)}_s{num_splits}", MANY_LENS_Q, MANY_LENS_K,
+                   heads=5, causal=causal, seed=41, with_sink=(num_splits == 1))
+    announce(f"dense {c.name}")
+    o, lse = run_case(c, num_splits=num_splits)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
+def test_dense_persistent_item_chains_repeat_identical(monkeypatch):
+    # the work a work-group picks up depends on timing; the result must not
+    monkeypatch.setenv("MLA_DENSE_WGS_PER_XCD", "2")
+    c = make_dense("chains_repeat", MANY_LENS_Q, MANY_LENS_K, heads=7, causal=True, seed=42)
+    announce(f"dense {c.name}")
+    first = run_case(c)
+    for _ in range(3):
+        again = run_case(c)
+        assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1], equal_nan=True)
