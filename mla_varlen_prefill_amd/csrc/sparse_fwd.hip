@@ -66,10 +66,22 @@ struct SparseCtx {
 };
 
 // Stage index slots [win0, win0 + IDX_WIN) of this token in LDS (entries past `len` read as -1).
+// All loads are issued before any is used (slots past the row's end read its slot 0, which
+// exists since topk >= 1), so the staging costs one memory round trip, not one per load.
 __device__ __forceinline__ void stage_indices(const SparseCtx& c, int tid) {
-  for (int e = tid; e < IDX_WIN; e += NTHREADS) {
-    const int slot = c.win0 + e;
-    c.idx[e] = (slot < c.len) ? c.irow[slot] : -1;
+  asm volatile("" : "+v"(tid));  // addresses are formed here, not hoisted into long-lived registers
+  constexpr int PER = IDX_WIN / NTHREADS;
+  static_assert(IDX_WIN % NTHREADS == 0, "whole rounds");
+  int v[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int slot = c.win0 + tid + i * NTHREADS;
+    v[i] = c.irow[slot < c.len ? slot : 0];
+  }
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int slot = c.win0 + tid + i * NTHREADS;
+    c.idx[tid + i * NTHREADS] = slot < c.len ? v[i] : -1;
   }
 }
 
