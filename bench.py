@@ -9,7 +9,10 @@ head 192 (128 nope + 64 rope), v head 128, bf16, causal, LSE on.
 Printed: ONE JSON line with the throughput in TFLOP/s of algorithmic work (visible query-key
 pairs x 640 FLOP x heads), the dense kernel's roofline position (its own device time from HIP
 events recorded around each launch on its stream) and the fp64 CPU oracle timed on a bounded
-sample of the same batch. Secondary measurements of the other workloads (long context, chunked
+sample of the same batch. "per_call" gives the median and minimum device time of single calls,
+warm (back to back) and cold (a 1 GiB write evicts the caches before each call); "calibration"
+gives this device's sustained rate of a pure bf16 MFMA loop and of a streaming HBM read, so the
+kernels can be quoted against measured as well as published peaks. Secondary measurements of the other workloads (long context, chunked
 prefill, sparse top-k, the 128-token case) are included under "secondary" unless
 --no-secondary is given.
 """
@@ -33,6 +36,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X published HBM3E bandwidth
 DQK, DV = 192, 128
 SP_D, SP_DV = 576, 512
 PROFILES = os.path.join(ROOT, "profiles")
+CALIB = {}                    # measured device rates (filled in by main unless --no-calib)
 
 
 # ----------------------------------------------------------------------------- work counting
@@ -82,6 +86,18 @@ def kernel_source_hash(files=("dense_fwd.hip", "common.h", "kernels.h")) -> str:
 
 
 # ----------------------------------------------------------------------------- timing helpers
+def settle(step, ms: float = 100.0):
+    """Run `step` back to back for about `ms` milliseconds. Right after an idle period the device
+    runs at transient clocks for a few tens of milliseconds (step times first drop, then rise
+    by up to 40 %, then settle), so secondary measurements start from the settled state."""
+    import torch
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(4):
+            step()
+        torch.cuda.synchronize()
+
+
 def time_steps(step, steps: int, warmup: int, kernel: str):
     import torch
     import mla_varlen_prefill_amd as mla
@@ -97,6 +113,34 @@ def time_steps(step, steps: int, warmup: int, kernel: str):
     k_ms, k_n = mla.profile_read(kernel)
     mla.profile_enable(False)
     return (t1 - t0) * 1e3 / steps, (k_ms / k_n if k_n else float("nan")), k_n
+
+
+def per_call_ms(step, reps: int, flush=None):
+    """Device milliseconds of single calls, each bracketed by events on the current stream. With
+    `flush` (a large device buffer) every call is preceded by a write over it, which evicts the L2
+    and the last-level cache, so the call starts cold."""
+    import torch
+    times = []
+    for _ in range(reps):
+        if flush is not None:
+            flush.zero_()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s.record()
+        step()
+        e.record()
+        torch.cuda.synchronize()
+        times.append(s.elapsed_time(e))
+    times.sort()
+    return {"median_ms": round(times[len(times) // 2], 5), "min_ms": round(times[0], 5), "calls": reps}
+
+
+def warm_cold(step, reps: int):
+    import torch
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    res = {"warm": per_call_ms(step, reps), "cold_1GiB_flush": per_call_ms(step, reps, flush)}
+    del flush
+    torch.cuda.empty_cache()
+    return res
 
 
 def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_splits=0):
@@ -115,16 +159,22 @@ def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_spli
         mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal=True,
                                num_splits=num_splits, out=out, lse=lse, workspace=ws)
 
+    settle(step)
     ms, kms, _ = time_steps(step, steps, warmup, "dense")
+    wc = warm_cold(step, max(3, min(steps, 7)))
     fl = dense_flops(lens_q, lens_k, heads, True)
     by = dense_bytes(lens_q, lens_k, heads)
     splits = mla.varlen_num_splits(len(lens_q), max_q, max_k, heads, True, num_splits)
     del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
-    return {"workload": name, "ms_per_call": round(ms, 4), "dense_kernel_ms": round(kms, 4),
-            "splits": splits, "tflops": round(fl / ms / 1e9, 2),
-            "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-            "kernel_tflops": round(fl / kms / 1e9, 2), "alg_gbps": round(by / ms / 1e6, 1)}
+    res = {"workload": name, "ms_per_call": round(ms, 4), "dense_kernel_ms": round(kms, 4),
+           "splits": splits, "tflops": round(fl / ms / 1e9, 2),
+           "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+           "kernel_tflops": round(fl / kms / 1e9, 2), "alg_gbps": round(by / ms / 1e6, 1),
+           "per_call": wc}
+    if CALIB:
+        res["frac_measured_mfma"] = round(fl / kms / 1e9 / CALIB["mfma_loop_tflops"], 4)
+    return res
 
 
 def sparse_case(steps, warmup):
@@ -140,17 +190,22 @@ def sparse_case(steps, warmup):
     def step():
         mla.mla_prefill_sparse(q, kv, idx, scale, sink=sink, out=out, lse=lse)
 
+    settle(step)
     ms, kms, _ = time_steps(step, steps, warmup, "sparse")
+    wc = warm_cold(step, max(3, min(steps, 7)))
     valid = int(((idx_host >= 0) & (idx_host < n_kv)).sum())
     fl = sparse_flops(valid, h)
     by = sparse_bytes(valid, t, h, topk)
     del q, kv, idx, out, lse
     torch.cuda.empty_cache()
-    return {"workload": "sparse_t4096_h128_topk2048_pool65536", "ms_per_call": round(ms, 4),
-            "sparse_kernel_ms": round(kms, 4), "tflops": round(fl / ms / 1e9, 2),
-            "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
-            "alg_gbps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
-            "kernel_alg_gbps": round(by / kms / 1e6, 1)}
+    res = {"workload": "sparse_t4096_h128_topk2048_pool65536", "ms_per_call": round(ms, 4),
+           "sparse_kernel_ms": round(kms, 4), "tflops": round(fl / ms / 1e9, 2),
+           "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
+           "alg_gbps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
+           "kernel_alg_gbps": round(by / kms / 1e6, 1), "per_call": wc}
+    if CALIB:
+        res["frac_measured_stream_read"] = round(by / kms / 1e6 / CALIB["stream_read_gbps"], 4)
+    return res
 
 
 # ----------------------------------------------------------------------------- CPU baseline
@@ -196,10 +251,13 @@ def measured_traffic(flops_unused=None):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first; about 40 are needed for the clocks to settle after idle")
     ap.add_argument("--no-secondary", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-calib", action="store_true",
+                    help="skip measuring this device's MFMA-loop and streaming-read rates")
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--only", default=None,
                     help="run one workload and print its line: dense_varlen, dense_long, dense_chunked, "
@@ -232,6 +290,12 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 3}))
         return
+
+    if not args.no_calib and args.only in (None, "dense_varlen", "dense_long", "dense_chunked",
+                                           "dense_small", "sparse"):
+        from mla_varlen_prefill_amd import calib
+        CALIB["mfma_loop_tflops"] = round(calib.mfma_tflops(), 1)
+        CALIB["stream_read_gbps"] = round(calib.stream_read_gbps(), 1)
 
     if args.only not in (None, "dense_varlen"):
         sec_runs = {
@@ -270,6 +334,7 @@ def main():
                                num_splits=0, out=out, lse=lse, workspace=ws)
 
     ms, dense_kernel_ms, launches = time_steps(step, args.steps, args.warmup, "dense")
+    per_call = warm_cold(step, max(3, min(args.steps, 11)))
     flops = dense_flops(lens, lens, heads, True)
     value = flops / (ms / 1e3) / 1e12
     achieved = flops / (dense_kernel_ms / 1e3) / 1e12
@@ -295,7 +360,11 @@ def main():
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "kernel": "dense_fwd_kernel",
                      "kernel_ms": round(dense_kernel_ms, 5), "launches_timed": launches},
+        "per_call": per_call,
+        "calibration": dict(CALIB) or None,
     }
+    if CALIB:
+        result["roofline"]["frac_measured_mfma"] = round(achieved / CALIB["mfma_loop_tflops"], 4)
     del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
 

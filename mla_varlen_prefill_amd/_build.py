@@ -16,6 +16,9 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libmla_prefill.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 SOURCES = ["abi.hip", "plan.hip", "dense_fwd.hip", "sparse_fwd.hip", "combine.hip"]
+# Calibration kernels used by the benchmark harness only (measured MFMA and HBM rates).
+CALIB_SOURCE = "calib.hip"
+CALIB_PATH = os.path.join(PKG_DIR, "libmla_calib.so")
 ARCH = "gfx950"
 
 
@@ -41,13 +44,14 @@ def build(verbose: bool = False, extra_flags=None) -> str:
     os.makedirs(obj_dir, exist_ok=True)
     objs = []
     procs = []
-    for src in SOURCES:
+    for src in SOURCES + [CALIB_SOURCE]:
         obj = os.path.join(obj_dir, src.replace(".hip", ".o"))
         cmd = [cc, *compile_flags(), *(extra_flags or []), "-c", os.path.join(CSRC, src), "-o", obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
-        objs.append(obj)
+        if src != CALIB_SOURCE:
+            objs.append(obj)
     failed = []
     for src, pr in procs:
         out, _ = pr.communicate()
@@ -66,6 +70,10 @@ def build(verbose: bool = False, extra_flags=None) -> str:
         print(" ".join(link), flush=True)
     subprocess.run(link, check=True)
     os.replace(tmp, LIB_PATH)
+    calib_tmp = CALIB_PATH + ".tmp"
+    subprocess.run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+                    os.path.join(obj_dir, CALIB_SOURCE.replace(".hip", ".o")), "-o", calib_tmp], check=True)
+    os.replace(calib_tmp, CALIB_PATH)
     return LIB_PATH
 
 

@@ -9,6 +9,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
+#include <string>
 #include <utility>
 #include <vector>
 
@@ -320,8 +321,17 @@ mla_status_t mla_prefill_varlen(
   {
     dp.wgs_per_xcd = L.wgs_per_xcd;
     const int units = num_heads * L.splits;
-    const int gu = 8 * dense_group_per_xcd();
-    dp.group_units = (units % gu == 0) ? gu : units;
+    const char* map = std::getenv("MLA_DENSE_XCD_MAP");
+    const bool contiguous = units % 8 == 0 && !(map != nullptr && std::string(map) == "interleave");
+    if (contiguous) {
+      dp.xcd_units = units / 8;
+      const int gu = dense_group_per_xcd();
+      dp.group_units = (dp.xcd_units % gu == 0) ? gu : dp.xcd_units;
+    } else {
+      dp.xcd_units = 0;
+      const int gu = 8 * dense_group_per_xcd();
+      dp.group_units = (units % gu == 0) ? gu : units;
+    }
     dp.counters = tickets;
   }
   if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, dense_nq(), stream); }) !=

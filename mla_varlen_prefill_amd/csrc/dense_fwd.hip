@@ -275,22 +275,36 @@ __device__ __forceinline__ const DenseParams& kargs() {
 }
 
 // Decodes position i of the work list of XCD `xcd` (the positions are handed out by that XCD's
-// ticket counter). The list holds the work items t = 8*i + xcd of one global order: units
-// u = h * num_splits + split in groups of group_units, group-major, then plan item (longest
-// first), then unit within the group. Returns false past the end of the list.
+// ticket counter). Work items are (plan item, unit) pairs with units u = h * num_splits + split.
+// When the units divide evenly over the XCDs, XCD k owns the contiguous units
+// [k * units/8, (k+1) * units/8) (neighbouring heads, whose rows sit side by side in memory) and
+// lists them in groups of group_units, group-major, then plan item (longest first), then unit
+// within the group. Otherwise the lists interleave one global order of the same form: XCD k holds
+// its positions t = 8*i + k. Returns false past the end of the list.
 __device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& item, int& h, int& split) {
   const DenseParams& p = kargs();
   const int units = p.num_heads * p.num_splits;
-  const int total = n_items * units;
-  const int n_x = total > xcd ? (total - xcd + 7) / 8 : 0;
-  if (i < 0 || i >= n_x) return false;
-  const int t = 8 * i + xcd;
   const int gu = p.group_units;
-  const int per_group = n_items * gu;
-  const int grp = t / per_group;
-  const int r = t - grp * per_group;
-  item = r / gu;
-  const int u = grp * gu + (r - item * gu);
+  int u;
+  if (p.xcd_units > 0) {
+    const int n_x = n_items * p.xcd_units;
+    if (i < 0 || i >= n_x) return false;
+    const int per_group = n_items * gu;
+    const int grp = i / per_group;
+    const int r = i - grp * per_group;
+    item = r / gu;
+    u = xcd * p.xcd_units + grp * gu + (r - item * gu);
+  } else {
+    const int total = n_items * units;
+    const int n_x = total > xcd ? (total - xcd + 7) / 8 : 0;
+    if (i < 0 || i >= n_x) return false;
+    const int t = 8 * i + xcd;
+    const int per_group = n_items * gu;
+    const int grp = t / per_group;
+    const int r = t - grp * per_group;
+    item = r / gu;
+    u = grp * gu + (r - item * gu);
+  }
   h = u / p.num_splits;
   split = u - h * p.num_splits;
   return true;

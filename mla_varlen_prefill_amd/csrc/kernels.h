@@ -44,7 +44,8 @@ struct DenseParams {
   float* lse_part;       // split mode: [S][total_q][H]
   int32_t total_q;
   int32_t wgs_per_xcd;   // persistent grid: 8 * wgs_per_xcd work-groups
-  int32_t group_units;   // (head, split) units per scheduling group; divides H * S
+  int32_t group_units;   // (head, split) units per scheduling group
+  int32_t xcd_units;     // > 0: units owned by each XCD (contiguous); 0: interleaved lists
   int32_t* counters;     // [8][32] work ticket counter per XCD list (element 0 of each
                          // 128-byte line), zero at launch
 };

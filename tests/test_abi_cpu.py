@@ -121,3 +121,17 @@ def test_combine_and_plan_argument_errors():
     assert lib.mla_prefill_plan(P, P, 2, 300, 100, 64, 1, P, 100, P, None) == 1   # block_m not a power of 2
     assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, P, 5, P, None) == 1     # capacity < 2*3
     assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, P + 4, 6, P, None) == 3
+
+
+def test_calibration_library_exports():
+    """The benchmark's calibration kernels (MFMA loop, streaming read) live in their own library;
+    it loads without a GPU and exports its three entry points."""
+    path = os.path.join(os.path.dirname(mla.LIB_PATH), "libmla_calib.so")
+    if not os.path.exists(path):
+        pytest.skip("libmla_calib.so not built")
+    lib = ctypes.CDLL(path)
+    for name in ("mla_calib_mfma_loop", "mla_calib_mfma_flop", "mla_calib_stream_read"):
+        assert hasattr(lib, name), name
+    lib.mla_calib_mfma_flop.restype = ctypes.c_double
+    lib.mla_calib_mfma_flop.argtypes = [ctypes.c_int, ctypes.c_int]
+    assert lib.mla_calib_mfma_flop(1, 1) == 4 * 8 * 2 * 32 * 32 * 16
