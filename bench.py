@@ -77,9 +77,9 @@ def sparse_bytes(valid_slots, tokens, heads, topk, lse=True) -> float:
                  + tokens * topk * 4 + (tokens * heads * 4 if lse else 0))
 
 
-def kernel_source_hash(files=("dense_fwd.hip", "common.h", "kernels.h")) -> str:
+def kernel_source_hash(kernel_file: str = "dense_fwd.hip") -> str:
     h = hashlib.sha256()
-    for f in files:
+    for f in (kernel_file, "common.h", "kernels.h"):
         with open(os.path.join(ROOT, "mla_varlen_prefill_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -203,6 +203,7 @@ def sparse_case(steps, warmup):
            "frac_bf16_peak": round(fl / ms / 1e9 / PEAK_BF16_TFLOPS, 4),
            "alg_gbps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4),
            "kernel_alg_gbps": round(by / kms / 1e6, 1), "per_call": wc}
+    res["traffic"] = measured_traffic("sparse_fwd_t4096_h128_topk2048_traffic.json", "sparse_fwd.hip")
     if CALIB:
         res["frac_measured_stream_read"] = round(by / kms / 1e6 / CALIB["stream_read_gbps"], 4)
     return res
@@ -234,15 +235,16 @@ def cpu_baseline(case, budget_s: float):
 
 
 # ----------------------------------------------------------------------------- traffic
-def measured_traffic(flops_unused=None):
-    """HBM bytes per dense-kernel launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
-    path = os.path.join(PROFILES, "dense_fwd_varlen_b8_h128_traffic.json")
+def measured_traffic(summary: str = "dense_fwd_varlen_b8_h128_traffic.json",
+                     kernel_file: str = "dense_fwd.hip"):
+    """HBM bytes per kernel launch from a committed rocprofv3 counter summary (FETCH_SIZE and
+    WRITE_SIZE scaled by a 1 GiB copy), if it was taken on the current kernel source; else None."""
+    path = os.path.join(PROFILES, summary)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         d = json.load(f)
-    if d.get("kernel_source_hash") != kernel_source_hash():
+    if d.get("kernel_source_hash") != kernel_source_hash(kernel_file):
         return None
     return d.get("hbm_bytes_per_launch")
 
