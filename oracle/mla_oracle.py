@@ -41,6 +41,13 @@ Readings taken where the pages are silent (each also listed with the design note
   R7 In the sparse path V is the first ``dv`` columns of the same gathered rows as K.
   R8 Indices are physical pool rows; any index outside [0, N_kv) is skipped like -1.
   R9 Slots at or beyond ``topk_length[t]`` are ignored even when they hold a valid row.
+  R11 Paged latent cache (page "SparseFlashMla": ``block_table`` for PageAttention, cache shape
+     [block_num, block_size, KV_N, D], ``topk_value_mode`` 1 = logical token indices,
+     ``seqused`` = valid KV length per sequence, ``cu_seqlens_q``). Token t belongs to sequence b
+     with cu_q[b] <= t < cu_q[b+1]; logical index p of its row is cache row
+     (block_table[b][p // block_size], p % block_size). A slot is valid iff R9 holds,
+     0 <= p < used_b (used_b = seqused[b] if given, else max_blocks * block_size) and the table
+     entry lies in [0, num_blocks). A token outside every sequence has no valid slot.
 """
 from __future__ import annotations
 
@@ -192,6 +199,42 @@ def sparse_mla_prefill(q: np.ndarray, kv: np.ndarray, indices: np.ndarray, scale
             out[t, h] = o[0]
             lse[t, h] = l[0]
     return out, lse
+
+
+def paged_physical_indices(indices: np.ndarray, block_table: np.ndarray, block_size: int,
+                           num_blocks: int, cu_q: Sequence[int],
+                           seqused: Optional[Sequence[int]] = None) -> np.ndarray:
+    """Logical index rows -> physical cache rows of [num_blocks * block_size] (reading R11);
+    invalid slots become -1. block_table is [B, max_blocks] int32."""
+    idx = np.asarray(indices, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    n_tok = idx.shape[0]
+    out = np.full(idx.shape, -1, dtype=np.int64)
+    max_blocks = bt.shape[1]
+    for b in range(len(cu_q) - 1):
+        used = max_blocks * block_size if seqused is None else min(int(seqused[b]), max_blocks * block_size)
+        for t in range(int(cu_q[b]), min(int(cu_q[b + 1]), n_tok)):
+            for k, pos in enumerate(idx[t]):
+                if 0 <= pos < used:
+                    entry = bt[b, pos // block_size]
+                    if 0 <= entry < num_blocks:
+                        out[t, k] = entry * block_size + pos % block_size
+    return out
+
+
+def sparse_mla_prefill_paged(q: np.ndarray, kv_cache: np.ndarray, block_table: np.ndarray,
+                             cu_q: Sequence[int], indices: np.ndarray, scale: float, dv: int = 512,
+                             seqused: Optional[Sequence[int]] = None,
+                             topk_length: Optional[np.ndarray] = None,
+                             sink: Optional[np.ndarray] = None,
+                             tokens: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """Sparse top-k attention over a paged latent cache kv_cache [num_blocks, block_size, D]
+    with logical indices (reading R11): the indices are mapped to cache rows, then the sparse
+    definition applies unchanged."""
+    num_blocks, block_size, d = kv_cache.shape
+    phys = paged_physical_indices(indices, block_table, block_size, num_blocks, cu_q, seqused)
+    rows = np.asarray(kv_cache).reshape(num_blocks * block_size, d)
+    return sparse_mla_prefill(q, rows, phys, scale, dv=dv, topk_length=topk_length, sink=sink, tokens=tokens)
 
 
 def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray,

@@ -271,6 +271,103 @@ def test_sparse_brute_force_with_topk_length_and_duplicates():
             np.testing.assert_allclose(o[ti, hi], softmax(lg)[:-1] @ np.array(vals), atol=1e-12)
 
 
+# ---------------------------------------------------------------- paged latent cache (R11)
+def _paged_case(rng, block_size, lens_kv, n_tok_per_seq, topk, d=6, num_blocks_extra=3):
+    """Per-sequence contiguous KV scattered into a shuffled block pool, with its block table."""
+    max_blocks = max((n + block_size - 1) // block_size for n in lens_kv)
+    nb = sum((n + block_size - 1) // block_size for n in lens_kv) + num_blocks_extra
+    perm = rng.permutation(nb)
+    cache = rng.standard_normal((nb, block_size, d)) * 0.5
+    table = np.full((len(lens_kv), max_blocks), -1, dtype=np.int32)
+    seq_kv = []
+    used = 0
+    for b, n in enumerate(lens_kv):
+        kv_b = rng.standard_normal((n, d)) * 0.5
+        seq_kv.append(kv_b)
+        for i in range((n + block_size - 1) // block_size):
+            blk = perm[used]
+            used += 1
+            table[b, i] = blk
+            chunk = kv_b[i * block_size:(i + 1) * block_size]
+            cache[blk, :len(chunk)] = chunk
+    cu_q = np.concatenate([[0], np.cumsum(n_tok_per_seq)]).astype(np.int32)
+    t = int(cu_q[-1])
+    idx = np.empty((t, topk), dtype=np.int32)
+    for b in range(len(lens_kv)):
+        for ti in range(cu_q[b], cu_q[b + 1]):
+            idx[ti] = rng.integers(-2, lens_kv[b] + 3, size=topk)   # includes -1/-2 and past-the-end
+    return cache, table, cu_q, idx, seq_kv
+
+
+@pytest.mark.parametrize("block_size", [1, 3, 4])
+def test_paged_brute_force_against_unpaged_sequences(block_size):
+    """Brute force with math.exp over each sequence's own contiguous KV (never paged): with
+    seqused = the sequence lengths, the paged oracle must give the same result whatever the block
+    size and the order of the blocks."""
+    rng = np.random.default_rng(11 + block_size)
+    lens_kv, n_tok, topk, h, d, dv = [7, 10], [2, 3], 5, 2, 6, 4
+    cache, table, cu_q, idx, seq_kv = _paged_case(rng, block_size, lens_kv, n_tok, topk, d=d)
+    q = rng.standard_normal((idx.shape[0], h, d)) * 0.5
+    scale = 0.7
+    o, lse = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx, scale, dv=dv, seqused=lens_kv)
+    for b in range(len(lens_kv)):
+        for ti in range(cu_q[b], cu_q[b + 1]):
+            for hi in range(h):
+                logits, vals = [], []
+                for pos in idx[ti]:
+                    if 0 <= pos < lens_kv[b]:
+                        row = seq_kv[b][pos]
+                        logits.append(scale * sum(q[ti, hi, x] * row[x] for x in range(d)))
+                        vals.append(row[:dv])
+                if not logits:
+                    assert lse[ti, hi] == -math.inf and np.all(o[ti, hi] == 0)
+                    continue
+                z = sum(math.exp(a) for a in logits)
+                want = sum(math.exp(a) * vv for a, vv in zip(logits, vals)) / z
+                np.testing.assert_allclose(o[ti, hi], want, atol=1e-12)
+                np.testing.assert_allclose(lse[ti, hi], math.log(z), atol=1e-12)
+
+
+def test_paged_seqused_equals_padding_past_the_used_length():
+    """seqused[b] = u drops exactly the logical positions >= u, like writing -1 there."""
+    rng = np.random.default_rng(21)
+    lens_kv, n_tok, topk, h, d = [9, 6], [2, 2], 6, 2, 6
+    cache, table, cu_q, idx, _ = _paged_case(rng, 4, lens_kv, n_tok, topk, d=d)
+    q = rng.standard_normal((idx.shape[0], h, d))
+    used = [5, 2]
+    o1, l1 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx, 0.5, dv=4, seqused=used)
+    idx2 = idx.copy()
+    for b in range(2):
+        for ti in range(cu_q[b], cu_q[b + 1]):
+            idx2[ti][idx2[ti] >= used[b]] = -1
+    o2, l2 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx2, 0.5, dv=4)
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_paged_bad_table_entry_drops_that_block_only():
+    """A table entry outside [0, num_blocks) invalidates exactly the slots in that logical block;
+    a token outside every sequence has no valid slot (O = 0, LSE = -inf; sink alone with a sink)."""
+    rng = np.random.default_rng(31)
+    lens_kv, n_tok, topk, h, d, bs = [8], [3], 8, 2, 6, 4
+    cache, table, cu_q, idx, _ = _paged_case(rng, bs, lens_kv, n_tok, topk, d=d)
+    q = rng.standard_normal((idx.shape[0] + 1, h, d))       # one token past cu_q[-1]
+    idx = np.concatenate([idx, rng.integers(0, 8, size=(1, topk)).astype(np.int32)])
+    t2 = table.copy()
+    t2[0, 1] = cache.shape[0] + 5                            # logical block 1: positions 4..7
+    o1, l1 = O.sparse_mla_prefill_paged(q, cache, t2, cu_q, idx, 0.5, dv=4)
+    idx2 = idx.copy()
+    idx2[:3][(idx2[:3] >= 4) & (idx2[:3] < 8)] = -1
+    o2, l2 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx2, 0.5, dv=4)
+    np.testing.assert_array_equal(o1[:3], o2[:3])
+    np.testing.assert_array_equal(l1[:3], l2[:3])
+    assert np.all(o1[3] == 0) and np.all(l1[3] == -math.inf)
+    sink = np.array([0.3, -1.0])
+    o3, l3 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx, 0.5, dv=4, sink=sink)
+    assert np.all(o3[3] == 0)
+    np.testing.assert_array_equal(l3[3], sink)
+
+
 # ---------------------------------------------------------------- combine
 @pytest.mark.parametrize("with_sink", [False, True])
 def test_combine_of_disjoint_key_splits_equals_unsplit(with_sink):
