@@ -209,6 +209,34 @@ def sparse_case(steps, warmup):
     return res
 
 
+def sparse_paged_case(steps, warmup, block_size=64):
+    """The sparse workload through a paged cache: the same latent rows scattered over shuffled
+    pages of `block_size` rows, logical indices mapped through the block table in the kernel."""
+    import torch
+    import mla_varlen_prefill_amd as mla
+    from workloads import device_sparse_paged
+    t, h, n_kv, topk = 4096, 128, 65536, 2048
+    q, kv, cache, table, cu_q, idx, sink, idx_host = device_sparse_paged(t, h, n_kv, topk, block_size, seed=5)
+    del kv
+    out = torch.empty((t, h, SP_DV), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((t, h), dtype=torch.float32, device="cuda")
+    scale = SP_D ** -0.5
+
+    def step():
+        mla.mla_prefill_sparse_paged(q, cache, table, cu_q, idx, scale, sink=sink, out=out, lse=lse)
+
+    settle(step)
+    ms, kms, _ = time_steps(step, steps, warmup, "sparse")
+    valid = int(((idx_host >= 0) & (idx_host < n_kv)).sum())
+    by = sparse_bytes(valid, t, h, topk)
+    del q, cache, idx, out, lse
+    torch.cuda.empty_cache()
+    return {"workload": f"sparse_paged_t4096_h128_topk2048_pool65536_bs{block_size}",
+            "ms_per_call": round(ms, 4), "sparse_kernel_ms": round(kms, 4),
+            "tflops": round(sparse_flops(valid, h) / ms / 1e9, 2),
+            "alg_gbps": round(by / ms / 1e6, 1), "frac_hbm": round(by / ms / 1e6 / PEAK_HBM_GBS, 4)}
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(case, budget_s: float):
     """The fp64 oracle, as it stands, on heads 0, 1, ... of the headline batch until the budget."""
@@ -263,7 +291,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--only", default=None,
                     help="run one workload and print its line: dense_varlen, dense_long, dense_chunked, "
-                         "dense_small, sparse, copy (a plain 1 GiB device copy for counter calibration)")
+                         "dense_small, sparse, sparse_paged, copy (a plain 1 GiB device copy for counter "
+                         "calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -294,7 +323,7 @@ def main():
         return
 
     if not args.no_calib and args.only in (None, "dense_varlen", "dense_long", "dense_chunked",
-                                           "dense_small", "sparse"):
+                                           "dense_small", "sparse", "sparse_paged"):
         from mla_varlen_prefill_amd import calib
         CALIB["mfma_loop_tflops"] = round(calib.mfma_tflops(), 1)
         CALIB["stream_read_gbps"] = round(calib.stream_read_gbps(), 1)
@@ -309,6 +338,7 @@ def main():
             "dense_small": lambda: dense_device_case("dense_small_1x128_h16", [128], [128], 16, 1,
                                                      args.steps, args.warmup),
             "sparse": lambda: sparse_case(args.steps, args.warmup),
+            "sparse_paged": lambda: sparse_paged_case(args.steps, args.warmup),
         }
         print(json.dumps(sec_runs[args.only]()), flush=True)
         return
@@ -378,6 +408,7 @@ def main():
         sec.append(dense_device_case("dense_chunked_b4_q2048", [2048] * 4, [16384, 12345, 8191, 4097],
                                      128, 4, ss, sw))
         sec.append(sparse_case(ss, sw))
+        sec.append(sparse_paged_case(ss, sw))
         result["secondary"] = sec
 
     if not args.no_cpu:

@@ -177,6 +177,51 @@ mla_status_t mla_prefill_sparse(
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Sparse top-k MLA prefill over a paged latent cache with logical indices.
+ *
+ * The same operation as mla_prefill_sparse, with the latent cache laid out in pages and the
+ * indices given as logical token positions of each query's own sequence (page "SparseFlashMla",
+ * Parameters table: block_table for PageAttention, cu_seqlens_q, seqused, topk_value_mode 1 =
+ * logical token indices; Constraints: PA_BBND cache [block_num, block_size, KV_N = 1, D],
+ * block_size 1..1024, block table [B, >= ceil(max KV length / block_size)]).
+ *
+ *   kv_cache    : bf16 [num_blocks * block_size, 576] rows, row stride kv_stride_row; block e
+ *                 holds rows [e * block_size, (e + 1) * block_size). Read only.
+ *   block_table : device int32 [batch, bt_stride_seq >= max_blocks_per_seq]; entry [b][i] is the
+ *                 cache block of logical positions [i * block_size, (i + 1) * block_size) of
+ *                 sequence b.
+ *   cu_seqlens_q: device int32 [batch + 1], non-decreasing, cu[0] = 0; token t belongs to the
+ *                 sequence b with cu[b] <= t < cu[b + 1].
+ *   seqused_kv  : nullable device int32 [batch]; the number of valid logical positions of each
+ *                 sequence (default: max_blocks_per_seq * block_size).
+ *   indices     : int32 [num_tokens, topk] logical positions, row stride idx_stride_tok.
+ * Slot s of token t takes part iff s < topk_length[t] (when given), 0 <= pos < min(seqused[b],
+ * max_blocks_per_seq * block_size) and 0 <= block_table[b][pos / block_size] < num_blocks; it
+ * then reads cache row block_table[b][pos / block_size] * block_size + pos % block_size. Any
+ * other slot (-1, past the used length, a bad table entry) is skipped, which is memory-safe.
+ * A token outside every sequence gets O = 0 and LSE = -inf (or the sink). Other arguments,
+ * outputs and ownership as for mla_prefill_sparse.
+ * Errors: INVALID_ARG (null block_table or cu_seqlens_q, batch, num_blocks, block_size or
+ * max_blocks_per_seq <= 0, bt_stride_seq < max_blocks_per_seq, and the mla_prefill_sparse
+ * checks); UNSUPPORTED (block_size > 1024, num_blocks * block_size or max_blocks_per_seq *
+ * block_size above 2^31 - 1, and the mla_prefill_sparse cases); ALIGNMENT (also int32 arrays
+ * not 4-byte aligned); HIP. Sequence boundaries and table contents are not validated on the host
+ * (they are device memory); the kernel only reads table entries [0, max_blocks_per_seq).
+ * ------------------------------------------------------------------------------------------ */
+mla_status_t mla_prefill_sparse_paged(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* kv_cache, int64_t kv_stride_row, int32_t num_blocks, int32_t block_size,
+    const int32_t* block_table, int64_t bt_stride_seq, int32_t max_blocks_per_seq,
+    const int32_t* cu_seqlens_q, int32_t batch, const int32_t* seqused_kv,
+    const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
+    const int32_t* topk_length,
+    int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
  * Combine S partial results of disjoint key sets into the final result (split-KV reduction;
  * also merges a context-chunk result with a new-token result through their LSEs).
  *

@@ -9,6 +9,7 @@ gfx950 GPU, every call raises.
 Entry points (same names as the C ABI):
   mla_prefill_varlen  dense varlen prefill, q/k 192 = 128 nope + 64 rope, v 128, causal or not
   mla_prefill_sparse  sparse top-k prefill over one shared 576-wide latent KV (v = first 512)
+  mla_prefill_sparse_paged  the same over a paged latent cache with logical indices
   mla_combine         merge split partial results through their LSEs
   mla_prefill_plan    the varlen tile plan (test hook for the bit-exact plan checks)
 """
@@ -30,7 +31,8 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 EXPORTED_SYMBOLS = (
     "mla_status_string", "mla_abi_version", "mla_dense_tile_shape", "mla_prefill_plan",
     "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_num_splits",
-    "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_combine",
+    "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_prefill_sparse_paged",
+    "mla_combine",
     "mla_profile_enable", "mla_profile_read",
 )
 KERNEL_IDS = {"plan": 0, "dense": 1, "combine": 2, "sparse": 3}
@@ -76,6 +78,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_prefill_sparse.restype = ctypes.c_int
     lib.mla_prefill_sparse.argtypes = [
         _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i32, _vp,
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64,
+        _vp, _c_sz, _vp]
+    lib.mla_prefill_sparse_paged.restype = ctypes.c_int
+    lib.mla_prefill_sparse_paged.argtypes = [
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i32, _c_i32, _vp, _c_i64, _c_i32, _vp, _c_i32, _vp,
+        _vp, _c_i64, _c_i32, _vp,
         _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64,
         _vp, _c_sz, _vp]
     lib.mla_combine.restype = ctypes.c_int
@@ -211,6 +219,50 @@ def mla_prefill_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
     _check("mla_prefill_sparse", lib.mla_prefill_sparse(
         _ptr(q), q.stride(0), q.stride(1), _ptr(kv), kv.stride(0), kv.shape[0],
         _ptr(indices), indices.stride(0), topk, _ptr(topk_length),
+        t, heads, dqk, dv, float(softmax_scale), _ptr(sink),
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
+        _ptr(ws), ws_bytes, _stream()))
+    return (out, lse) if return_lse else out
+
+
+def mla_prefill_sparse_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_table: torch.Tensor,
+                             cu_seqlens_q: torch.Tensor, indices: torch.Tensor, softmax_scale: float,
+                             seqused_kv: Optional[torch.Tensor] = None,
+                             topk_length: Optional[torch.Tensor] = None,
+                             sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                             return_lse: bool = True, lse: Optional[torch.Tensor] = None,
+                             dv: int = 512):
+    """Sparse top-k MLA prefill over a paged latent cache. kv_cache bf16 [num_blocks, block_size,
+    576] (contiguous rows), block_table int32 [B, max_blocks], cu_seqlens_q int32 [B+1], indices
+    int32 [T, topk] logical positions of each token's sequence (-1 = padded), seqused_kv int32
+    [B] or None. Returns out [T,H,512] bf16 (and lse float32 [T,H])."""
+    lib = load_library()
+    _require_cuda(q, kv_cache, block_table, cu_seqlens_q, indices, seqused_kv, topk_length, sink, out, lse)
+    if q.dtype != torch.bfloat16 or kv_cache.dtype != torch.bfloat16 or q.stride(-1) != 1:
+        raise ValueError("q and kv_cache must be bf16 with a contiguous last dim")
+    if kv_cache.dim() != 3 or kv_cache.stride(2) != 1 or kv_cache.stride(0) != kv_cache.shape[1] * kv_cache.stride(1):
+        raise ValueError("kv_cache must be [num_blocks, block_size, 576] with rows of one stride")
+    for name, x in (("indices", indices), ("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q),
+                    ("seqused_kv", seqused_kv)):
+        if x is not None and (x.dtype != torch.int32 or x.stride(-1) != 1):
+            raise ValueError(f"{name} must be int32 with a contiguous last dim")
+    t, heads, dqk = q.shape
+    topk = indices.shape[1]
+    num_blocks, block_size = kv_cache.shape[0], kv_cache.shape[1]
+    batch = cu_seqlens_q.numel() - 1
+    if block_table.dim() != 2 or block_table.shape[0] != batch:
+        raise ValueError("block_table must be [batch, max_blocks]")
+    if out is None:
+        out = torch.empty((t, heads, dv), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((t, heads), dtype=torch.float32, device=q.device)
+    ws_bytes = lib.mla_prefill_sparse_workspace_size(t, heads, topk, dv)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
+    _check("mla_prefill_sparse_paged", lib.mla_prefill_sparse_paged(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(kv_cache), kv_cache.stride(1), num_blocks, block_size,
+        _ptr(block_table), block_table.stride(0), block_table.shape[1], _ptr(cu_seqlens_q), batch,
+        _ptr(seqused_kv), _ptr(indices), indices.stride(0), topk, _ptr(topk_length),
         t, heads, dqk, dv, float(softmax_scale), _ptr(sink),
         _ptr(out), out.stride(0), out.stride(1),
         _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,

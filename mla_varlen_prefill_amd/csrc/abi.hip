@@ -364,18 +364,19 @@ size_t mla_prefill_sparse_workspace_size(int32_t num_tokens, int32_t num_heads, 
   return 0;
 }
 
-mla_status_t mla_prefill_sparse(
-    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
-    const void* kv, int64_t kv_stride_row, int64_t n_kv,
-    const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
-    const int32_t* topk_length,
-    int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
-    float softmax_scale, const float* sink,
-    void* out, int64_t o_stride_tok, int64_t o_stride_head,
-    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
-    void* workspace, size_t workspace_bytes, void* hip_stream) {
-  (void)workspace;
-  (void)workspace_bytes;
+}  // extern "C"
+
+namespace {
+
+// Checks shared by the physical-row and the paged sparse entry points, then the launch.
+mla_status_t sparse_call(mla::SparseParams& sp, const void* q, int64_t q_stride_tok,
+                         int64_t q_stride_head, const void* kv, int64_t kv_stride_row, int64_t n_kv,
+                         const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
+                         const int32_t* topk_length, int32_t num_tokens, int32_t num_heads,
+                         int32_t head_dim_qk, int32_t head_dim_v, float softmax_scale,
+                         const float* sink, void* out, int64_t o_stride_tok, int64_t o_stride_head,
+                         float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+                         void* hip_stream) {
   if (q == nullptr || kv == nullptr || indices == nullptr || out == nullptr)
     return MLA_ERR_INVALID_ARG;
   if (num_tokens < 0 || num_heads <= 0 || n_kv < 0 || topk <= 0 || !std::isfinite(softmax_scale))
@@ -401,7 +402,6 @@ mla_status_t mla_prefill_sparse(
   if (di == nullptr) return MLA_ERR_HIP;
   if (!di->gfx950) return MLA_ERR_UNSUPPORTED;
 
-  mla::SparseParams sp{};
   sp.q = static_cast<const __bf16*>(q); sp.q_st = q_stride_tok; sp.q_sh = q_stride_head;
   sp.kv = static_cast<const __bf16*>(kv); sp.kv_st = kv_stride_row; sp.n_kv = n_kv;
   sp.idx = indices; sp.idx_st = idx_stride_tok; sp.topk = topk;
@@ -417,6 +417,64 @@ mla_status_t mla_prefill_sparse(
                       [&] { return mla::launch_sparse_fwd(sp, (hipStream_t)hip_stream); }) == hipSuccess
              ? MLA_OK
              : MLA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+mla_status_t mla_prefill_sparse(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* kv, int64_t kv_stride_row, int64_t n_kv,
+    const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
+    const int32_t* topk_length,
+    int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  mla::SparseParams sp{};
+  return sparse_call(sp, q, q_stride_tok, q_stride_head, kv, kv_stride_row, n_kv, indices,
+                     idx_stride_tok, topk, topk_length, num_tokens, num_heads, head_dim_qk,
+                     head_dim_v, softmax_scale, sink, out, o_stride_tok, o_stride_head, lse,
+                     lse_stride_tok, lse_stride_head, hip_stream);
+}
+
+mla_status_t mla_prefill_sparse_paged(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* kv_cache, int64_t kv_stride_row, int32_t num_blocks, int32_t block_size,
+    const int32_t* block_table, int64_t bt_stride_seq, int32_t max_blocks_per_seq,
+    const int32_t* cu_seqlens_q, int32_t batch, const int32_t* seqused_kv,
+    const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
+    const int32_t* topk_length,
+    int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  (void)workspace;
+  (void)workspace_bytes;
+  if (block_table == nullptr || cu_seqlens_q == nullptr) return MLA_ERR_INVALID_ARG;
+  if (batch <= 0 || num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq <= 0 ||
+      bt_stride_seq < max_blocks_per_seq)
+    return MLA_ERR_INVALID_ARG;
+  if (block_size > 1024 || (int64_t)num_blocks * block_size > INT32_MAX ||
+      (int64_t)max_blocks_per_seq * block_size > INT32_MAX)
+    return MLA_ERR_UNSUPPORTED;
+  if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) != 0 ||
+      (seqused_kv != nullptr && (reinterpret_cast<uintptr_t>(seqused_kv) & 3u) != 0))
+    return MLA_ERR_ALIGNMENT;
+  mla::SparseParams sp{};
+  sp.block_table = block_table; sp.bt_st = bt_stride_seq;
+  sp.max_blocks = max_blocks_per_seq; sp.block_size = block_size; sp.num_blocks = num_blocks;
+  sp.cu_q = cu_seqlens_q; sp.batch = batch; sp.seqused = seqused_kv;
+  return sparse_call(sp, q, q_stride_tok, q_stride_head, kv_cache, kv_stride_row,
+                     (int64_t)num_blocks * block_size, indices, idx_stride_tok, topk, topk_length,
+                     num_tokens, num_heads, head_dim_qk, head_dim_v, softmax_scale, sink, out,
+                     o_stride_tok, o_stride_head, lse, lse_stride_tok, lse_stride_head, hip_stream);
 }
 
 mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num_splits,

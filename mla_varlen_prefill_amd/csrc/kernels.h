@@ -60,6 +60,15 @@ struct SparseParams {
   const float* sink;
   __bf16* out; int64_t o_st, o_sh;
   float* lse; int64_t l_st, l_sh;
+  // Paged latent cache (null block_table: indices are physical rows). Token t belongs to the
+  // sequence b with cu_q[b] <= t < cu_q[b+1]; logical position pos of its index row is cache row
+  // block_table[b * bt_st + pos / block_size] * block_size + pos % block_size, valid only for
+  // 0 <= pos < min(seqused[b] (if given), max_blocks * block_size) and a table entry in
+  // [0, num_blocks).
+  const int32_t* block_table; int64_t bt_st;
+  int32_t max_blocks, block_size, num_blocks;
+  const int32_t* cu_q; int32_t batch;
+  const int32_t* seqused;
 };
 
 struct CombineParams {

@@ -78,11 +78,16 @@ struct SparseCtx {
   const int32_t* irow;     // this token's index row
   int win0;                // first slot of the staged index window
   int* idx;                // LDS index window
+  const int32_t* bt_row;   // paged cache: block-table row of the token's sequence (else null)
+  int used;                // paged cache: logical positions [0, used) may be valid
+  int bs, nblocks;         // paged cache: block size, number of blocks
 };
 
 // Stage index slots [win0, win0 + IDX_WIN) of this token in LDS (entries past `len` read as -1).
 // All loads are issued before any is used (slots past the row's end read its slot 0, which
-// exists since topk >= 1), so the staging costs one memory round trip, not one per load.
+// exists since topk >= 1), so the staging costs one memory round trip, not one per load. With a
+// paged cache the logical positions are turned into cache rows here (-1 when invalid), with one
+// more round trip for the block-table entries, so the gather itself is the same in both modes.
 __device__ __forceinline__ void stage_indices(const SparseCtx& c, int tid) {
   asm volatile("" : "+v"(tid));  // addresses are formed here, not hoisted into long-lived registers
   constexpr int PER = IDX_WIN / NTHREADS;
@@ -92,6 +97,21 @@ __device__ __forceinline__ void stage_indices(const SparseCtx& c, int tid) {
   for (int i = 0; i < PER; ++i) {
     const int slot = c.win0 + tid + i * NTHREADS;
     v[i] = c.irow[slot < c.len ? slot : 0];
+  }
+  if (c.bt_row != nullptr) {
+    int e[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const bool ok = v[i] >= 0 && v[i] < c.used;
+      e[i] = c.bt_row[ok ? v[i] / c.bs : 0];  // entry 0 exists (max_blocks >= 1)
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int pos = v[i];
+      const bool ok = pos >= 0 && pos < c.used && e[i] >= 0 && e[i] < c.nblocks;
+      const int blk = ok ? pos / c.bs : 0;
+      v[i] = ok ? e[i] * c.bs + (pos - blk * c.bs) : -1;
+    }
   }
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
@@ -240,6 +260,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
   c.irow = p.idx + (int64_t)t * p.idx_st;
   c.win0 = 0;
   c.idx = idx_lds;
+  c.bt_row = nullptr;
+  c.used = 0;
+  c.bs = p.block_size;
+  c.nblocks = p.num_blocks;
+  if (p.block_table != nullptr) {
+    // sequence of token t: the last b with cu_q[b] <= t (empty sequences are skipped over)
+    int lo = 0, hi = p.batch - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    if (p.cu_q[lo] <= t && t < p.cu_q[lo + 1]) {
+      c.bt_row = p.block_table + (int64_t)lo * p.bt_st;
+      int64_t used = (int64_t)p.max_blocks * p.block_size;
+      if (p.seqused != nullptr) used = min(used, (int64_t)max(p.seqused[lo], 0));
+      c.used = (int)used;
+    } else {
+      c.len = 0;  // a token outside every sequence has no valid slot
+    }
+  }
   const int nblk = (c.len + BNS - 1) / BNS;
 
   // ---- Q^T of this lane's head: the 8 columns of the chunk its lane group contracts per step

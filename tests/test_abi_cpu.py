@@ -109,6 +109,38 @@ def test_sparse_argument_errors():
     assert _sparse(lib, t=0) == 0
 
 
+def _sparse_paged(lib, **kw):
+    a = dict(q=P, qst=128 * 576, qsh=576, kv=P, kvst=576, nb=100, bs=64, bt=P, btst=16, maxb=16,
+             cu=P, batch=2, used=None, idx=P, idxst=64, topk=64, tl=None, t=4, heads=128, dqk=576,
+             dv=512, scale=0.04, sink=None, out=P, ost=128 * 512, osh=512, lse=None, lst=128, lsh=1,
+             ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.mla_prefill_sparse_paged(
+        a["q"], a["qst"], a["qsh"], a["kv"], a["kvst"], a["nb"], a["bs"], a["bt"], a["btst"],
+        a["maxb"], a["cu"], a["batch"], a["used"], a["idx"], a["idxst"], a["topk"], a["tl"], a["t"],
+        a["heads"], a["dqk"], a["dv"], a["scale"], a["sink"], a["out"], a["ost"], a["osh"], a["lse"],
+        a["lst"], a["lsh"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_sparse_paged_argument_errors():
+    """The paged entry point rejects bad table/cache geometry before touching a GPU, then applies
+    the same checks as the physical-row entry point."""
+    lib = mla.load_library()
+    assert _sparse_paged(lib, bt=None) == 1
+    assert _sparse_paged(lib, cu=None) == 1
+    assert _sparse_paged(lib, batch=0) == 1
+    assert _sparse_paged(lib, bs=0) == 1
+    assert _sparse_paged(lib, nb=0) == 1
+    assert _sparse_paged(lib, btst=8) == 1                       # stride below max_blocks
+    assert _sparse_paged(lib, bs=1025) == 2                      # page sizes 1..1024
+    assert _sparse_paged(lib, nb=1 << 22, bs=1024) == 2          # rows above 2^31 - 1
+    assert _sparse_paged(lib, bt=P + 2) == 3
+    assert _sparse_paged(lib, used=P + 1) == 3
+    assert _sparse_paged(lib, heads=129) == 2                    # shared sparse checks
+    assert _sparse_paged(lib, kv=P + 4) == 3
+    assert _sparse_paged(lib, t=0) == 0
+
+
 def test_combine_and_plan_argument_errors():
     lib = mla.load_library()
     args = [P, P, 2, 4, 8, 128, None, P, 8 * 128, 128, None, 8, 1, None]

@@ -170,6 +170,60 @@ def make_sparse(name: str, num_tokens: int, heads: int, n_kv: int, topk: int, se
     return SparseCase(name, q, kv, idx, float(np.float32(scale)), tl, sink)
 
 
+@dataclass
+class PagedSparseCase:
+    name: str
+    q: np.ndarray            # uint16 bf16 bits [T, H, 576]
+    kv_cache: np.ndarray     # uint16 bf16 bits [num_blocks, block_size, 576]
+    block_table: np.ndarray  # int32 [B, max_blocks]
+    cu_q: np.ndarray         # int32 [B+1]
+    indices: np.ndarray      # int32 [T, topk] logical positions of each token's sequence
+    scale: float
+    seqused: Optional[np.ndarray] = None      # int32 [B]
+    topk_length: Optional[np.ndarray] = None  # int32 [T]
+    sink: Optional[np.ndarray] = None         # float32 [H]
+    meta: dict = field(default_factory=dict)
+
+
+def make_sparse_paged(name: str, lens_kv: Sequence[int], n_tok: Sequence[int], heads: int, topk: int,
+                      block_size: int, seed: int, pad_p: float = 0.05, spare_blocks: int = 3,
+                      with_seqused: bool = True, with_sink: bool = True,
+                      with_topk_length: bool = False) -> PagedSparseCase:
+    """Paged latent cache: sequence b owns ceil(lens_kv[b] / block_size) blocks drawn from a
+    shuffled pool that also holds `spare_blocks` never-referenced blocks; unused table entries are
+    -1. Token rows of sequence b draw logical positions uniformly from [-1, lens_kv[b] + 2] (so
+    some are padded or past the used length), then each slot is padded with probability pad_p."""
+    rng = np.random.default_rng([seed, STREAM_LENS])
+    blocks = [(n + block_size - 1) // block_size for n in lens_kv]
+    max_blocks = max(1, max(blocks))
+    nb = sum(blocks) + spare_blocks
+    perm = rng.permutation(nb)
+    table = np.full((len(lens_kv), max_blocks), -1, dtype=np.int32)
+    used = 0
+    for b, nblk in enumerate(blocks):
+        table[b, :nblk] = perm[used:used + nblk]
+        used += nblk
+    cache = randn_bf16(np.random.default_rng([seed, STREAM_K]), (nb, block_size, DQK_SPARSE))
+    cu_q = cu_from_lens(n_tok)
+    t = int(cu_q[-1])
+    idx = np.empty((t, topk), dtype=np.int32)
+    for b, n in enumerate(lens_kv):
+        for ti in range(int(cu_q[b]), int(cu_q[b + 1])):
+            idx[ti] = rng.integers(-1, n + 3, size=topk)
+    if pad_p > 0:
+        idx[np.random.default_rng([seed, STREAM_PAD]).random(idx.shape) < pad_p] = -1
+    q = randn_bf16(np.random.default_rng([seed, STREAM_Q]), (t, heads, DQK_SPARSE))
+    sink = None
+    if with_sink:
+        sink = np.random.default_rng([seed, STREAM_SINK]).standard_normal(heads, dtype=np.float32)
+    tl = None
+    if with_topk_length:
+        tl = np.random.default_rng([seed, STREAM_PAD + 1]).integers(0, topk + 1, size=t).astype(np.int32)
+    seqused = np.asarray(lens_kv, dtype=np.int32) if with_seqused else None
+    return PagedSparseCase(name, q, cache, table, cu_q, idx, float(np.float32(DQK_SPARSE ** -0.5)),
+                           seqused, tl, sink)
+
+
 # --------------------------------------------------------------------------------------------
 # The five workloads (shapes from the pages' serving use: vLLM MLA prefill with K/V expanded to
 # 128 heads; absorbed sparse MLA over one latent head). Each is generated on demand.
@@ -245,6 +299,25 @@ def device_sparse(num_tokens: int, heads: int, n_kv: int, topk: int, seed: int, 
     idx_host = sparse_indices(seed, num_tokens, n_kv, topk, pad_p)
     sink = np.random.default_rng([seed, STREAM_SINK]).standard_normal(heads, dtype=np.float32)
     return q, kv, torch.from_numpy(idx_host).to(device), torch.from_numpy(sink).to(device), idx_host
+
+
+def device_sparse_paged(num_tokens: int, heads: int, n_kv: int, topk: int, block_size: int, seed: int,
+                        pad_p: float = 0.05, device="cuda"):
+    """The full-size sparse workload laid out as a paged cache: the latent rows of
+    ``device_sparse`` (one sequence of n_kv positions) scattered over n_kv / block_size blocks in
+    a seeded random order, with the block table of that order; the indices of ``device_sparse``
+    become logical positions. Returns (q, kv_rows, cache, block_table, cu_q, idx, sink, idx_host):
+    kv_rows are the unpaged rows, so the paged call must reproduce the physical-row call."""
+    import torch
+    assert n_kv % block_size == 0
+    q, kv, idx, sink, idx_host = device_sparse(num_tokens, heads, n_kv, topk, seed, pad_p, device)
+    nb = n_kv // block_size
+    perm = np.random.default_rng([seed, STREAM_LENS + 7]).permutation(nb).astype(np.int32)
+    cache = torch.empty((nb, block_size, kv.shape[1]), dtype=kv.dtype, device=device)
+    cache[torch.from_numpy(perm).to(device).long()] = kv.view(nb, block_size, kv.shape[1])
+    table = torch.from_numpy(perm[None, :].copy()).to(device)
+    cu_q = torch.tensor([0, num_tokens], dtype=torch.int32, device=device)
+    return q, kv, cache, table, cu_q, idx, sink, idx_host
 
 
 def bf16_tensor_to_bits(t) -> np.ndarray:
