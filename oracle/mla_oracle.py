@@ -41,6 +41,12 @@ Readings taken where the pages are silent (each also listed with the design note
   R7 In the sparse path V is the first ``dv`` columns of the same gathered rows as K.
   R8 Indices are physical pool rows; any index outside [0, N_kv) is skipped like -1.
   R9 Slots at or beyond ``topk_length[t]`` are ignored even when they hold a valid row.
+  R12 Sliding window / band mask (page "Sgl project Sglang FA4 Interface", ``window_size`` =
+     (left, right), e.g. (256, 0) = causal with a 256-key window; page "SparseFlashMla",
+     ``ori_win_left`` / ``ori_win_right``: the number of past / future tokens a query sees, -1 =
+     unlimited, Band mask mode). Aligned bottom-right like R3, with d = Sk - Sq: key j is visible
+     to query i iff j >= i + d - left (when left >= 0) and j <= i + d + right (when right >= 0).
+     ``causal`` is the case right = 0 and overrides a given right.
   R11 Paged latent cache (page "SparseFlashMla": ``block_table`` for PageAttention, cache shape
      [block_num, block_size, KV_N, D], ``topk_value_mode`` 1 = logical token indices,
      ``seqused`` = valid KV length per sequence, ``cu_seqlens_q``). Token t belongs to sequence b
@@ -91,24 +97,33 @@ def _softmax_rows(scores: np.ndarray, visible: np.ndarray, values: np.ndarray,
     return out, lse
 
 
-def dense_visible(sq: int, sk: int, causal: bool, rows: Optional[np.ndarray] = None) -> np.ndarray:
-    """Visibility mask [len(rows), sk] for one sequence (reading R3: bottom-right causal)."""
+def dense_visible(sq: int, sk: int, causal: bool, rows: Optional[np.ndarray] = None,
+                  window: Tuple[int, int] = (-1, -1)) -> np.ndarray:
+    """Visibility mask [len(rows), sk] for one sequence (readings R3 and R12: bottom-right
+    causal, optional (left, right) window with -1 = unlimited)."""
     i = np.arange(sq) if rows is None else np.asarray(rows)
     j = np.arange(sk)
-    if not causal:
-        return np.ones((i.size, sk), dtype=bool)
-    return j[None, :] <= (i[:, None] + (sk - sq))
+    left, right = int(window[0]), int(window[1])
+    if causal:
+        right = 0
+    vis = np.ones((i.size, sk), dtype=bool)
+    if right >= 0:
+        vis &= j[None, :] <= (i[:, None] + (sk - sq) + right)
+    if left >= 0:
+        vis &= j[None, :] >= (i[:, None] + (sk - sq) - left)
+    return vis
 
 
 def dense_mla_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Sequence[int],
                       cu_k: Sequence[int], scale: float, causal: bool,
                       sink: Optional[np.ndarray] = None,
-                      heads: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                      heads: Optional[Iterable[int]] = None,
+                      window: Tuple[int, int] = (-1, -1)) -> Tuple[np.ndarray, np.ndarray]:
     """Dense varlen attention, per sequence and head, straight from the definition.
 
     q [Tq, H, Dqk], k [Tk, H, Dqk], v [Tk, H, Dv] (float64 or bf16 bits). Sequence b owns query
     rows cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1]. For query i of sequence b and head h:
-    s_j = scale * <q_i, k_j> over all Dqk columns, visible keys per R3, softmax with the optional
+    s_j = scale * <q_i, k_j> over all Dqk columns, visible keys per R3/R12, softmax with the optional
     sink (R6), O = sum_j p_j v_j, LSE = log(sum exp). Returns O [Tq, H, Dv] and LSE [Tq, H]
     (rows of heads not requested stay NaN).
     """
@@ -123,7 +138,7 @@ def dense_mla_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Sequenc
         sq, sk = q1 - q0, k1 - k0
         if sq == 0:
             continue
-        vis = dense_visible(sq, sk, causal)
+        vis = dense_visible(sq, sk, causal, window=window)
         for h in heads:
             scores = scale * (q[q0:q1, h, :] @ k[k0:k1, h, :].T)
             s = None if sink is None else float(sink[h])
@@ -136,7 +151,8 @@ def dense_mla_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Sequenc
 def dense_mla_prefill_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Sequence[int],
                            cu_k: Sequence[int], scale: float, causal: bool,
                            tokens: Sequence[int], heads: Sequence[int],
-                           sink: Optional[np.ndarray] = None) -> Tuple[np.ndarray, np.ndarray]:
+                           sink: Optional[np.ndarray] = None,
+                           window: Tuple[int, int] = (-1, -1)) -> Tuple[np.ndarray, np.ndarray]:
     """The same definition evaluated only at the given (token, head) grid: O [n_tok, n_head, Dv],
     LSE [n_tok, n_head]. Used to check large problems at sampled rows."""
     cu_q = np.asarray(cu_q)
@@ -149,7 +165,7 @@ def dense_mla_prefill_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Se
         q0, k0, k1 = int(cu_q[b]), int(cu_k[b]), int(cu_k[b + 1])
         sq, sk = int(cu_q[b + 1]) - q0, k1 - k0
         i = int(t) - q0
-        vis = dense_visible(sq, sk, causal, rows=np.array([i]))
+        vis = dense_visible(sq, sk, causal, rows=np.array([i]), window=window)
         for hi, h in enumerate(heads):
             qrow = _as_f64(q[t, h, :])[None, :]
             scores = scale * (qrow @ _as_f64(k[k0:k1, h, :]).T)

@@ -17,9 +17,13 @@ Slots: ``slot = b * Mt + m`` for sequence ``b`` in [0, B) and query tile ``m`` i
 ``Mt = ceil(max_seqlen_q / BM)``. A slot is a work item iff ``m * BM < Sq_b``.
 
 For an item: ``kv_end`` is the number of leading keys any row of the tile can see:
-``Sk_b`` without a causal mask; with the bottom-right causal mask it is
-``clamp(i_last + Sk_b - Sq_b + 1, 0, Sk_b)`` where ``i_last = min((m+1)*BM, Sq_b) - 1``.
-``n_blocks = ceil(kv_end / BN)``.
+``Sk_b`` without a right limit; with the bottom-right causal mask (right window 0) or a right
+window ``r >= 0`` it is ``clamp(i_last + Sk_b - Sq_b + r + 1, 0, Sk_b)`` where
+``i_last = min((m+1)*BM, Sq_b) - 1``. With a left window ``l >= 0`` the first key any row can see
+is ``kv_start = clamp(m*BM + Sk_b - Sq_b - l, 0, Sk_b)`` (else 0). ``n_blocks`` counts the key
+blocks from ``kv_start // BN`` up to ``ceil(kv_end / BN)``, and is 0 when ``kv_end <= kv_start``;
+without a left window it is ``ceil(kv_end / BN)``. The dense kernel recomputes ``kv_start // BN``
+from ``(m, Sq_b, Sk_b, l)``.
 
 Each item is four int32 words ``(b, m, n_blocks, kv_end)``. Items are ordered longest first:
 by ``n_blocks`` descending, ties by slot ascending. When there are more than ``SORT_CAPACITY``
@@ -36,8 +40,12 @@ MAX_BLOCKS = 0x3FFFE
 
 
 def plan_items(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: int, bn: int,
-               causal: bool) -> list:
-    """The work items as (b, m, n_blocks, kv_end) tuples, in plan order."""
+               causal: bool, window: Tuple[int, int] = (-1, -1)) -> list:
+    """The work items as (b, m, n_blocks, kv_end) tuples, in plan order; window = (left, right),
+    -1 = unlimited, causal forces right = 0."""
+    left, right = int(window[0]), int(window[1])
+    if causal:
+        right = 0
     b_count = len(cu_q) - 1
     mt = -(-int(max_seqlen_q) // bm) if max_seqlen_q > 0 else 0
     items = []
@@ -47,12 +55,13 @@ def plan_items(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: 
         for m in range(mt):
             if m * bm >= sq:
                 continue
-            if causal:
+            if right >= 0:
                 i_last = min((m + 1) * bm, sq) - 1
-                kv_end = min(max(i_last + sk - sq + 1, 0), sk)
+                kv_end = min(max(i_last + sk - sq + right + 1, 0), sk)
             else:
                 kv_end = sk
-            n_blocks = -(-kv_end // bn)
+            kv_start = min(max(m * bm + sk - sq - left, 0), sk) if left >= 0 else 0
+            n_blocks = 0 if kv_end <= kv_start else -(-kv_end // bn) - kv_start // bn
             items.append((b * mt + m, (b, m, n_blocks, kv_end)))
     if b_count * mt <= SORT_CAPACITY:
         items.sort(key=lambda it: (-it[1][2], it[0]))
@@ -60,9 +69,9 @@ def plan_items(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: 
 
 
 def plan_buffer(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: int, bn: int,
-                causal: bool, capacity: int) -> Tuple[np.ndarray, int]:
+                causal: bool, capacity: int, window: Tuple[int, int] = (-1, -1)) -> Tuple[np.ndarray, int]:
     """The full plan buffer (int32 [capacity, 4]) and the item count."""
-    items = plan_items(cu_q, cu_k, max_seqlen_q, bm, bn, causal)
+    items = plan_items(cu_q, cu_k, max_seqlen_q, bm, bn, causal, window)
     if len(items) > capacity:
         raise ValueError("plan capacity too small")
     buf = np.full((capacity, 4), -1, dtype=np.int32)

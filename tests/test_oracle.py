@@ -271,6 +271,66 @@ def test_sparse_brute_force_with_topk_length_and_duplicates():
             np.testing.assert_allclose(o[ti, hi], softmax(lg)[:-1] @ np.array(vals), atol=1e-12)
 
 
+# ---------------------------------------------------------------- sliding window (R12)
+def test_window_special_cases_reduce_to_causal_and_full():
+    """(-1, -1) is the unmasked rule, (-1, 0) the bottom-right causal rule, causal overrides a
+    given right window, and a window wider than the sequence changes nothing."""
+    for sq, sk in [(5, 9), (9, 9), (7, 3)]:
+        full = O.dense_visible(sq, sk, False)
+        caus = O.dense_visible(sq, sk, True)
+        assert np.array_equal(O.dense_visible(sq, sk, False, window=(-1, -1)), full)
+        assert np.array_equal(O.dense_visible(sq, sk, False, window=(-1, 0)), caus)
+        assert np.array_equal(O.dense_visible(sq, sk, True, window=(-1, 5)), caus)
+        assert np.array_equal(O.dense_visible(sq, sk, False, window=(sk + sq, sk + sq)), full)
+        assert np.array_equal(O.dense_visible(sq, sk, True, window=(sk + sq, 3)), caus)
+
+
+def test_window_brute_force_band_and_sparse_equivalence():
+    """A band of left 3 / right 1 by brute force (math.exp over an explicit list of visible keys),
+    and the same rows as sparse top-k attention over the enumerated key indices (the sparse
+    definition is pinned separately)."""
+    rng = np.random.default_rng(91)
+    sq, sk, h, d, dv = 6, 9, 2, 5, 3
+    q = rng.standard_normal((sq, h, d))
+    k = rng.standard_normal((sk, h, d))
+    v = rng.standard_normal((sk, h, dv))
+    scale, left, right = 0.6, 3, 1
+    o, lse = O.dense_mla_prefill(q, k, v, [0, sq], [0, sk], scale, False, window=(left, right))
+    off = sk - sq
+    for i in range(sq):
+        keys = [j for j in range(sk) if i + off - left <= j <= i + off + right]
+        for hh in range(h):
+            lg = [scale * sum(q[i, hh, x] * k[j, hh, x] for x in range(d)) for j in keys]
+            z = sum(math.exp(a) for a in lg)
+            want = sum(math.exp(a) * v[j, hh] for a, j in zip(lg, keys)) / z
+            np.testing.assert_allclose(o[i, hh], want, atol=1e-12)
+            np.testing.assert_allclose(lse[i, hh], math.log(z), atol=1e-12)
+        # the same row as sparse attention over the enumerated indices, head by head (one shared
+        # "latent" row per key: concatenate k and v of that head)
+        for hh in range(h):
+            kv = np.concatenate([v[:, hh, :], k[:, hh, :]], axis=1)   # value columns first
+            qq = np.concatenate([np.zeros((1, 1, dv)), q[i:i + 1, hh:hh + 1, :]], axis=2)
+            idx = np.array([keys + [-1] * (sk - len(keys))], dtype=np.int32)
+            so, sl = O.sparse_mla_prefill(qq, kv, idx, scale, dv=dv)
+            np.testing.assert_allclose(so[0, 0], o[i, hh], atol=1e-12)
+            np.testing.assert_allclose(sl[0, 0], lse[i, hh], atol=1e-12)
+
+
+def test_window_rows_with_no_key_are_empty():
+    """A left window of 0 with right -1 on Sq > Sk leaves the rows before the diagonal with no key."""
+    rng = np.random.default_rng(92)
+    q = rng.standard_normal((5, 1, 4)); k = rng.standard_normal((2, 1, 4)); v = rng.standard_normal((2, 1, 3))
+    o, lse = O.dense_mla_prefill(q, k, v, [0, 5], [0, 2], 1.0, False, window=(0, -1))
+    # d = -3: row i sees keys j >= i - 3 -> rows 0..3 see keys, row 4 sees j >= 1 only
+    vis = O.dense_visible(5, 2, False, window=(0, -1))
+    assert vis.tolist() == [[True, True], [True, True], [True, True], [True, True], [False, True]]
+    o2, lse2 = O.dense_mla_prefill(q, k, v, [0, 5], [0, 2], 1.0, False, window=(0, 0))
+    # band (0, 0): only j == i - 3 -> rows 3, 4 see one key each, rows 0..2 none
+    assert np.isneginf(lse2[:3]).all() and np.all(o2[:3] == 0)
+    np.testing.assert_allclose(o2[3, 0], v[0, 0], atol=1e-12)
+    np.testing.assert_allclose(o2[4, 0], v[1, 0], atol=1e-12)
+
+
 # ---------------------------------------------------------------- paged latent cache (R11)
 def _paged_case(rng, block_size, lens_kv, n_tok_per_seq, topk, d=6, num_blocks_extra=3):
     """Per-sequence contiguous KV scattered into a shuffled block pool, with its block table."""

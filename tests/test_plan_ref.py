@@ -42,6 +42,35 @@ def test_plan_items_cover_and_order(lens_q, lens_k, causal, bm, bn):
     assert keys == sorted(keys)
 
 
+@pytest.mark.parametrize("lens_q,lens_k,causal,window,bm,bn", [
+    ([1726, 583, 280], None, True, (256, -1), 128, 64),
+    ([300, 5, 129], [700, 7, 129], False, (100, 30), 64, 32),
+    ([2048, 100], [4096, 100], False, (0, 0), 128, 64),
+    ([513, 64], [513, 1000], False, (-1, 17), 128, 64),
+    ([200], [50], True, (10, -1), 64, 64),               # many rows see nothing
+])
+def test_plan_items_window_extent_brute_force(lens_q, lens_k, causal, window, bm, bn):
+    """With a (left, right) window the block range of each item is exactly the span of keys some
+    row of its tile can see, by brute force over the oracle's visibility mask (reading R12)."""
+    lens_k = lens_q if lens_k is None else lens_k
+    cu_q, cu_k = cu_from_lens(lens_q), cu_from_lens(lens_k)
+    items = plan_ref.plan_items(cu_q, cu_k, max(lens_q), bm, bn, causal, window)
+    assert len(items) == sum(-(-sq // bm) for sq in lens_q)
+    for (b, m, nb, kv_end) in items:
+        sq, sk = lens_q[b], lens_k[b]
+        rows = np.arange(m * bm, min((m + 1) * bm, sq))
+        cols = np.nonzero(dense_visible(sq, sk, causal, rows=rows, window=window).any(axis=0))[0]
+        if cols.size == 0:
+            assert nb == 0
+            continue
+        lo_blk, hi_blk = int(cols.min()) // bn, -(-(int(cols.max()) + 1) // bn)
+        assert kv_end == int(cols.max()) + 1
+        assert nb == hi_blk - lo_blk
+        left = window[0]
+        kv_start = min(max(m * bm + sk - sq - left, 0), sk) if left >= 0 else 0
+        assert kv_start // bn == lo_blk
+
+
 def test_plan_buffer_fill_and_capacity():
     cu = cu_from_lens([3, 200])
     buf, n = plan_ref.plan_buffer(cu, cu, 200, 64, 64, True, capacity=10)
