@@ -40,26 +40,25 @@ CALIB = {}                    # measured device rates (filled in by main unless 
 
 
 # ----------------------------------------------------------------------------- work counting
-def dense_pairs(lens_q, lens_k, causal: bool) -> int:
-    """Visible (query, key) pairs: bottom-right causal, or all pairs."""
+def dense_pairs(lens_q, lens_k, causal: bool, window=(-1, -1)) -> int:
+    """Visible (query, key) pairs: bottom-right causal, an optional (left, right) window (-1 =
+    unlimited, causal = right 0), or all pairs."""
+    import numpy as np
+    left, right = int(window[0]), int(window[1])
+    if causal:
+        right = 0
     total = 0
     for sq, sk in zip(lens_q, lens_k):
-        if not causal:
-            total += sq * sk
-            continue
-        for_all = 0
-        # row i sees min(sk, max(0, i + sk - sq + 1)) keys
-        lo = max(0, sq - sk)                      # rows before this see nothing
-        # rows lo..sq-1 see (i + sk - sq + 1) keys, capped at sk (never exceeds since i < sq)
-        n = sq - lo
-        first = lo + sk - sq + 1
-        for_all = n * first + n * (n - 1) // 2
-        total += for_all
+        i = np.arange(sq, dtype=np.int64)
+        d = sk - sq
+        hi = np.minimum(sk - 1, i + d + right) if right >= 0 else np.full(sq, sk - 1, dtype=np.int64)
+        lo = np.maximum(0, i + d - left) if left >= 0 else np.zeros(sq, dtype=np.int64)
+        total += int(np.maximum(hi - lo + 1, 0).sum())
     return total
 
 
-def dense_flops(lens_q, lens_k, heads, causal) -> float:
-    return float(2 * (DQK + DV) * heads * dense_pairs(lens_q, lens_k, causal))
+def dense_flops(lens_q, lens_k, heads, causal, window=(-1, -1)) -> float:
+    return float(2 * (DQK + DV) * heads * dense_pairs(lens_q, lens_k, causal, window))
 
 
 def dense_bytes(lens_q, lens_k, heads, lse=True) -> float:
@@ -143,7 +142,7 @@ def warm_cold(step, reps: int):
     return res
 
 
-def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_splits=0):
+def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_splits=0, window=None):
     import torch
     import mla_varlen_prefill_amd as mla
     from workloads import device_dense
@@ -157,12 +156,12 @@ def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_spli
 
     def step():
         mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal=True,
-                               num_splits=num_splits, out=out, lse=lse, workspace=ws)
+                               num_splits=num_splits, out=out, lse=lse, workspace=ws, window=window)
 
     settle(step)
     ms, kms, _ = time_steps(step, steps, warmup, "dense")
     wc = warm_cold(step, max(3, min(steps, 7)))
-    fl = dense_flops(lens_q, lens_k, heads, True)
+    fl = dense_flops(lens_q, lens_k, heads, True, window if window is not None else (-1, -1))
     by = dense_bytes(lens_q, lens_k, heads)
     splits = mla.varlen_num_splits(len(lens_q), max_q, max_k, heads, True, num_splits)
     del q, k, v, out, lse, ws
@@ -291,7 +290,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--only", default=None,
                     help="run one workload and print its line: dense_varlen, dense_long, dense_chunked, "
-                         "dense_small, sparse, sparse_paged, copy (a plain 1 GiB device copy for counter "
+                         "dense_small, dense_window, sparse, sparse_paged, copy (a plain 1 GiB device copy for counter "
                          "calibration)")
     args = ap.parse_args()
 
@@ -323,7 +322,7 @@ def main():
         return
 
     if not args.no_calib and args.only in (None, "dense_varlen", "dense_long", "dense_chunked",
-                                           "dense_small", "sparse", "sparse_paged"):
+                                           "dense_small", "dense_window", "sparse", "sparse_paged"):
         from mla_varlen_prefill_amd import calib
         CALIB["mfma_loop_tflops"] = round(calib.mfma_tflops(), 1)
         CALIB["stream_read_gbps"] = round(calib.stream_read_gbps(), 1)
@@ -339,6 +338,8 @@ def main():
                                                      args.steps, args.warmup),
             "sparse": lambda: sparse_case(args.steps, args.warmup),
             "sparse_paged": lambda: sparse_paged_case(args.steps, args.warmup),
+            "dense_window": lambda: dense_device_case("dense_window_1x32768_h128_w4096", [32768], [32768], 128,
+                                                      3, args.steps, args.warmup, window=(4096, -1)),
         }
         print(json.dumps(sec_runs[args.only]()), flush=True)
         return
@@ -407,6 +408,8 @@ def main():
         sec.append(dense_device_case("dense_long_1x32768_h128", [32768], [32768], 128, 3, ss, sw))
         sec.append(dense_device_case("dense_chunked_b4_q2048", [2048] * 4, [16384, 12345, 8191, 4097],
                                      128, 4, ss, sw))
+        sec.append(dense_device_case("dense_window_1x32768_h128_w4096", [32768], [32768], 128, 3, ss, sw,
+                                     window=(4096, -1)))
         sec.append(sparse_case(ss, sw))
         sec.append(sparse_paged_case(ss, sw))
         result["secondary"] = sec

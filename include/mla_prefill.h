@@ -62,22 +62,26 @@ void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n);
  *
  * Slots are (b, m) for b < batch and m < Mt = ceil(max_seqlen_q / block_m); slot (b, m) is an
  * item iff m * block_m < Sq_b. Each item is four int32 words (b, m, n_blocks, kv_end): kv_end is
- * the count of leading keys any row of the tile may see (Sk_b when causal == 0, else the
- * bottom-right causal bound clamp(i_last + Sk_b - Sq_b + 1, 0, Sk_b) with i_last the tile's last
- * row) and n_blocks = ceil(kv_end / block_n). Items are ordered by n_blocks descending, then by
- * slot (b * Mt + m) ascending; with more than 16384 slots they stay in slot order. Words of
- * unused items up to plan_capacity are set to -1.
+ * the count of leading keys any row of the tile may see (Sk_b without a right limit, else the
+ * bottom-right bound clamp(i_last + Sk_b - Sq_b + r + 1, 0, Sk_b) with i_last the tile's last
+ * row and r the right window, 0 when causal). With a left window l >= 0 the first key any row
+ * may see is kv_start = clamp(m * block_m + Sk_b - Sq_b - l, 0, Sk_b), else 0; n_blocks counts
+ * the blocks from kv_start / block_n to ceil(kv_end / block_n) (0 when kv_end <= kv_start).
+ * Items are ordered by n_blocks descending, then by slot (b * Mt + m) ascending; with more than
+ * 16384 slots they stay in slot order. Words of unused items up to plan_capacity are set to -1.
  *
  *   cu_seqlens_q, cu_seqlens_k : device int32 [batch + 1], non-decreasing, starting at 0.
+ *   causal, window_left, window_right : the mask rule of mla_prefill_varlen_window.
  *   plan                       : device int32 [plan_capacity * 4], written.
  *   num_items                  : device int32 [1], written.
  * Errors: INVALID_ARG for null pointers, batch < 0, max_seqlen_q < 0, block sizes that are not
- * powers of two in [16, 1024], or plan_capacity < batch * Mt.
+ * powers of two in [16, 1024], plan_capacity < batch * Mt, or a window below -1.
  * ------------------------------------------------------------------------------------------ */
 mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                               int32_t batch, int32_t max_seqlen_q, int32_t block_m,
-                              int32_t block_n, int32_t causal, int32_t* plan,
-                              int32_t plan_capacity, int32_t* num_items, void* hip_stream);
+                              int32_t block_n, int32_t causal, int32_t window_left,
+                              int32_t window_right, int32_t* plan, int32_t plan_capacity,
+                              int32_t* num_items, void* hip_stream);
 
 /* ------------------------------------------------------------------------------------------
  * Dense varlen MLA prefill.
@@ -131,6 +135,33 @@ mla_status_t mla_prefill_varlen(
     int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
     int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
     float softmax_scale, int32_t causal, int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Dense varlen MLA prefill with a sliding-window (band) mask.
+ *
+ * mla_prefill_varlen with a window (page "Sgl project Sglang FA4 Interface", window_size =
+ * (left, right), e.g. (256, 0) = causal with a 256-key window; page "SparseFlashMla",
+ * ori_win_left / ori_win_right: past / future tokens a query sees, -1 = unlimited). Aligned
+ * bottom-right like the causal mask: with d = Sk_b - Sq_b, key j is visible to local query i iff
+ * j >= i + d - window_left (when window_left >= 0) and j <= i + d + window_right (when
+ * window_right >= 0); causal != 0 sets window_right to 0. (-1, -1) without causal is the
+ * unmasked rule and equals mla_prefill_varlen. Rows with no visible key get O = 0 and
+ * LSE = -inf (or the sink). Key blocks outside every row's window are not read. Arguments,
+ * workspace (mla_prefill_varlen_workspace_size), outputs and errors as for mla_prefill_varlen,
+ * plus INVALID_ARG for a window below -1.
+ * ------------------------------------------------------------------------------------------ */
+mla_status_t mla_prefill_varlen_window(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+    int32_t num_splits, const float* sink,
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream);

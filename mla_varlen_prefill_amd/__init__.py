@@ -8,6 +8,7 @@ gfx950 GPU, every call raises.
 
 Entry points (same names as the C ABI):
   mla_prefill_varlen  dense varlen prefill, q/k 192 = 128 nope + 64 rope, v 128, causal or not
+  mla_prefill_varlen_window  the same with a (left, right) sliding-window band mask
   mla_prefill_sparse  sparse top-k prefill over one shared 576-wide latent KV (v = first 512)
   mla_prefill_sparse_paged  the same over a paged latent cache with logical indices
   mla_combine         merge split partial results through their LSEs
@@ -30,7 +31,8 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 
 EXPORTED_SYMBOLS = (
     "mla_status_string", "mla_abi_version", "mla_dense_tile_shape", "mla_prefill_plan",
-    "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_num_splits",
+    "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_window",
+    "mla_prefill_varlen_num_splits",
     "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_prefill_sparse_paged",
     "mla_combine",
     "mla_profile_enable", "mla_profile_read",
@@ -63,7 +65,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_dense_tile_shape.restype = None
     lib.mla_dense_tile_shape.argtypes = [ctypes.POINTER(_c_i32), ctypes.POINTER(_c_i32)]
     lib.mla_prefill_plan.restype = ctypes.c_int
-    lib.mla_prefill_plan.argtypes = [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _c_i32, _vp, _vp]
+    lib.mla_prefill_plan.argtypes = [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+                                     _vp, _c_i32, _vp, _vp]
     lib.mla_prefill_varlen_workspace_size.restype = _c_sz
     lib.mla_prefill_varlen_workspace_size.argtypes = [_c_i32] * 8
     lib.mla_prefill_varlen_num_splits.restype = _c_i32
@@ -73,6 +76,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
         _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
         _c_f32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_sz, _vp]
+    lib.mla_prefill_varlen_window.restype = ctypes.c_int
+    lib.mla_prefill_varlen_window.argtypes = [
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+        _c_f32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp,
+        _c_sz, _vp]
     lib.mla_prefill_sparse_workspace_size.restype = _c_sz
     lib.mla_prefill_sparse_workspace_size.argtypes = [_c_i32] * 4
     lib.mla_prefill_sparse.restype = ctypes.c_int
@@ -125,7 +134,8 @@ def dense_tile_shape() -> Tuple[int, int]:
 
 def mla_prefill_plan(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max_seqlen_q: int,
                      causal: bool, block_m: Optional[int] = None, block_n: Optional[int] = None,
-                     capacity: Optional[int] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+                     capacity: Optional[int] = None,
+                     window: Tuple[int, int] = (-1, -1)) -> Tuple[torch.Tensor, torch.Tensor]:
     """Run the GPU planner; returns (plan int32 [capacity, 4], num_items int32 [1])."""
     lib = load_library()
     _require_cuda(cu_seqlens_q, cu_seqlens_k)
@@ -139,7 +149,7 @@ def mla_prefill_plan(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max
     n = torch.empty(1, dtype=torch.int32, device=cu_seqlens_q.device)
     _check("mla_prefill_plan", lib.mla_prefill_plan(
         _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, max_seqlen_q, bm, bn, int(bool(causal)),
-        _ptr(plan), cap, _ptr(n), _stream()))
+        int(window[0]), int(window[1]), _ptr(plan), cap, _ptr(n), _stream()))
     return plan[:cap], n
 
 
@@ -161,10 +171,12 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        causal: bool = True, num_splits: int = 0,
                        sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                        return_lse: bool = True, lse: Optional[torch.Tensor] = None,
-                       workspace: Optional[torch.Tensor] = None):
+                       workspace: Optional[torch.Tensor] = None,
+                       window: Optional[Tuple[int, int]] = None):
     """Dense varlen MLA prefill. q [Tq,H,192], k [Tk,H,192], v [Tk,H,128] bf16 (last dim
-    contiguous; V may be strided); cu_seqlens int32 [B+1]. Returns out [Tq,H,128] bf16 and, when
-    ``return_lse``, lse float32 [Tq,H]."""
+    contiguous; V may be strided); cu_seqlens int32 [B+1]. With ``window`` = (left, right)
+    (-1 = unlimited) the sliding-window entry point mla_prefill_varlen_window is called. Returns
+    out [Tq,H,128] bf16 and, when ``return_lse``, lse float32 [Tq,H]."""
     lib = load_library()
     _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, sink, out, lse, workspace)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -185,15 +197,28 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
     if sink is not None and (sink.dtype != torch.float32 or not sink.is_contiguous()):
         raise ValueError("sink must be a contiguous float32 [H] tensor")
-    _check("mla_prefill_varlen", lib.mla_prefill_varlen(
-        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
-        _ptr(v), v.stride(0), v.stride(1), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
-        batch, total_q, max_seqlen_q, max_seqlen_k, heads, dqk, dv,
-        float(softmax_scale), int(bool(causal)), num_splits, _ptr(sink),
-        _ptr(out), out.stride(0), out.stride(1),
-        _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
-        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    head = (_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
+            _ptr(v), v.stride(0), v.stride(1), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
+            batch, total_q, max_seqlen_q, max_seqlen_k, heads, dqk, dv,
+            float(softmax_scale), int(bool(causal)))
+    tail = (num_splits, _ptr(sink), _ptr(out), out.stride(0), out.stride(1),
+            _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
+            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
+    if window is None:
+        _check("mla_prefill_varlen", lib.mla_prefill_varlen(*head, *tail))
+    else:
+        _check("mla_prefill_varlen_window",
+               lib.mla_prefill_varlen_window(*head, int(window[0]), int(window[1]), *tail))
     return (out, lse) if return_lse else out
+
+
+def mla_prefill_varlen_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                              cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                              max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                              causal: bool, window_left: int, window_right: int, **kw):
+    """Dense varlen MLA prefill with a (left, right) sliding window, -1 = unlimited."""
+    return mla_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                              softmax_scale, causal=causal, window=(window_left, window_right), **kw)
 
 
 def mla_prefill_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,

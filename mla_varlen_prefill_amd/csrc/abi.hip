@@ -203,19 +203,23 @@ void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n) {
 
 mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
                               int32_t batch, int32_t max_seqlen_q, int32_t block_m,
-                              int32_t block_n, int32_t causal, int32_t* plan,
-                              int32_t plan_capacity, int32_t* num_items, void* hip_stream) {
+                              int32_t block_n, int32_t causal, int32_t window_left,
+                              int32_t window_right, int32_t* plan, int32_t plan_capacity,
+                              int32_t* num_items, void* hip_stream) {
   if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr || plan == nullptr || num_items == nullptr)
     return MLA_ERR_INVALID_ARG;
   auto pow2 = [](int32_t x) { return x >= 16 && x <= 1024 && (x & (x - 1)) == 0; };
-  if (batch < 0 || max_seqlen_q < 0 || !pow2(block_m) || !pow2(block_n) || plan_capacity < 0)
+  if (batch < 0 || max_seqlen_q < 0 || !pow2(block_m) || !pow2(block_n) || plan_capacity < 0 ||
+      window_left < -1 || window_right < -1)
     return MLA_ERR_INVALID_ARG;
+  const int32_t right = causal ? 0 : window_right;
   const int64_t mt = cdiv(max_seqlen_q, block_m);
   if ((int64_t)batch * mt > plan_capacity) return MLA_ERR_INVALID_ARG;
   if (!aligned16(plan)) return MLA_ERR_ALIGNMENT;
   if (device_info() == nullptr) return MLA_ERR_HIP;
   mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, (int32_t)mt, block_m, block_n,
-                     causal ? 1 : 0, plan, plan_capacity, num_items};
+                     right >= 0 ? 1 : 0, right >= 0 ? right : 0, window_left,
+                     plan, plan_capacity, num_items};
   return timed_launch(MLA_KERNEL_PLAN, (hipStream_t)hip_stream,
                       [&] { return mla::launch_plan(pp, (hipStream_t)hip_stream); }) == hipSuccess
              ? MLA_OK
@@ -240,14 +244,15 @@ size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t
   return varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits).total;
 }
 
-mla_status_t mla_prefill_varlen(
+static mla_status_t varlen_call(
     const void* q, int64_t q_stride_tok, int64_t q_stride_head,
     const void* k, int64_t k_stride_tok, int64_t k_stride_head,
     const void* v, int64_t v_stride_tok, int64_t v_stride_head,
     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
     int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
     int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
-    float softmax_scale, int32_t causal, int32_t num_splits, const float* sink,
+    float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+    int32_t num_splits, const float* sink,
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream) {
@@ -255,8 +260,10 @@ mla_status_t mla_prefill_varlen(
       cu_seqlens_k == nullptr || out == nullptr)
     return MLA_ERR_INVALID_ARG;
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads <= 0 ||
-      num_splits < 0 || num_splits > kMaxSplits || !std::isfinite(softmax_scale))
+      num_splits < 0 || num_splits > kMaxSplits || !std::isfinite(softmax_scale) ||
+      window_left < -1 || window_right < -1)
     return MLA_ERR_INVALID_ARG;
+  const int32_t right = causal ? 0 : window_right;  // causal is the right window 0
   if (head_dim_qk != kDenseDqk || head_dim_v != kDenseDv || num_heads > 65535 ||
       max_seqlen_k > (1 << 24) || k_stride_tok >= (1 << 23) || v_stride_tok >= (1 << 23))
     return MLA_ERR_UNSUPPORTED;  // key-block byte offsets are kept in 31 bits
@@ -290,8 +297,8 @@ mla_status_t mla_prefill_varlen(
 
   int32_t* tickets = reinterpret_cast<int32_t*>(ws + L.off_tickets);
   int32_t* plan_ext = reinterpret_cast<int32_t*>(ws + L.off_plan_ext);
-  mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, L.mt, L.bm, kDenseBN, causal ? 1 : 0,
-                     plan, L.n_slots, num_items, tickets, plan_ext};
+  mla::PlanParams pp{cu_seqlens_q, cu_seqlens_k, batch, L.mt, L.bm, kDenseBN, right >= 0 ? 1 : 0,
+                     right >= 0 ? right : 0, window_left, plan, L.n_slots, num_items, tickets, plan_ext};
   if (timed_launch(MLA_KERNEL_PLAN, stream, [&] { return mla::launch_plan(pp, stream); }) != hipSuccess)
     return MLA_ERR_HIP;
 
@@ -307,7 +314,9 @@ mla_status_t mla_prefill_varlen(
   dp.n_slots = L.n_slots;
   dp.num_heads = num_heads;
   dp.num_splits = L.splits;
-  dp.causal = causal ? 1 : 0;
+  dp.causal = right >= 0 ? 1 : 0;
+  dp.win_right = right >= 0 ? right : 0;
+  dp.win_left = window_left;
   dp.scale = softmax_scale;
   dp.scale_log2 = softmax_scale * 1.4426950408889634f;
   dp.sink = sink;
@@ -353,6 +362,43 @@ mla_status_t mla_prefill_varlen(
       return MLA_ERR_HIP;
   }
   return MLA_OK;
+}
+
+mla_status_t mla_prefill_varlen(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
+                     v_stride_head, cu_seqlens_q, cu_seqlens_k, batch, total_q, max_seqlen_q,
+                     max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal, -1, -1,
+                     num_splits, sink, out, o_stride_tok, o_stride_head, lse, lse_stride_tok,
+                     lse_stride_head, workspace, workspace_bytes, hip_stream);
+}
+
+mla_status_t mla_prefill_varlen_window(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+    int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
+                     v_stride_head, cu_seqlens_q, cu_seqlens_k, batch, total_q, max_seqlen_q,
+                     max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal,
+                     window_left, window_right, num_splits, sink, out, o_stride_tok, o_stride_head,
+                     lse, lse_stride_tok, lse_stride_head, workspace, workspace_bytes, hip_stream);
 }
 
 size_t mla_prefill_sparse_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,

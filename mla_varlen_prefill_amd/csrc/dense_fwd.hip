@@ -115,6 +115,15 @@ __device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, const It
 // NMT: how many of the block's two 32-key tiles this wave computes (2, or 1 when the second tile
 // is entirely masked for every row of the wave; a wave with both tiles masked skips the block).
 // q_done(kk) runs right after the last product that reads the Q^T fragments qf[.][kk].
+// The kernel's arguments, re-read from the kernel-argument segment at each use: values needed
+// only once per work item are loaded there instead of being held in scalar registers for the
+// whole kernel (the optimiser cannot see through the empty asm, so it cannot hoist the loads).
+__device__ __forceinline__ const DenseParams& kargs() {
+  auto kp = (const __attribute__((address_space(4))) DenseParams*)__builtin_amdgcn_kernarg_segment_ptr();
+  asm volatile("" : "+s"(kp));
+  return *(const DenseParams*)kp;
+}
+
 template <int NQ, int NMT, bool MASK, class QDone>
 __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item& it, int j,
                                               const char* ks, const char* vs,
@@ -157,22 +166,29 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item&
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[nq][1][i] = -INFINITY;
   }
-  // ---- mask (diagonal and tail blocks only; wave-uniform test)
+  // ---- mask (diagonal, tail and left-window blocks only; wave-uniform test). Key j is visible
+  // to local row i iff j < Sk, j <= i + diag (when right-limited: causal or a right window, whose
+  // width is folded into diag) and j >= i + dleft (with a left window).
   const int key0 = j * BN;
   const int qmin = it.row0 + c.wave * 32 * NQ;  // smallest local query row of this wave
-  const int diag = it.sk - it.sq;                // bottom-right alignment offset
-  const bool need_mask = MASK && ((key0 + BN > it.sk) || (causal && key0 + BN - 1 > qmin + diag));
+  const int wl = kargs().win_left;
+  const int diag = it.sk - it.sq + kargs().win_right;  // bottom-right alignment offset (+ right window)
+  const int dleft = it.sk - it.sq - wl;
+  const bool need_mask = MASK && ((key0 + BN > it.sk) || (causal && key0 + BN - 1 > qmin + diag) ||
+                                  (wl >= 0 && key0 < qmin + 32 * NQ - 1 + dleft));
   if (need_mask) {
 #pragma unroll
     for (int nq = 0; nq < NQ; ++nq) {
       const int qrow = qmin + nq * 32 + c.l32;
-      const int lim = (causal ? min(it.sk - 1, qrow + diag) : (it.sk - 1)) - key0 - 4 * (int)(opaque(c.lane) >> 5);
+      const int half = 4 * (int)(opaque(c.lane) >> 5);
+      const int lim = (causal ? min(it.sk - 1, qrow + diag) : (it.sk - 1)) - key0 - half;
+      const int lo = (wl >= 0 ? qrow + dleft : -(1 << 30)) - key0 - half;
 #pragma unroll
       for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int kofs = mt * 32 + 8 * (i >> 2) + (i & 3);
-          if (kofs > lim) s[nq][mt][i] = -INFINITY;
+          if (kofs > lim || kofs < lo) s[nq][mt][i] = -INFINITY;
         }
     }
   }
@@ -265,15 +281,6 @@ __device__ __forceinline__ T ld_const(const T* ptr, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)ptr)[i];
 }
 
-// The kernel's arguments, re-read from the kernel-argument segment at each use: values needed
-// only once per work item are loaded there instead of being held in scalar registers for the
-// whole kernel (the optimiser cannot see through the empty asm, so it cannot hoist the loads).
-__device__ __forceinline__ const DenseParams& kargs() {
-  auto kp = (const __attribute__((address_space(4))) DenseParams*)__builtin_amdgcn_kernarg_segment_ptr();
-  asm volatile("" : "+s"(kp));
-  return *(const DenseParams*)kp;
-}
-
 // Decodes position i of the work list of XCD `xcd` (the positions are handed out by that XCD's
 // ticket counter). Work items are (plan item, unit) pairs with units u = h * num_splits + split.
 // When the units divide evenly over the XCDs, XCD k owns the contiguous units
@@ -325,8 +332,10 @@ __device__ __forceinline__ Item make_item(int item, int h, int split) {
   it.sk = f[3];
   it.row0 = m * 128 * NQ;
   it.rows = min(128 * NQ, it.sq - it.row0);
-  it.blo = (int)(((int64_t)split * nb) / p.num_splits);
-  it.bhi = (int)(((int64_t)(split + 1) * nb) / p.num_splits);
+  // with a left window the item's blocks start at the block of the first key its first row sees
+  const int blk0 = p.win_left >= 0 ? min(max(it.row0 + it.sk - it.sq - p.win_left, 0), it.sk) / BN : 0;
+  it.blo = blk0 + (int)(((int64_t)split * nb) / p.num_splits);
+  it.bhi = blk0 + (int)(((int64_t)(split + 1) * nb) / p.num_splits);
   it.h = h;
   it.split = split;
   it.kbase = reinterpret_cast<const char*>(p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh);
@@ -587,7 +596,7 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
       // Blocks before jd need no mask for any row of the tile: they hold no key past the sequence
       // end and, when causal, none past the bottom-right diagonal of the tile's first row. The
       // last two blocks always run in the later loops, which prepare the hand-over.
-      const int diag = cur.sk - cur.sq;
+      const int diag = cur.sk - cur.sq + p.win_right;
       int jd = cur.sk / BN;
       if (causal) {
         const int x = cur.row0 + diag - (BN - 1);
@@ -613,6 +622,20 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
         }
       };
       int j = cur.blo;
+      // With a left window, the blocks holding a key below the window of the tile's last row need
+      // the mask; they come first (at most up to the last block, which runs below).
+      if (p.win_left >= 0) {
+        const int x = cur.row0 + cur.rows - 1 + cur.sk - cur.sq - p.win_left;  // last row's first key
+        const int jl = min(x <= 0 ? 0 : (x + BN - 1) / BN, cur.bhi - 1);
+        for (; j < jl; ++j, st ^= 1) {
+          prepare(j);
+          block_step<NQ, 2, true>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st),
+                                  stage_v(st), qf, m_run, l_run, o, p.scale_log2, causal, no_q);
+          wait_vmem();
+          __syncthreads();
+          touch_done(touched);
+        }
+      }
       for (; j < jm; ++j, st ^= 1) {
         if (j == fetch_j) fetch();
         block_step<NQ, 2, false>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st), stage_v(st),

@@ -14,7 +14,9 @@ struct PlanParams {
   int32_t batch;
   int32_t mt;        // query tiles per sequence slot = ceil(max_seqlen_q / bm)
   int32_t bm, bn;
-  int32_t causal;
+  int32_t causal;    // right-limited: keys past the bottom-right diagonal + win_right are hidden
+  int32_t win_right; // >= 0 (0 when causal)
+  int32_t win_left;  // -1: unlimited; else keys before the diagonal - win_left are hidden
   int32_t* plan;     // [capacity][4]
   int32_t capacity;
   int32_t* num_items;
@@ -34,7 +36,9 @@ struct DenseParams {
   int32_t n_slots;       // plan capacity (batch * Mt)
   int32_t num_heads;
   int32_t num_splits;
-  int32_t causal;
+  int32_t causal;        // right-limited (causal, or a right window of win_right keys)
+  int32_t win_right;     // >= 0: keys up to diagonal + win_right are visible (0 when causal)
+  int32_t win_left;      // -1: unlimited; else keys from diagonal - win_left are visible
   float scale;           // softmax scale
   float scale_log2;      // softmax scale * log2(e)
   const float* sink;     // nullable [H]; applied here only when unsplit

@@ -6,7 +6,8 @@
 // set_buffer_lengths_to_zero); a metadata call producing a fixed-size int32 task split before
 // the attention call (page "SparseFlashMla", Description). The format is this library's own:
 // items (b, m, n_blocks, kv_end), longest first (n_blocks descending, then slot ascending),
-// unused entries -1. Longest-first dispatch keeps causal and varlen batches load-balanced.
+// unused entries -1. With a left window n_blocks counts from the block of the first key the
+// tile's first row sees (the dense kernel recomputes that block). Longest-first dispatch keeps causal and varlen batches load-balanced.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,10 +35,11 @@ __device__ __forceinline__ Item slot_item(const PlanParams& p, int s) {
   int kv_end = sk;
   if (p.causal) {
     const int i_last = min((it.m + 1) * p.bm, sq) - 1;
-    kv_end = min(max(i_last + sk - sq + 1, 0), sk);
+    kv_end = min(max(i_last + sk - sq + p.win_right + 1, 0), sk);
   }
+  const int kv_start = p.win_left >= 0 ? min(max(it.m * p.bm + sk - sq - p.win_left, 0), sk) : 0;
   it.kv_end = kv_end;
-  it.nb = (kv_end + p.bn - 1) / p.bn;
+  it.nb = kv_end <= kv_start ? 0 : (kv_end + p.bn - 1) / p.bn - kv_start / p.bn;
   return it;
 }
 

@@ -54,6 +54,29 @@ def _varlen(lib, **kw):
                                   a["lse"], a["lst"], a["lsh"], a["ws"], a["ws_bytes"], a["stream"])
 
 
+def _varlen_window(lib, wl, wr, **kw):
+    a = dict(q=P, qst=128 * 192, qsh=192, k=P, kst=128 * 192, ksh=192, v=P, vst=128 * 128, vsh=128,
+             cuq=P, cuk=P, batch=1, total_q=16, max_q=16, max_k=16, heads=128, dqk=192, dv=128,
+             scale=0.07, causal=0, splits=1, sink=None, out=P, ost=128 * 128, osh=128, lse=None,
+             lst=128, lsh=1, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.mla_prefill_varlen_window(
+        a["q"], a["qst"], a["qsh"], a["k"], a["kst"], a["ksh"], a["v"], a["vst"], a["vsh"], a["cuq"],
+        a["cuk"], a["batch"], a["total_q"], a["max_q"], a["max_k"], a["heads"], a["dqk"], a["dv"],
+        a["scale"], a["causal"], wl, wr, a["splits"], a["sink"], a["out"], a["ost"], a["osh"], a["lse"],
+        a["lst"], a["lsh"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_varlen_window_argument_errors():
+    """Windows below -1 are rejected; the other checks are those of mla_prefill_varlen."""
+    lib = mla.load_library()
+    assert _varlen_window(lib, -2, 0) == 1
+    assert _varlen_window(lib, 5, -3) == 1
+    assert _varlen_window(lib, 256, 0, dqk=128) == 2
+    assert _varlen_window(lib, 256, 0, q=P + 2) == 3
+    assert _varlen_window(lib, 256, 0, batch=0) == 0
+
+
 def test_varlen_argument_errors():
     lib = mla.load_library()
     assert _varlen(lib, q=None) == 1
@@ -150,9 +173,10 @@ def test_combine_and_plan_argument_errors():
     assert lib.mla_combine(*bad) == 1
     bad = list(args); bad[0] = P + 4
     assert lib.mla_combine(*bad) == 3
-    assert lib.mla_prefill_plan(P, P, 2, 300, 100, 64, 1, P, 100, P, None) == 1   # block_m not a power of 2
-    assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, P, 5, P, None) == 1     # capacity < 2*3
-    assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, P + 4, 6, P, None) == 3
+    assert lib.mla_prefill_plan(P, P, 2, 300, 100, 64, 1, -1, -1, P, 100, P, None) == 1  # block_m not a power of 2
+    assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, -1, -1, P, 5, P, None) == 1    # capacity < 2*3
+    assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, -2, -1, P, 6, P, None) == 1    # window below -1
+    assert lib.mla_prefill_plan(P, P, 2, 300, 128, 64, 1, -1, -1, P + 4, 6, P, None) == 3
 
 
 def test_calibration_library_exports():
