@@ -47,6 +47,16 @@ Readings taken where the pages are silent (each also listed with the design note
      unlimited, Band mask mode). Aligned bottom-right like R3, with d = Sk - Sq: key j is visible
      to query i iff j >= i + d - left (when left >= 0) and j <= i + d + right (when right >= 0).
      ``causal`` is the case right = 0 and overrides a given right.
+  R13 Context from the latent cache (page "FlashAttention backend for MLA prefill",
+     ``run_prefill_new_tokens`` / ``run_prefill_context_chunk``: new tokens attend causally to
+     themselves, context keys without a mask, the LSE merges the parts; page
+     "mla_prefill_branch_sparse_fp8": latent rows of 512 + 64 rope, ``w_uk`` / ``w_uv``
+     up-projections). The context key of head h at cached token t is
+     [c_t W_UK_h^T (128) || rope_t (64)] and its value is c_t W_UV_h^T (128), where c_t is the
+     512-wide latent and rope_t the last 64 columns of the cached row; W_KV is laid out like a
+     linear layer's weight, [H * 256, 512], rows h*256 + 0..127 for W_UK_h and h*256 + 128..255
+     for W_UV_h. The result for a new query is attention over [context keys || new keys] with
+     the bottom-right causal mask (R3), i.e. every context key plus the causal new keys.
   R11 Paged latent cache (page "SparseFlashMla": ``block_table`` for PageAttention, cache shape
      [block_num, block_size, KV_N, D], ``topk_value_mode`` 1 = logical token indices,
      ``seqused`` = valid KV length per sequence, ``cu_seqlens_q``). Token t belongs to sequence b
@@ -251,6 +261,36 @@ def sparse_mla_prefill_paged(q: np.ndarray, kv_cache: np.ndarray, block_table: n
     phys = paged_physical_indices(indices, block_table, block_size, num_blocks, cu_q, seqused)
     rows = np.asarray(kv_cache).reshape(num_blocks * block_size, d)
     return sparse_mla_prefill(q, rows, phys, scale, dv=dv, topk_length=topk_length, sink=sink, tokens=tokens)
+
+
+def upproject_latent(latent_rows: np.ndarray, w_kv: np.ndarray, heads: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Context K [n, H, 192] and V [n, H, 128] from cached latent rows [n, 576] (reading R13)."""
+    c = _as_f64(latent_rows)
+    w = _as_f64(w_kv).reshape(heads, 256, 512)
+    kv = np.einsum("nd,hcd->nhc", c[:, :512], w)           # [n, H, 256]
+    rope = np.broadcast_to(c[:, None, 512:576], (c.shape[0], heads, 64))
+    return np.concatenate([kv[:, :, :128], rope], axis=2), kv[:, :, 128:]
+
+
+def mla_prefill_with_latent_context(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray,
+                                    cu_q: Sequence[int], latent: np.ndarray, cu_ctx: Sequence[int],
+                                    w_kv: np.ndarray, scale: float,
+                                    sink: Optional[np.ndarray] = None,
+                                    heads: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+    """New tokens q [T, H, 192] (with their k_new [T, H, 192], v_new [T, H, 128]) attending to
+    their sequence's cached context (latent rows [cu_ctx[b]:cu_ctx[b+1]] of latent [N, 576],
+    up-projected by w_kv) and causally to themselves (reading R13). Returns O [T, H, 128] and
+    LSE [T, H]."""
+    h_all = np.asarray(q).shape[1]
+    k_parts, v_parts, cu_k = [], [], [0]
+    for b in range(len(cu_q) - 1):
+        kc, vc = upproject_latent(np.asarray(latent)[int(cu_ctx[b]):int(cu_ctx[b + 1])], w_kv, h_all)
+        k_parts += [kc, _as_f64(np.asarray(k_new)[int(cu_q[b]):int(cu_q[b + 1])])]
+        v_parts += [vc, _as_f64(np.asarray(v_new)[int(cu_q[b]):int(cu_q[b + 1])])]
+        cu_k.append(cu_k[-1] + kc.shape[0] + int(cu_q[b + 1]) - int(cu_q[b]))
+    k_all = np.concatenate(k_parts) if k_parts else np.zeros((0, h_all, 192))
+    v_all = np.concatenate(v_parts) if v_parts else np.zeros((0, h_all, 128))
+    return dense_mla_prefill(q, k_all, v_all, cu_q, cu_k, scale, True, sink=sink, heads=heads)
 
 
 def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray,

@@ -331,6 +331,77 @@ def test_window_rows_with_no_key_are_empty():
     np.testing.assert_allclose(o2[4, 0], v[1, 0], atol=1e-12)
 
 
+# ---------------------------------------------------------------- latent context (R13)
+def _latent_case(rng, ctx, new, h):
+    cu_q = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
+    cu_c = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    q = rng.standard_normal((cu_q[-1], h, 192)) * 0.3
+    kn = rng.standard_normal((cu_q[-1], h, 192)) * 0.3
+    vn = rng.standard_normal((cu_q[-1], h, 128))
+    lat = rng.standard_normal((cu_c[-1], 576))
+    return q, kn, vn, cu_q, lat, cu_c
+
+
+def test_latent_context_selector_weights_reduce_to_dense():
+    """With W_UK_h selecting latent columns 0..127 and W_UV_h columns 128..255, the context keys
+    are [latent[:, :128] || rope] and values latent[:, 128:256]: the result must equal the dense
+    definition on those explicitly built keys, with all context keys visible."""
+    rng = np.random.default_rng(101)
+    h = 2
+    q, kn, vn, cu_q, lat, cu_c = _latent_case(rng, [5, 0, 7], [3, 2, 4], h)
+    w = np.zeros((h, 256, 512))
+    for hh in range(h):
+        w[hh, :128, :128] = np.eye(128)
+        w[hh, 128:, 128:256] = np.eye(128)
+    o, lse = O.mla_prefill_with_latent_context(q, kn, vn, cu_q, lat, cu_c, w.reshape(h * 256, 512), 0.2)
+    for b in range(3):
+        c = lat[cu_c[b]:cu_c[b + 1]]
+        kc = np.repeat(np.concatenate([c[:, :128], c[:, 512:]], axis=1)[:, None, :], h, axis=1)
+        vc = np.repeat(c[:, None, 128:256], h, axis=1)
+        k_all = np.concatenate([kc, kn[cu_q[b]:cu_q[b + 1]]])
+        v_all = np.concatenate([vc, vn[cu_q[b]:cu_q[b + 1]]])
+        sq, sk = cu_q[b + 1] - cu_q[b], k_all.shape[0]
+        ro, rl = O.dense_mla_prefill(q[cu_q[b]:cu_q[b + 1]], k_all, v_all, [0, sq], [0, sk], 0.2, True)
+        np.testing.assert_allclose(o[cu_q[b]:cu_q[b + 1]], ro, atol=1e-12)
+        np.testing.assert_allclose(lse[cu_q[b]:cu_q[b + 1]], rl, atol=1e-12)
+
+
+def test_latent_context_equals_merge_of_context_and_new_token_passes():
+    """The pages' decomposition: an unmasked pass over the context keys and a causal pass over
+    the new tokens, merged through their LSEs (combine formula, pinned separately), equals the
+    single bottom-right causal pass over [context || new]."""
+    rng = np.random.default_rng(102)
+    h = 3
+    q, kn, vn, cu_q, lat, cu_c = _latent_case(rng, [6, 4], [4, 5], h)
+    w = rng.standard_normal((h * 256, 512)) * 0.05
+    sink = np.array([0.1, -0.4, 0.7])
+    o, lse = O.mla_prefill_with_latent_context(q, kn, vn, cu_q, lat, cu_c, w, 0.3, sink=sink)
+    for b in range(2):
+        kc, vc = O.upproject_latent(lat[cu_c[b]:cu_c[b + 1]], w, h)
+        qs = q[cu_q[b]:cu_q[b + 1]]
+        sq = qs.shape[0]
+        o1, l1 = O.dense_mla_prefill(qs, kc, vc, [0, sq], [0, kc.shape[0]], 0.3, False)
+        o2, l2 = O.dense_mla_prefill(qs, kn[cu_q[b]:cu_q[b + 1]], vn[cu_q[b]:cu_q[b + 1]], [0, sq], [0, sq], 0.3, True)
+        om, lm = O.combine_partials(np.stack([o1.reshape(-1, 128), o2.reshape(-1, 128)]),
+                                    np.stack([l1.reshape(-1), l2.reshape(-1)]), np.tile(sink, sq))
+        np.testing.assert_allclose(o[cu_q[b]:cu_q[b + 1]].reshape(-1, 128), om, atol=1e-12)
+        np.testing.assert_allclose(lse[cu_q[b]:cu_q[b + 1]].reshape(-1), lm, atol=1e-12)
+
+
+def test_latent_upprojection_brute_force():
+    """Element-wise sums for the up-projection and the rope broadcast on a tiny case."""
+    rng = np.random.default_rng(103)
+    lat = rng.standard_normal((2, 576))
+    w = rng.standard_normal((2 * 256, 512))
+    k, v = O.upproject_latent(lat, w, 2)
+    for t in range(2):
+        for hh in (0, 1):
+            for c in (0, 77, 127):
+                assert abs(k[t, hh, c] - sum(lat[t, d] * w[hh * 256 + c, d] for d in range(512))) < 1e-9
+                assert abs(v[t, hh, c] - sum(lat[t, d] * w[hh * 256 + 128 + c, d] for d in range(512))) < 1e-9
+            assert np.array_equal(k[t, hh, 128:], lat[t, 512:])
+
+
 # ---------------------------------------------------------------- paged latent cache (R11)
 def _paged_case(rng, block_size, lens_kv, n_tok_per_seq, topk, d=6, num_blocks_extra=3):
     """Per-sequence contiguous KV scattered into a shuffled block pool, with its block table."""
