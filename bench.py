@@ -208,6 +208,54 @@ def sparse_case(steps, warmup):
     return res
 
 
+def chunked_context_case(steps, warmup, chunk_tokens=4096):
+    """The chunked-prefill shape with its context in a latent cache: 4 sequences of 2048 new tokens
+    over 14336 / 10297 / 6143 / 2049 cached positions (so 16384 / 12345 / 8191 / 4097 keys in
+    all), 128 heads; the context is up-projected chunk by chunk (W_KV ~ N(0, 1/512))."""
+    import numpy as np
+    import torch
+    import mla_varlen_prefill_amd as mla
+    from workloads import device_dense, device_randn_bf16, cu_from_lens
+    new = [2048] * 4
+    ctx = [n - 2048 for n in (16384, 12345, 8191, 4097)]
+    h = 128
+    q, k, v, cu_q, _ = device_dense(new, new, h, 4)
+    latent = device_randn_bf16((sum(ctx), SP_D), 4, 9)
+    w_kv = (device_randn_bf16((h * 256, 512), 4, 10).float() * 512 ** -0.5).to(torch.bfloat16)
+    cu_c = torch.from_numpy(cu_from_lens(ctx)).cuda()
+    out = torch.empty((q.shape[0], h, DV), dtype=torch.bfloat16, device="cuda")
+    lse = torch.empty((q.shape[0], h), dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(mla.chunked_context_workspace_bytes(4, q.shape[0], 2048, h, chunk_tokens), 16),
+                     dtype=torch.uint8, device="cuda")
+
+    def step():
+        mla.mla_prefill_chunked_context(q, k, v, cu_q, latent, cu_c, w_kv, 2048, max(ctx), DQK ** -0.5,
+                                        chunk_tokens=chunk_tokens, out=out, lse=lse, workspace=ws)
+
+    settle(step)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    mla.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    kern = {name: mla.profile_read(name) for name in ("dense", "upproj", "merge", "combine")}
+    mla.profile_enable(False)
+    att = dense_flops(new, [c + n for c, n in zip(ctx, new)], h, True)
+    up = 2.0 * sum(ctx) * h * 256 * 512
+    del q, k, v, latent, w_kv, out, lse, ws
+    torch.cuda.empty_cache()
+    per_step = {name: round(t / steps, 4) for name, (t, n) in kern.items()}
+    return {"workload": f"chunked_context_b4_q2048_ctx14336..2049_h128_chunk{chunk_tokens}",
+            "ms_per_call": round(ms, 4), "attention_flop": att, "upproj_flop": up,
+            "tflops_attention_plus_upproj": round((att + up) / ms / 1e9, 2),
+            "kernel_ms_per_call": per_step,
+            "upproj_tflops": round(up / (per_step["upproj"] * 1e9), 2) if per_step["upproj"] > 0 else None}
+
+
 def sparse_paged_case(steps, warmup, block_size=64):
     """The sparse workload through a paged cache: the same latent rows scattered over shuffled
     pages of `block_size` rows, logical indices mapped through the block table in the kernel."""
@@ -290,7 +338,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--only", default=None,
                     help="run one workload and print its line: dense_varlen, dense_long, dense_chunked, "
-                         "dense_small, dense_window, sparse, sparse_paged, copy (a plain 1 GiB device copy for counter "
+                         "dense_small, dense_window, chunked_context, sparse, sparse_paged, copy (a plain 1 GiB device copy for counter "
                          "calibration)")
     args = ap.parse_args()
 
@@ -322,7 +370,8 @@ def main():
         return
 
     if not args.no_calib and args.only in (None, "dense_varlen", "dense_long", "dense_chunked",
-                                           "dense_small", "dense_window", "sparse", "sparse_paged"):
+                                           "dense_small", "dense_window", "chunked_context", "sparse",
+                                           "sparse_paged"):
         from mla_varlen_prefill_amd import calib
         CALIB["mfma_loop_tflops"] = round(calib.mfma_tflops(), 1)
         CALIB["stream_read_gbps"] = round(calib.stream_read_gbps(), 1)
@@ -338,6 +387,7 @@ def main():
                                                      args.steps, args.warmup),
             "sparse": lambda: sparse_case(args.steps, args.warmup),
             "sparse_paged": lambda: sparse_paged_case(args.steps, args.warmup),
+            "chunked_context": lambda: chunked_context_case(args.steps, args.warmup),
             "dense_window": lambda: dense_device_case("dense_window_1x32768_h128_w4096", [32768], [32768], 128,
                                                       3, args.steps, args.warmup, window=(4096, -1)),
         }
@@ -410,6 +460,7 @@ def main():
                                      128, 4, ss, sw))
         sec.append(dense_device_case("dense_window_1x32768_h128_w4096", [32768], [32768], 128, 3, ss, sw,
                                      window=(4096, -1)))
+        sec.append(chunked_context_case(ss, sw))
         sec.append(sparse_case(ss, sw))
         sec.append(sparse_paged_case(ss, sw))
         result["secondary"] = sec

@@ -253,6 +253,70 @@ mla_status_t mla_prefill_sparse_paged(
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Dense MLA prefill of new tokens over a cached latent context, chunk by chunk.
+ *
+ * The new tokens of each sequence attend causally to themselves and, without a mask, to the
+ * sequence's cached context; the parts are merged through their LSEs (page "FlashAttention
+ * backend for MLA prefill", run_prefill_new_tokens, run_prefill_context_chunk with causal=False
+ * and the LSE always returned). The context is cached as latent rows of 512 columns + 64 rope
+ * columns and turned into per-head K/V by the W_UK / W_UV up-projections (page
+ * "mla_prefill_branch_sparse_fp8", w_uk / w_uv): head h's key of cached row c is
+ * [c[0:512] W_UK_h^T (128) || c[512:576] (64)] and its value c[0:512] W_UV_h^T (128).
+ * Equivalently: attention over [context keys || new keys] with the bottom-right causal mask.
+ *
+ * The context is processed in chunks of chunk_tokens positions per sequence through a bounded
+ * buffer (batch * chunk_tokens rows of K and V, in the workspace): per chunk, the rows are
+ * up-projected (mla_latent_upproject), attended without a mask into an fp32 partial result and
+ * merged into the running one; the sink is folded in once at the end.
+ *
+ *   q, k, v        : the new tokens, bf16 [total_q, H, 192] / [total_q, H, 192] / [total_q, H, 128].
+ *   cu_seqlens_q   : device int32 [batch + 1] (new tokens of each sequence).
+ *   latent         : bf16 [N, 576] cached rows, row stride latent_stride_row; sequence b's context
+ *                    is rows [cu_seqlens_ctx[b], cu_seqlens_ctx[b + 1]) in position order.
+ *   cu_seqlens_ctx : device int32 [batch + 1]; max_seqlen_ctx >= every context length (the number
+ *                    of chunks is ceil(max_seqlen_ctx / chunk_tokens)).
+ *   w_kv           : bf16 [H * 256, 512], row stride w_stride_row: rows h*256 + 0..127 = W_UK_h,
+ *                    h*256 + 128..255 = W_UV_h (a linear layer's weight layout).
+ *   sink, out, lse : as for mla_prefill_varlen.
+ *   workspace      : mla_prefill_chunked_context_workspace_size(...) bytes, 16-byte aligned.
+ * Errors: INVALID_ARG, UNSUPPORTED (batch > 65535, chunk buffer above 2^31 - 1 rows), ALIGNMENT,
+ * WORKSPACE, HIP, and those of mla_prefill_varlen for the new-token tensors.
+ * ------------------------------------------------------------------------------------------ */
+size_t mla_prefill_chunked_context_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                                  int32_t num_heads, int32_t chunk_tokens);
+
+mla_status_t mla_prefill_chunked_context(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const void* latent, int64_t latent_stride_row,
+    const int32_t* cu_seqlens_ctx, const void* w_kv, int64_t w_stride_row,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_ctx,
+    int32_t num_heads, int32_t chunk_tokens, float softmax_scale, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Up-projection of one chunk of cached latent rows into per-head K/V (the building block of
+ * mla_prefill_chunked_context; same reading of the pages).
+ *
+ * For each sequence b, the context positions [ctx_start, ctx_start + chunk_tokens) that exist
+ * (clamped to its length) are written to consecutive rows of k_out / v_out, sequence after
+ * sequence; cu_chunk (device int32 [batch + 1], written) receives the row offsets, so k_out /
+ * v_out with cu_chunk are directly the keys of a varlen call.
+ *   k_out : bf16 [batch * chunk_tokens, H, 192] (token stride H * 192), written: key columns
+ *           0..127 = c W_UK_h^T, 128..191 = the rope columns.
+ *   v_out : bf16 [batch * chunk_tokens, H, 128] (token stride H * 128), written.
+ * Errors: INVALID_ARG, UNSUPPORTED (batch > 65535), ALIGNMENT, HIP.
+ * ------------------------------------------------------------------------------------------ */
+mla_status_t mla_latent_upproject(const void* latent, int64_t latent_stride_row,
+                                  const int32_t* cu_seqlens_ctx, int32_t batch, int32_t ctx_start,
+                                  int32_t chunk_tokens, const void* w_kv, int64_t w_stride_row,
+                                  int32_t num_heads, int32_t* cu_chunk, void* k_out, void* v_out,
+                                  void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
  * Combine S partial results of disjoint key sets into the final result (split-KV reduction;
  * also merges a context-chunk result with a new-token result through their LSEs).
  *
@@ -283,10 +347,12 @@ mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num
  * for the recorded events and accumulates per-kernel launch counts and total device time.
  * Enabling clears the totals. Events are created on first use and reused; at most 65536
  * launches are held between two reads (later ones are not timed).
- *   kernel: MLA_KERNEL_PLAN, MLA_KERNEL_DENSE, MLA_KERNEL_COMBINE or MLA_KERNEL_SPARSE.
+ *   kernel: MLA_KERNEL_PLAN, MLA_KERNEL_DENSE, MLA_KERNEL_COMBINE, MLA_KERNEL_SPARSE,
+ *           MLA_KERNEL_UPPROJ (latent up-projection) or MLA_KERNEL_MERGE (chunk merge).
  * Errors: INVALID_ARG (unknown kernel, null outputs); HIP (event calls failed).
  * ------------------------------------------------------------------------------------------ */
-enum { MLA_KERNEL_PLAN = 0, MLA_KERNEL_DENSE = 1, MLA_KERNEL_COMBINE = 2, MLA_KERNEL_SPARSE = 3 };
+enum { MLA_KERNEL_PLAN = 0, MLA_KERNEL_DENSE = 1, MLA_KERNEL_COMBINE = 2, MLA_KERNEL_SPARSE = 3,
+       MLA_KERNEL_UPPROJ = 4, MLA_KERNEL_MERGE = 5 };
 mla_status_t mla_profile_enable(int32_t enable);
 mla_status_t mla_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
 

@@ -11,6 +11,8 @@ Entry points (same names as the C ABI):
   mla_prefill_varlen_window  the same with a (left, right) sliding-window band mask
   mla_prefill_sparse  sparse top-k prefill over one shared 576-wide latent KV (v = first 512)
   mla_prefill_sparse_paged  the same over a paged latent cache with logical indices
+  mla_prefill_chunked_context  new tokens over an up-projected latent context, chunk by chunk
+  mla_latent_upproject  one chunk of cached latent rows -> per-head K/V
   mla_combine         merge split partial results through their LSEs
   mla_prefill_plan    the varlen tile plan (test hook for the bit-exact plan checks)
 """
@@ -34,10 +36,11 @@ EXPORTED_SYMBOLS = (
     "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_window",
     "mla_prefill_varlen_num_splits",
     "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_prefill_sparse_paged",
+    "mla_prefill_chunked_context_workspace_size", "mla_prefill_chunked_context", "mla_latent_upproject",
     "mla_combine",
     "mla_profile_enable", "mla_profile_read",
 )
-KERNEL_IDS = {"plan": 0, "dense": 1, "combine": 2, "sparse": 3}
+KERNEL_IDS = {"plan": 0, "dense": 1, "combine": 2, "sparse": 3, "upproj": 4, "merge": 5}
 
 _c_i32, _c_i64, _c_f32, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -95,6 +98,16 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         _vp, _c_i64, _c_i32, _vp,
         _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64,
         _vp, _c_sz, _vp]
+    lib.mla_prefill_chunked_context_workspace_size.restype = _c_sz
+    lib.mla_prefill_chunked_context_workspace_size.argtypes = [_c_i32] * 5
+    lib.mla_prefill_chunked_context.restype = ctypes.c_int
+    lib.mla_prefill_chunked_context.argtypes = [
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp, _c_i64, _vp, _vp, _c_i64,
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64,
+        _vp, _c_sz, _vp]
+    lib.mla_latent_upproject.restype = ctypes.c_int
+    lib.mla_latent_upproject.argtypes = [_vp, _c_i64, _vp, _c_i32, _c_i32, _c_i32, _vp, _c_i64, _c_i32, _vp,
+                                         _vp, _vp, _vp]
     lib.mla_combine.restype = ctypes.c_int
     lib.mla_combine.argtypes = [_vp, _vp, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64,
                                 _vp, _c_i64, _c_i64, _vp]
@@ -295,6 +308,61 @@ def mla_prefill_sparse_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_tabl
     return (out, lse) if return_lse else out
 
 
+def chunked_context_workspace_bytes(batch: int, total_q: int, max_seqlen_q: int, num_heads: int,
+                                    chunk_tokens: int) -> int:
+    return load_library().mla_prefill_chunked_context_workspace_size(batch, total_q, max_seqlen_q, num_heads,
+                                                                      chunk_tokens)
+
+
+def mla_prefill_chunked_context(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
+                                latent: torch.Tensor, cu_seqlens_ctx: torch.Tensor, w_kv: torch.Tensor,
+                                max_seqlen_q: int, max_seqlen_ctx: int, softmax_scale: float,
+                                chunk_tokens: int = 4096, sink: Optional[torch.Tensor] = None,
+                                out: Optional[torch.Tensor] = None, return_lse: bool = True,
+                                lse: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None):
+    """New tokens (q/k/v [T,H,192/192/128] bf16, cu_seqlens_q) over their cached latent context
+    (latent [N,576] bf16 rows, cu_seqlens_ctx int32 [B+1]) up-projected by w_kv [H*256, 512] bf16,
+    chunk_tokens context positions per sequence at a time. Returns out [T,H,128] bf16 (and lse)."""
+    lib = load_library()
+    _require_cuda(q, k, v, cu_seqlens_q, latent, cu_seqlens_ctx, w_kv, sink, out, lse, workspace)
+    for name, t in (("q", q), ("k", k), ("v", v), ("latent", latent), ("w_kv", w_kv)):
+        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
+            raise ValueError(f"{name} must be bf16 with a contiguous last dim")
+    total_q, heads, _ = q.shape
+    batch = cu_seqlens_q.numel() - 1
+    if out is None:
+        out = torch.empty((total_q, heads, 128), dtype=torch.bfloat16, device=q.device)
+    if return_lse and lse is None:
+        lse = torch.empty((total_q, heads), dtype=torch.float32, device=q.device)
+    ws_bytes = lib.mla_prefill_chunked_context_workspace_size(batch, total_q, max_seqlen_q, heads, chunk_tokens)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    _check("mla_prefill_chunked_context", lib.mla_prefill_chunked_context(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1), _ptr(v), v.stride(0), v.stride(1),
+        _ptr(cu_seqlens_q), _ptr(latent), latent.stride(0), _ptr(cu_seqlens_ctx), _ptr(w_kv), w_kv.stride(0),
+        batch, total_q, max_seqlen_q, max_seqlen_ctx, heads, chunk_tokens, float(softmax_scale), _ptr(sink),
+        _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()))
+    return (out, lse) if return_lse else out
+
+
+def mla_latent_upproject(latent: torch.Tensor, cu_seqlens_ctx: torch.Tensor, w_kv: torch.Tensor, num_heads: int,
+                         ctx_start: int, chunk_tokens: int):
+    """One chunk of cached latent rows -> (k [B*chunk, H, 192], v [B*chunk, H, 128], cu_chunk [B+1])."""
+    lib = load_library()
+    _require_cuda(latent, cu_seqlens_ctx, w_kv)
+    batch = cu_seqlens_ctx.numel() - 1
+    rows = max(batch * chunk_tokens, 1)
+    k = torch.empty((rows, num_heads, 192), dtype=torch.bfloat16, device=latent.device)
+    v = torch.empty((rows, num_heads, 128), dtype=torch.bfloat16, device=latent.device)
+    cu = torch.empty(batch + 1, dtype=torch.int32, device=latent.device)
+    _check("mla_latent_upproject", lib.mla_latent_upproject(
+        _ptr(latent), latent.stride(0), _ptr(cu_seqlens_ctx), batch, ctx_start, chunk_tokens, _ptr(w_kv),
+        w_kv.stride(0), num_heads, _ptr(cu), _ptr(k), _ptr(v), _stream()))
+    return k, v, cu
+
+
 def mla_combine(o_part: torch.Tensor, lse_part: torch.Tensor, num_heads: int,
                 sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                 return_lse: bool = True, lse: Optional[torch.Tensor] = None):
@@ -325,7 +393,7 @@ def profile_enable(enable: bool = True) -> None:
 
 def profile_read(kernel: str) -> Tuple[float, int]:
     """(total device ms, launches) of one kernel kind since profile_enable(): plan, dense,
-    combine or sparse. Waits for the recorded events."""
+    combine, sparse, upproj or merge. Waits for the recorded events."""
     ms, n = ctypes.c_double(), _c_i64()
     _check("mla_profile_read", load_library().mla_profile_read(KERNEL_IDS[kernel], ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value

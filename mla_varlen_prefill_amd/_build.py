@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 LIB_NAME = "libmla_prefill.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
-SOURCES = ["abi.hip", "plan.hip", "dense_fwd.hip", "sparse_fwd.hip", "combine.hip"]
+SOURCES = ["abi.hip", "plan.hip", "dense_fwd.hip", "sparse_fwd.hip", "combine.hip", "latent_ctx.hip"]
 # Calibration kernels used by the benchmark harness only (measured MFMA and HBM rates).
 CALIB_SOURCE = "calib.hip"
 CALIB_PATH = os.path.join(PKG_DIR, "libmla_calib.so")

@@ -50,7 +50,7 @@ const DeviceInfo* device_info() {
 }
 
 // ---- launch timing (measurement aid) ------------------------------------------------------
-constexpr int kNumKernels = 4;
+constexpr int kNumKernels = 6;
 constexpr size_t kMaxPending = 65536;
 
 struct Profiler {
@@ -255,7 +255,11 @@ static mla_status_t varlen_call(
     int32_t num_splits, const float* sink,
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
-    void* workspace, size_t workspace_bytes, void* hip_stream) {
+    void* workspace, size_t workspace_bytes, void* hip_stream,
+    float* part_o = nullptr, float* part_lse = nullptr) {
+  // part_o / part_lse (internal use): write the normalised fp32 result [total_q, H, 128] and its
+  // LSE [total_q, H] there instead of `out` / `lse`, unsplit and without the sink.
+  if (part_o != nullptr) num_splits = 1;
   if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
       cu_seqlens_k == nullptr || out == nullptr)
     return MLA_ERR_INVALID_ARG;
@@ -326,6 +330,9 @@ static mla_status_t varlen_call(
   if (L.splits > 1) {
     dp.o_part = reinterpret_cast<float*>(ws + L.off_opart);
     dp.lse_part = reinterpret_cast<float*>(ws + L.off_lpart);
+  } else if (part_o != nullptr) {
+    dp.o_part = part_o;
+    dp.lse_part = part_lse;
   }
   {
     dp.wgs_per_xcd = L.wgs_per_xcd;
@@ -399,6 +406,151 @@ mla_status_t mla_prefill_varlen_window(
                      max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal,
                      window_left, window_right, num_splits, sink, out, o_stride_tok, o_stride_head,
                      lse, lse_stride_tok, lse_stride_head, workspace, workspace_bytes, hip_stream);
+}
+
+namespace {
+
+// Workspace of mla_prefill_chunked_context: the dense workspace, then the chunk's row offsets,
+// the bounded K/V buffer and the fp32 accumulators.
+struct ChunkedLayout {
+  size_t dense, off_cu, off_k, off_v, off_acc, off_part, off_la, off_lb, off_lp, total;
+};
+
+ChunkedLayout chunked_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_t heads, int32_t chunk) {
+  ChunkedLayout C{};
+  C.dense = align256(varlen_layout(batch, total_q, max_q, std::max(max_q, chunk), heads, 1).total);
+  const size_t rows = (size_t)batch * chunk;
+  const size_t th = (size_t)total_q * heads;
+  C.off_cu = C.dense;
+  C.off_k = align256(C.off_cu + (size_t)(batch + 1) * 4);
+  C.off_v = align256(C.off_k + rows * heads * kDenseDqk * 2);
+  C.off_acc = align256(C.off_v + rows * heads * kDenseDv * 2);
+  C.off_part = align256(C.off_acc + th * kDenseDv * 4);
+  C.off_la = align256(C.off_part + th * kDenseDv * 4);
+  C.off_lb = align256(C.off_la + th * 4);
+  C.off_lp = align256(C.off_lb + th * 4);
+  C.total = align256(C.off_lp + th * 4);
+  return C;
+}
+
+}  // namespace
+
+size_t mla_prefill_chunked_context_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
+                                                  int32_t num_heads, int32_t chunk_tokens) {
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || num_heads <= 0 || chunk_tokens <= 0) return 0;
+  return chunked_layout(batch, total_q, max_seqlen_q, num_heads, chunk_tokens).total;
+}
+
+mla_status_t mla_latent_upproject(const void* latent, int64_t latent_stride_row,
+                                  const int32_t* cu_seqlens_ctx, int32_t batch, int32_t ctx_start,
+                                  int32_t chunk_tokens, const void* w_kv, int64_t w_stride_row,
+                                  int32_t num_heads, int32_t* cu_chunk, void* k_out, void* v_out,
+                                  void* hip_stream) {
+  if (latent == nullptr || cu_seqlens_ctx == nullptr || w_kv == nullptr || cu_chunk == nullptr ||
+      k_out == nullptr || v_out == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || ctx_start < 0 || chunk_tokens <= 0 || num_heads <= 0 || latent_stride_row < kSparseDqk ||
+      w_stride_row < 512)
+    return MLA_ERR_INVALID_ARG;
+  if (batch > 65535 || num_heads > 32767 || chunk_tokens > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(latent) || !aligned16(w_kv) || !aligned16(k_out) || !aligned16(v_out) ||
+      !stride_ok(latent_stride_row) || !stride_ok(w_stride_row) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_ctx) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cu_chunk) & 3u) != 0)
+    return MLA_ERR_ALIGNMENT;
+  if (batch == 0) return MLA_OK;
+  const DeviceInfo* di = device_info();
+  if (di == nullptr) return MLA_ERR_HIP;
+  if (!di->gfx950) return MLA_ERR_UNSUPPORTED;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  if (mla::launch_chunk_cu(cu_seqlens_ctx, batch, ctx_start, chunk_tokens, cu_chunk, stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  mla::UpprojParams up{};
+  up.latent = static_cast<const __bf16*>(latent); up.lat_st = latent_stride_row;
+  up.cu_ctx = cu_seqlens_ctx; up.cu_chunk = cu_chunk;
+  up.batch = batch; up.c0 = ctx_start; up.w = chunk_tokens;
+  up.w_kv = static_cast<const __bf16*>(w_kv); up.w_st = w_stride_row;
+  up.num_heads = num_heads;
+  up.kbuf = static_cast<__bf16*>(k_out); up.k_st = (int64_t)num_heads * kDenseDqk; up.k_sh = kDenseDqk;
+  up.vbuf = static_cast<__bf16*>(v_out); up.v_st = (int64_t)num_heads * kDenseDv; up.v_sh = kDenseDv;
+  return timed_launch(MLA_KERNEL_UPPROJ, stream, [&] { return mla::launch_upproj(up, stream); }) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
+}
+
+mla_status_t mla_prefill_chunked_context(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const void* latent, int64_t latent_stride_row,
+    const int32_t* cu_seqlens_ctx, const void* w_kv, int64_t w_stride_row,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_ctx,
+    int32_t num_heads, int32_t chunk_tokens, float softmax_scale, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (latent == nullptr || cu_seqlens_ctx == nullptr || w_kv == nullptr || q == nullptr || out == nullptr)
+    return MLA_ERR_INVALID_ARG;
+  if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_ctx < 0 || num_heads <= 0 ||
+      chunk_tokens <= 0 || latent_stride_row < kSparseDqk || w_stride_row < 512 || !std::isfinite(softmax_scale))
+    return MLA_ERR_INVALID_ARG;
+  if (batch > 65535 || num_heads > 32767 || chunk_tokens > (1 << 24) ||
+      (int64_t)batch * chunk_tokens > INT32_MAX || (int64_t)num_heads * kDenseDqk >= (1 << 23))
+    return MLA_ERR_UNSUPPORTED;
+  if (!aligned16(latent) || !aligned16(w_kv) || !stride_ok(latent_stride_row) || !stride_ok(w_stride_row) ||
+      (reinterpret_cast<uintptr_t>(cu_seqlens_ctx) & 3u) != 0)
+    return MLA_ERR_ALIGNMENT;
+  if (batch == 0 || total_q == 0) return MLA_OK;
+  const ChunkedLayout C = chunked_layout(batch, total_q, max_seqlen_q, num_heads, chunk_tokens);
+  if (workspace == nullptr || workspace_bytes < C.total) return MLA_ERR_WORKSPACE;
+  if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
+  hipStream_t stream = (hipStream_t)hip_stream;
+  char* ws = static_cast<char*>(workspace);
+  float* acc = reinterpret_cast<float*>(ws + C.off_acc);
+  float* part = reinterpret_cast<float*>(ws + C.off_part);
+  float* la = reinterpret_cast<float*>(ws + C.off_la);
+  float* lb = reinterpret_cast<float*>(ws + C.off_lb);
+  float* lp = reinterpret_cast<float*>(ws + C.off_lp);
+  int32_t* cu_chunk = reinterpret_cast<int32_t*>(ws + C.off_cu);
+  void* kbuf = ws + C.off_k;
+  void* vbuf = ws + C.off_v;
+  // 1. the new tokens against themselves, causally: the first accumulated part
+  mla_status_t st = varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
+                                v_stride_head, cu_seqlens_q, cu_seqlens_q, batch, total_q, max_seqlen_q,
+                                max_seqlen_q, num_heads, kDenseDqk, kDenseDv, softmax_scale, 1, -1, -1, 1,
+                                nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws, C.dense,
+                                hip_stream, acc, la);
+  if (st != MLA_OK) return st;
+  // 2. each context chunk: up-project into the bounded buffer, attend without a mask, merge
+  const int64_t kst = (int64_t)num_heads * kDenseDqk, vst = (int64_t)num_heads * kDenseDv;
+  const int32_t rows = total_q * num_heads;
+  for (int64_t c0 = 0; c0 < max_seqlen_ctx; c0 += chunk_tokens) {
+    st = mla_latent_upproject(latent, latent_stride_row, cu_seqlens_ctx, batch, (int32_t)c0, chunk_tokens, w_kv,
+                              w_stride_row, num_heads, cu_chunk, kbuf, vbuf, hip_stream);
+    if (st != MLA_OK) return st;
+    st = varlen_call(q, q_stride_tok, q_stride_head, kbuf, kst, kDenseDqk, vbuf, vst, kDenseDv, cu_seqlens_q,
+                     cu_chunk, batch, total_q, max_seqlen_q, chunk_tokens, num_heads, kDenseDqk, kDenseDv,
+                     softmax_scale, 0, -1, -1, 1, nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws,
+                     C.dense, hip_stream, part, lp);
+    if (st != MLA_OK) return st;
+    mla::MergeParams mp{acc, la, part, lp, lb, rows, kDenseDv};
+    if (timed_launch(MLA_KERNEL_MERGE, stream, [&] { return mla::launch_merge_partial(mp, stream); }) != hipSuccess)
+      return MLA_ERR_HIP;
+    std::swap(la, lb);
+  }
+  // 3. the accumulated result to bf16, with the sink folded in once
+  mla::CombineParams cp{};
+  cp.o_part = acc;
+  cp.lse_part = la;
+  cp.num_splits = 1;
+  cp.rows = rows;
+  cp.num_heads = num_heads;
+  cp.dv = kDenseDv;
+  cp.sink = sink;
+  cp.out = static_cast<__bf16*>(out); cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
+  cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
+  return timed_launch(MLA_KERNEL_COMBINE, stream, [&] { return mla::launch_combine(cp, stream); }) == hipSuccess
+             ? MLA_OK
+             : MLA_ERR_HIP;
 }
 
 size_t mla_prefill_sparse_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,

@@ -87,7 +87,30 @@ struct CombineParams {
   float* lse; int64_t l_st, l_sh;
 };
 
+// Up-projection of a chunk of cached latent rows into per-head K/V (see latent_ctx.hip).
+struct UpprojParams {
+  const __bf16* latent; int64_t lat_st;   // [N, 576] rows: 512 latent + 64 rope
+  const int32_t* cu_ctx;                   // [batch + 1] cached rows of each sequence
+  const int32_t* cu_chunk;                 // [batch + 1] buffer rows of each sequence in the chunk
+  int32_t batch, c0, w;                    // chunk: context positions [c0, c0 + w) of each sequence
+  const __bf16* w_kv; int64_t w_st;        // [H * 256, 512]
+  int32_t num_heads;
+  __bf16* kbuf; int64_t k_st, k_sh;        // [rows, H, 192]
+  __bf16* vbuf; int64_t v_st, v_sh;        // [rows, H, 128]
+};
+
+struct MergeParams {
+  float* o_acc; const float* lse_acc;      // [rows, dv], [rows]; o_acc updated in place
+  const float* o_part; const float* lse_part;
+  float* lse_out;                          // [rows], must not alias lse_acc
+  int32_t rows, dv;
+};
+
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
+hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int32_t w, int32_t* cu_chunk,
+                           hipStream_t stream);
+hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream);
+hipError_t launch_merge_partial(const MergeParams& p, hipStream_t stream);
 hipError_t launch_dense_fwd(const DenseParams& p, int nq, hipStream_t stream);
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);

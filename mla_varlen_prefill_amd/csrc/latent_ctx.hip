@@ -1,0 +1,207 @@
+// Context from the latent cache, chunk by chunk: the kernels that turn a window of cached latent
+// rows into per-head K/V in a bounded buffer, and the merge of a chunk's partial result into the
+// running one.
+//
+// The pages run the new tokens causally against themselves and every context chunk without a
+// mask, always returning the LSE, and merge the parts (page "FlashAttention backend for MLA
+// prefill", run_prefill_new_tokens and run_prefill_context_chunk). The cached rows are the
+// 512-wide latent followed by 64 rope columns, turned into per-head keys and values by the W_UK /
+// W_UV up-projections (page "mla_prefill_branch_sparse_fp8", w_uk / w_uv). Reading: head h's key
+// is [c W_UK_h^T (128) || rope (64)] and its value c W_UV_h^T (128), with W_KV laid out like a
+// linear layer's weight, [H * 256, 512]: rows h*256 + 0..127 are W_UK_h, h*256 + 128..255 W_UV_h.
+//
+// Up-projection: a bf16 GEMM C = W_KV * C_latent^T on 32x32x16 MFMA with both operands
+// contiguous along the 512-deep contraction. A work-group (4 waves) computes 128 output columns
+// (half of one head: its key or its value part) for 128 cached rows of one sequence; each wave
+// holds a 64 x 64 block (2 x 2 accumulator tiles). The contraction runs in 8 stages of 64,
+// double-buffered in LDS and copied straight from global memory (global_load_lds, 1 KiB per wave
+// copy); a 128-byte operand row keeps its 16-byte chunk c at c ^ ((r >> 1) & 7), which makes the
+// operand reads conflict-free under gfx950's 16-byte read grouping. The key work-groups also copy
+// the rope columns into every head's key.
+#include "common.h"
+#include "kernels.h"
+
+namespace mla {
+
+namespace {
+
+constexpr int UP_TILE = 128;               // rows and output columns per work-group
+constexpr int UP_KS = 64;                  // contraction per stage
+constexpr int UP_STAGE = UP_TILE * UP_KS * 2;  // 16 KiB per operand per stage
+constexpr int LAT_D = 512;
+constexpr int KV_COLS = 256;               // per head: 128 key + 128 value columns
+
+__device__ __forceinline__ int swz_pos(int r, int c) { return r * (UP_KS * 2) + ((c ^ ((r >> 1) & 7)) << 4); }
+
+}  // namespace
+
+// cu_chunk[b] = sum over b' < b of clamp(ctx_{b'} - c0, 0, W): the buffer rows of each sequence's
+// slice [c0, c0 + W) of its context. One work-group; each thread owns a run of sequences.
+__global__ __launch_bounds__(1024) void chunk_cu_kernel(const int32_t* cu_ctx, int32_t batch, int32_t c0,
+                                                        int32_t w, int32_t* cu_chunk) {
+  __shared__ int part[1024];
+  const int tid = threadIdx.x;
+  const int per = (batch + 1023) / 1024;
+  const int b0 = tid * per, b1 = min(batch, b0 + per);
+  int sum = 0;
+  for (int b = b0; b < b1; ++b) sum += min(max(cu_ctx[b + 1] - cu_ctx[b] - c0, 0), w);
+  part[tid] = sum;
+  __syncthreads();
+  // inclusive scan of the per-thread sums (Hillis-Steele)
+  for (int off = 1; off < 1024; off <<= 1) {
+    const int v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int run = tid == 0 ? 0 : part[tid - 1];
+  if (tid == 0) cu_chunk[0] = 0;
+  for (int b = b0; b < b1; ++b) {
+    run += min(max(cu_ctx[b + 1] - cu_ctx[b] - c0, 0), w);
+    cu_chunk[b + 1] = run;
+  }
+}
+
+__global__ __launch_bounds__(256) void upproj_kernel(UpprojParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds_w[2][UP_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds_c[2][UP_STAGE];
+  const int b = blockIdx.y;
+  const int tile = blockIdx.x;
+  const int z = blockIdx.z;               // 2h: key columns of head h, 2h + 1: value columns
+  const int h = z >> 1;
+  const bool is_key = (z & 1) == 0;
+  const int ctx_b = p.cu_ctx[b + 1] - p.cu_ctx[b];
+  const int len = min(max(ctx_b - p.c0, 0), p.w);   // this sequence's rows in the chunk
+  const int r0 = tile * UP_TILE;
+  if (r0 >= len) return;
+  const int rows = min(UP_TILE, len - r0);
+  const int64_t lat_row0 = (int64_t)p.cu_ctx[b] + p.c0 + r0;    // first cached row of the tile
+  const int64_t buf_row0 = (int64_t)p.cu_chunk[b] + r0;          // first buffer row of the tile
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l32 = lane & 31, hl = lane >> 5;
+  // copy addresses: wave copy q covers tile rows (4 wave + q) * 8 + lane / 8, slot lane % 8
+  const __bf16* wsrc[4];
+  const __bf16* csrc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = (wave * 4 + q) * 8 + (lane >> 3);
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    wsrc[q] = p.w_kv + (int64_t)(h * KV_COLS + (is_key ? 0 : 128) + r) * p.w_st + c * 8;
+    csrc[q] = p.latent + (lat_row0 + min(r, rows - 1)) * p.lat_st + c * 8;  // tail rows re-read the last
+  }
+  auto issue = [&](int s, int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      g2lds16(wsrc[q] + s * UP_KS, lds_w[buf] + (wave * 4 + q) * 1024);
+      g2lds16(csrc[q] + s * UP_KS, lds_c[buf] + (wave * 4 + q) * 1024);
+    }
+  };
+  // wave (wm, wn) computes output columns [64 wm, 64 wm + 64) x rows [64 wn, 64 wn + 64)
+  const int wm = wave & 1, wn = wave >> 1;
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+  issue(0, 0);
+  wait_vmem();
+  __syncthreads();
+  constexpr int NSTAGE = LAT_D / UP_KS;
+  for (int s = 0; s < NSTAGE; ++s) {
+    const int buf = s & 1;
+    if (s + 1 < NSTAGE) issue(s + 1, buf ^ 1);
+#pragma unroll
+    for (int kk = 0; kk < UP_KS / 16; ++kk) {
+      bf16x8 a[2], bb[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        a[i] = lds_read_b128(lds_w[buf] + swz_pos(wm * 64 + i * 32 + l32, 2 * kk + hl));
+        bb[i] = lds_read_b128(lds_c[buf] + swz_pos(wn * 64 + i * 32 + l32, 2 * kk + hl));
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+  // accumulator (i, j): lane holds output columns 64 wm + 32 i + 8 (e / 4) + 4 hl + e % 4 of tile
+  // row 64 wn + 32 j + l32
+  __bf16* dst = is_key ? p.kbuf : p.vbuf;
+  const int64_t dst_st = is_key ? p.k_st : p.v_st;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = wn * 64 + j * 32 + l32;
+    if (r >= rows) continue;
+    __bf16* row = dst + (buf_row0 + r) * dst_st + (int64_t)h * (is_key ? p.k_sh : p.v_sh);
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = wm * 64 + i * 32 + 8 * g + 4 * hl;
+        const f32x16& v = acc[i][j];
+        u32x2 o = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
+        *reinterpret_cast<u32x2*>(row + col) = o;
+      }
+  }
+  if (is_key) {
+    // rope columns 512..575 of the cached row -> key columns 128..191 of head h
+    const int r = tid >> 1, half = tid & 1;
+    if (r < rows) {
+      const u32x4* src = reinterpret_cast<const u32x4*>(p.latent + (lat_row0 + r) * p.lat_st + LAT_D + half * 32);
+      u32x4* d = reinterpret_cast<u32x4*>(p.kbuf + (buf_row0 + r) * p.k_st + (int64_t)h * p.k_sh + 128 + half * 32);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) d[i] = src[i];
+    }
+  }
+}
+
+// Running merge of a chunk's partial result into the accumulated one, rows of dv columns:
+// LSE = log(exp(L_acc) + exp(L_part)), O = w_acc O_acc + w_part O_part with w = exp(L - LSE);
+// the accumulated O is updated in place, the new LSE goes to lse_out (other threads of the row
+// still read lse_acc). Rows empty on both sides keep O = 0 and LSE = -inf.
+__global__ __launch_bounds__(256) void merge_partial_kernel(MergeParams p) {
+  const int c4_per_row = p.dv >> 2;
+  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= (int64_t)p.rows * c4_per_row) return;
+  const int64_t row = t / c4_per_row;
+  const int c4 = (int)(t - row * c4_per_row);
+  const float la = p.lse_acc[row], lp = p.lse_part[row];
+  const float mx = fmaxf(la, lp);
+  f32x4* oa = reinterpret_cast<f32x4*>(p.o_acc + row * p.dv + c4 * 4);
+  if (mx == -INFINITY) {
+    if (c4 == 0) p.lse_out[row] = -INFINITY;
+    return;
+  }
+  const float wa = __expf(la - mx), wp = __expf(lp - mx);
+  const float tot = wa + wp;
+  const f32x4 op = *reinterpret_cast<const f32x4*>(p.o_part + row * p.dv + c4 * 4);
+  const f32x4 cur = *oa;
+  *oa = (cur * wa + op * wp) * (1.f / tot);
+  if (c4 == 0) p.lse_out[row] = mx + __logf(tot);
+}
+
+hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int32_t w, int32_t* cu_chunk,
+                           hipStream_t stream) {
+  hipLaunchKernelGGL(chunk_cu_kernel, dim3(1), dim3(1024), 0, stream, cu_ctx, batch, c0, w, cu_chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream) {
+  const int tiles = (p.w + UP_TILE - 1) / UP_TILE;
+  if (tiles == 0 || p.batch == 0) return hipSuccess;
+  hipLaunchKernelGGL(upproj_kernel, dim3(tiles, p.batch, 2 * p.num_heads), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_partial(const MergeParams& p, hipStream_t stream) {
+  const int64_t threads = (int64_t)p.rows * (p.dv >> 2);
+  if (threads == 0) return hipSuccess;
+  hipLaunchKernelGGL(merge_partial_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace mla

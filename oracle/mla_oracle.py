@@ -57,6 +57,9 @@ Readings taken where the pages are silent (each also listed with the design note
      linear layer's weight, [H * 256, 512], rows h*256 + 0..127 for W_UK_h and h*256 + 128..255
      for W_UV_h. The result for a new query is attention over [context keys || new keys] with
      the bottom-right causal mask (R3), i.e. every context key plus the causal new keys.
+  R14 The up-projected context K/V are materialised in bf16 (round-to-nearest-even of the fp32
+     products), the type the attention takes its K/V in; the parity tests compare with the
+     oracle evaluated on the same rounded K/V, so that the attention is what is measured.
   R11 Paged latent cache (page "SparseFlashMla": ``block_table`` for PageAttention, cache shape
      [block_num, block_size, KV_N, D], ``topk_value_mode`` 1 = logical token indices,
      ``seqused`` = valid KV length per sequence, ``cu_seqlens_q``). Token t belongs to sequence b
@@ -263,11 +266,24 @@ def sparse_mla_prefill_paged(q: np.ndarray, kv_cache: np.ndarray, block_table: n
     return sparse_mla_prefill(q, rows, phys, scale, dv=dv, topk_length=topk_length, sink=sink, tokens=tokens)
 
 
-def upproject_latent(latent_rows: np.ndarray, w_kv: np.ndarray, heads: int) -> Tuple[np.ndarray, np.ndarray]:
-    """Context K [n, H, 192] and V [n, H, 128] from cached latent rows [n, 576] (reading R13)."""
+def round_to_bf16(x: np.ndarray) -> np.ndarray:
+    """Values rounded to bfloat16 through float32, round-to-nearest-even at each step (the
+    precision in which K/V are materialised for the attention), returned as float64."""
+    f = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16 << 16
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def upproject_latent(latent_rows: np.ndarray, w_kv: np.ndarray, heads: int,
+                     round_bf16: bool = False) -> Tuple[np.ndarray, np.ndarray]:
+    """Context K [n, H, 192] and V [n, H, 128] from cached latent rows [n, 576] (reading R13);
+    with round_bf16 the up-projected columns are rounded to bf16 (R14)."""
     c = _as_f64(latent_rows)
-    w = _as_f64(w_kv).reshape(heads, 256, 512)
-    kv = np.einsum("nd,hcd->nhc", c[:, :512], w)           # [n, H, 256]
+    w = _as_f64(w_kv).reshape(heads * 256, 512)
+    kv = (c[:, :512] @ w.T).reshape(c.shape[0], heads, 256)   # row h*256 + j of W gives column (h, j)
+    if round_bf16:
+        kv = round_to_bf16(kv)
     rope = np.broadcast_to(c[:, None, 512:576], (c.shape[0], heads, 64))
     return np.concatenate([kv[:, :, :128], rope], axis=2), kv[:, :, 128:]
 
@@ -276,7 +292,8 @@ def mla_prefill_with_latent_context(q: np.ndarray, k_new: np.ndarray, v_new: np.
                                     cu_q: Sequence[int], latent: np.ndarray, cu_ctx: Sequence[int],
                                     w_kv: np.ndarray, scale: float,
                                     sink: Optional[np.ndarray] = None,
-                                    heads: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                                    heads: Optional[Iterable[int]] = None,
+                                    round_kv_bf16: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """New tokens q [T, H, 192] (with their k_new [T, H, 192], v_new [T, H, 128]) attending to
     their sequence's cached context (latent rows [cu_ctx[b]:cu_ctx[b+1]] of latent [N, 576],
     up-projected by w_kv) and causally to themselves (reading R13). Returns O [T, H, 128] and
@@ -284,7 +301,8 @@ def mla_prefill_with_latent_context(q: np.ndarray, k_new: np.ndarray, v_new: np.
     h_all = np.asarray(q).shape[1]
     k_parts, v_parts, cu_k = [], [], [0]
     for b in range(len(cu_q) - 1):
-        kc, vc = upproject_latent(np.asarray(latent)[int(cu_ctx[b]):int(cu_ctx[b + 1])], w_kv, h_all)
+        kc, vc = upproject_latent(np.asarray(latent)[int(cu_ctx[b]):int(cu_ctx[b + 1])], w_kv, h_all,
+                                  round_bf16=round_kv_bf16)
         k_parts += [kc, _as_f64(np.asarray(k_new)[int(cu_q[b]):int(cu_q[b + 1])])]
         v_parts += [vc, _as_f64(np.asarray(v_new)[int(cu_q[b]):int(cu_q[b + 1])])]
         cu_k.append(cu_k[-1] + kc.shape[0] + int(cu_q[b + 1]) - int(cu_q[b]))

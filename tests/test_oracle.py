@@ -402,6 +402,14 @@ def test_latent_upprojection_brute_force():
             assert np.array_equal(k[t, hh, 128:], lat[t, 512:])
 
 
+def test_round_to_bf16_hand_values():
+    """Round-to-nearest-even at the 8-bit mantissa: ties go to the even neighbour, values just
+    above a tie go up, and representable values are kept."""
+    x = np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, 1.0 + 2 ** -8 + 2 ** -20, -2.5, 1.0 + 2 ** -7, 0.0])
+    want = np.array([1.0, 1.0 + 2 ** -6, 1.0 + 2 ** -7, -2.5, 1.0 + 2 ** -7, 0.0])
+    np.testing.assert_array_equal(O.round_to_bf16(x), want)
+
+
 # ---------------------------------------------------------------- paged latent cache (R11)
 def _paged_case(rng, block_size, lens_kv, n_tok_per_seq, topk, d=6, num_blocks_extra=3):
     """Per-sequence contiguous KV scattered into a shuffled block pool, with its block table."""
