@@ -41,13 +41,20 @@ Readings taken where the pages are silent (each also listed with the design note
   R7 In the sparse path V is the first ``dv`` columns of the same gathered rows as K.
   R8 Indices are physical pool rows; any index outside [0, N_kv) is skipped like -1.
   R9 Slots at or beyond ``topk_length[t]`` are ignored even when they hold a valid row.
-  R12 Sliding window / band mask (page "Sgl project Sglang FA4 Interface", ``window_size`` =
+  R17 Paged latent cache (page "SparseFlashMla": ``block_table`` for PageAttention, cache shape
+     [block_num, block_size, KV_N, D], ``topk_value_mode`` 1 = logical token indices,
+     ``seqused`` = valid KV length per sequence, ``cu_seqlens_q``). Token t belongs to sequence b
+     with cu_q[b] <= t < cu_q[b+1]; logical index p of its row is cache row
+     (block_table[b][p // block_size], p % block_size). A slot is valid iff R9 holds,
+     0 <= p < used_b (used_b = seqused[b] if given, else max_blocks * block_size) and the table
+     entry lies in [0, num_blocks). A token outside every sequence has no valid slot.
+  R18 Sliding window / band mask (page "Sgl project Sglang FA4 Interface", ``window_size`` =
      (left, right), e.g. (256, 0) = causal with a 256-key window; page "SparseFlashMla",
      ``ori_win_left`` / ``ori_win_right``: the number of past / future tokens a query sees, -1 =
      unlimited, Band mask mode). Aligned bottom-right like R3, with d = Sk - Sq: key j is visible
      to query i iff j >= i + d - left (when left >= 0) and j <= i + d + right (when right >= 0).
      ``causal`` is the case right = 0 and overrides a given right.
-  R13 Context from the latent cache (page "FlashAttention backend for MLA prefill",
+  R19 Context from the latent cache (page "FlashAttention backend for MLA prefill",
      ``run_prefill_new_tokens`` / ``run_prefill_context_chunk``: new tokens attend causally to
      themselves, context keys without a mask, the LSE merges the parts; page
      "mla_prefill_branch_sparse_fp8": latent rows of 512 + 64 rope, ``w_uk`` / ``w_uv``
@@ -57,16 +64,9 @@ Readings taken where the pages are silent (each also listed with the design note
      linear layer's weight, [H * 256, 512], rows h*256 + 0..127 for W_UK_h and h*256 + 128..255
      for W_UV_h. The result for a new query is attention over [context keys || new keys] with
      the bottom-right causal mask (R3), i.e. every context key plus the causal new keys.
-  R14 The up-projected context K/V are materialised in bf16 (round-to-nearest-even of the fp32
+  R20 The up-projected context K/V are materialised in bf16 (round-to-nearest-even of the fp32
      products), the type the attention takes its K/V in; the parity tests compare with the
      oracle evaluated on the same rounded K/V, so that the attention is what is measured.
-  R11 Paged latent cache (page "SparseFlashMla": ``block_table`` for PageAttention, cache shape
-     [block_num, block_size, KV_N, D], ``topk_value_mode`` 1 = logical token indices,
-     ``seqused`` = valid KV length per sequence, ``cu_seqlens_q``). Token t belongs to sequence b
-     with cu_q[b] <= t < cu_q[b+1]; logical index p of its row is cache row
-     (block_table[b][p // block_size], p % block_size). A slot is valid iff R9 holds,
-     0 <= p < used_b (used_b = seqused[b] if given, else max_blocks * block_size) and the table
-     entry lies in [0, num_blocks). A token outside every sequence has no valid slot.
 """
 from __future__ import annotations
 
@@ -112,7 +112,7 @@ def _softmax_rows(scores: np.ndarray, visible: np.ndarray, values: np.ndarray,
 
 def dense_visible(sq: int, sk: int, causal: bool, rows: Optional[np.ndarray] = None,
                   window: Tuple[int, int] = (-1, -1)) -> np.ndarray:
-    """Visibility mask [len(rows), sk] for one sequence (readings R3 and R12: bottom-right
+    """Visibility mask [len(rows), sk] for one sequence (readings R3 and R18: bottom-right
     causal, optional (left, right) window with -1 = unlimited)."""
     i = np.arange(sq) if rows is None else np.asarray(rows)
     j = np.arange(sk)
@@ -136,7 +136,7 @@ def dense_mla_prefill(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Sequenc
 
     q [Tq, H, Dqk], k [Tk, H, Dqk], v [Tk, H, Dv] (float64 or bf16 bits). Sequence b owns query
     rows cu_q[b]:cu_q[b+1] and key rows cu_k[b]:cu_k[b+1]. For query i of sequence b and head h:
-    s_j = scale * <q_i, k_j> over all Dqk columns, visible keys per R3/R12, softmax with the optional
+    s_j = scale * <q_i, k_j> over all Dqk columns, visible keys per R3/R18, softmax with the optional
     sink (R6), O = sum_j p_j v_j, LSE = log(sum exp). Returns O [Tq, H, Dv] and LSE [Tq, H]
     (rows of heads not requested stay NaN).
     """
@@ -233,7 +233,7 @@ def sparse_mla_prefill(q: np.ndarray, kv: np.ndarray, indices: np.ndarray, scale
 def paged_physical_indices(indices: np.ndarray, block_table: np.ndarray, block_size: int,
                            num_blocks: int, cu_q: Sequence[int],
                            seqused: Optional[Sequence[int]] = None) -> np.ndarray:
-    """Logical index rows -> physical cache rows of [num_blocks * block_size] (reading R11);
+    """Logical index rows -> physical cache rows of [num_blocks * block_size] (reading R17);
     invalid slots become -1. block_table is [B, max_blocks] int32."""
     idx = np.asarray(indices, dtype=np.int64)
     bt = np.asarray(block_table, dtype=np.int64)
@@ -258,7 +258,7 @@ def sparse_mla_prefill_paged(q: np.ndarray, kv_cache: np.ndarray, block_table: n
                              sink: Optional[np.ndarray] = None,
                              tokens: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Sparse top-k attention over a paged latent cache kv_cache [num_blocks, block_size, D]
-    with logical indices (reading R11): the indices are mapped to cache rows, then the sparse
+    with logical indices (reading R17): the indices are mapped to cache rows, then the sparse
     definition applies unchanged."""
     num_blocks, block_size, d = kv_cache.shape
     phys = paged_physical_indices(indices, block_table, block_size, num_blocks, cu_q, seqused)
@@ -277,8 +277,8 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
 
 def upproject_latent(latent_rows: np.ndarray, w_kv: np.ndarray, heads: int,
                      round_bf16: bool = False) -> Tuple[np.ndarray, np.ndarray]:
-    """Context K [n, H, 192] and V [n, H, 128] from cached latent rows [n, 576] (reading R13);
-    with round_bf16 the up-projected columns are rounded to bf16 (R14)."""
+    """Context K [n, H, 192] and V [n, H, 128] from cached latent rows [n, 576] (reading R19);
+    with round_bf16 the up-projected columns are rounded to bf16 (R20)."""
     c = _as_f64(latent_rows)
     w = _as_f64(w_kv).reshape(heads * 256, 512)
     kv = (c[:, :512] @ w.T).reshape(c.shape[0], heads, 256)   # row h*256 + j of W gives column (h, j)
@@ -296,7 +296,7 @@ def mla_prefill_with_latent_context(q: np.ndarray, k_new: np.ndarray, v_new: np.
                                     round_kv_bf16: bool = False) -> Tuple[np.ndarray, np.ndarray]:
     """New tokens q [T, H, 192] (with their k_new [T, H, 192], v_new [T, H, 128]) attending to
     their sequence's cached context (latent rows [cu_ctx[b]:cu_ctx[b+1]] of latent [N, 576],
-    up-projected by w_kv) and causally to themselves (reading R13). Returns O [T, H, 128] and
+    up-projected by w_kv) and causally to themselves (reading R19). Returns O [T, H, 128] and
     LSE [T, H]."""
     h_all = np.asarray(q).shape[1]
     k_parts, v_parts, cu_k = [], [], [0]

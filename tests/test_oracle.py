@@ -271,7 +271,7 @@ def test_sparse_brute_force_with_topk_length_and_duplicates():
             np.testing.assert_allclose(o[ti, hi], softmax(lg)[:-1] @ np.array(vals), atol=1e-12)
 
 
-# ---------------------------------------------------------------- sliding window (R12)
+# ---------------------------------------------------------------- sliding window (R18)
 def test_window_special_cases_reduce_to_causal_and_full():
     """(-1, -1) is the unmasked rule, (-1, 0) the bottom-right causal rule, causal overrides a
     given right window, and a window wider than the sequence changes nothing."""
@@ -331,7 +331,7 @@ def test_window_rows_with_no_key_are_empty():
     np.testing.assert_allclose(o2[4, 0], v[1, 0], atol=1e-12)
 
 
-# ---------------------------------------------------------------- latent context (R13)
+# ---------------------------------------------------------------- latent context (R19)
 def _latent_case(rng, ctx, new, h):
     cu_q = np.concatenate([[0], np.cumsum(new)]).astype(np.int32)
     cu_c = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
@@ -410,7 +410,7 @@ def test_round_to_bf16_hand_values():
     np.testing.assert_array_equal(O.round_to_bf16(x), want)
 
 
-# ---------------------------------------------------------------- paged latent cache (R11)
+# ---------------------------------------------------------------- paged latent cache (R17)
 def _paged_case(rng, block_size, lens_kv, n_tok_per_seq, topk, d=6, num_blocks_extra=3):
     """Per-sequence contiguous KV scattered into a shuffled block pool, with its block table."""
     max_blocks = max((n + block_size - 1) // block_size for n in lens_kv)

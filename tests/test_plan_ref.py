@@ -51,7 +51,7 @@ def test_plan_items_cover_and_order(lens_q, lens_k, causal, bm, bn):
 ])
 def test_plan_items_window_extent_brute_force(lens_q, lens_k, causal, window, bm, bn):
     """With a (left, right) window the block range of each item is exactly the span of keys some
-    row of its tile can see, by brute force over the oracle's visibility mask (reading R12)."""
+    row of its tile can see, by brute force over the oracle's visibility mask (reading R18)."""
     lens_k = lens_q if lens_k is None else lens_k
     cu_q, cu_k = cu_from_lens(lens_q), cu_from_lens(lens_k)
     items = plan_ref.plan_items(cu_q, cu_k, max(lens_q), bm, bn, causal, window)
