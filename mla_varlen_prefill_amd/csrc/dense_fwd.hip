@@ -137,7 +137,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item&
   for (int nq = 0; nq < NQ; ++nq) s[nq][0] = s[nq][1] = f32x16{};
   {
     constexpr int NSTEP = NMT * (DQK / 16);  // (kk, mt) steps
-    constexpr int PF = 4;
+    constexpr int PF = 6;
     bf16x8 a[NSTEP];
 #pragma unroll
     for (int st = 0; st < PF; ++st) {
@@ -234,7 +234,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item&
   // run PF steps ahead of their MFMA.
   {
     constexpr int NSTEP = 2 * NMT * (DV / 32);   // (mt, cc) x dt
-    constexpr int PF = 4;
+    constexpr int PF = 6;
     bf16x8 a[NSTEP];
 #pragma unroll
     for (int st = 0; st < PF; ++st) {
