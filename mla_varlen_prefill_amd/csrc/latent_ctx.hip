@@ -13,11 +13,11 @@
 // Up-projection: a bf16 GEMM C = W_KV * C_latent^T on 32x32x16 MFMA with both operands
 // contiguous along the 512-deep contraction. A work-group (4 waves) computes 128 output columns
 // (half of one head: its key or its value part) for 128 cached rows of one sequence; each wave
-// holds a 64 x 64 block (2 x 2 accumulator tiles). The contraction runs in 8 stages of 64,
-// double-buffered in LDS and copied straight from global memory (global_load_lds, 1 KiB per wave
-// copy); a 128-byte operand row keeps its 16-byte chunk c at c ^ ((r >> 1) & 7), which makes the
-// operand reads conflict-free under gfx950's 16-byte read grouping. The key work-groups also copy
-// the rope columns into every head's key.
+// holds a 64 x 64 block (2 x 2 accumulator tiles); three work-groups share a CU. The contraction runs in 16 stages of 32 through
+// a 3-slot LDS ring, copied straight from global memory (global_load_lds, 1 KiB per wave copy)
+// two stages ahead of the compute; a 64-byte operand row keeps its 16-byte chunk c at
+// c ^ ((r >> 2) & 3), which makes the operand reads conflict-free under gfx950's 16-byte read
+// grouping. The key work-groups also copy the rope columns into every head's key.
 #include "common.h"
 #include "kernels.h"
 
@@ -26,12 +26,30 @@ namespace mla {
 namespace {
 
 constexpr int UP_TILE = 128;               // rows and output columns per work-group
-constexpr int UP_KS = 64;                  // contraction per stage
-constexpr int UP_STAGE = UP_TILE * UP_KS * 2;  // 16 KiB per operand per stage
+constexpr int UP_KS = 32;                  // contraction per stage
+constexpr int UP_STAGE = UP_TILE * UP_KS * 2;  // 8 KiB per operand per stage
+constexpr int UP_THREADS = 256;
+constexpr int UP_NBUF = 3;                 // ring slots (copies run two stages ahead)
 constexpr int LAT_D = 512;
 constexpr int KV_COLS = 256;               // per head: 128 key + 128 value columns
 
-__device__ __forceinline__ int swz_pos(int r, int c) { return r * (UP_KS * 2) + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ int swz_pos(int r, int c) { return r * (UP_KS * 2) + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// Direct global -> LDS copy of 16 bytes per lane (lane l's bytes land at lds_base + 16 l), issued
+// from asm so that the compiler's wait-count bookkeeping does not track it: the ring slot being
+// read is chosen at run time, and a tracked copy into any slot would make every operand read wait
+// for all copies in flight. The copies are waited for explicitly (vmcnt) before the barrier that
+// precedes their use. The instruction writes no vector register; M0 is declared clobbered.
+__device__ __forceinline__ void g2lds16_untracked(const void* gptr, const void* lds_base) {
+  const uint32_t m0v = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)lds_base);
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gptr), "s"(m0v) : "memory", "m0");
+}
+
+// LDS reads done, then the work-group barrier; copies in flight stay in flight.
+__device__ __forceinline__ void ring_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+}
 
 }  // namespace
 
@@ -62,9 +80,9 @@ __global__ __launch_bounds__(1024) void chunk_cu_kernel(const int32_t* cu_ctx, i
   }
 }
 
-__global__ __launch_bounds__(256) void upproj_kernel(UpprojParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds_w[2][UP_STAGE];
-  __shared__ __attribute__((aligned(1024))) char lds_c[2][UP_STAGE];
+__global__ __launch_bounds__(UP_THREADS) void upproj_kernel(UpprojParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds_w[UP_NBUF * UP_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds_c[UP_NBUF * UP_STAGE];
   const int b = blockIdx.y;
   const int tile = blockIdx.x;
   const int z = blockIdx.z;               // 2h: key columns of head h, 2h + 1: value columns
@@ -80,21 +98,21 @@ __global__ __launch_bounds__(256) void upproj_kernel(UpprojParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l32 = lane & 31, hl = lane >> 5;
-  // copy addresses: wave copy q covers tile rows (4 wave + q) * 8 + lane / 8, slot lane % 8
-  const __bf16* wsrc[4];
-  const __bf16* csrc[4];
+  // copy addresses: wave copy q (= 2 wave + i) covers tile rows 16 q + lane / 4, slot lane % 4
+  const __bf16* wsrc[2];
+  const __bf16* csrc[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = (wave * 4 + q) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    wsrc[q] = p.w_kv + (int64_t)(h * KV_COLS + (is_key ? 0 : 128) + r) * p.w_st + c * 8;
-    csrc[q] = p.latent + (lat_row0 + min(r, rows - 1)) * p.lat_st + c * 8;  // tail rows re-read the last
+  for (int i = 0; i < 2; ++i) {
+    const int r = (wave * 2 + i) * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    wsrc[i] = p.w_kv + (int64_t)(h * KV_COLS + (is_key ? 0 : 128) + r) * p.w_st + c * 8;
+    csrc[i] = p.latent + (lat_row0 + min(r, rows - 1)) * p.lat_st + c * 8;  // tail rows re-read the last
   }
-  auto issue = [&](int s, int buf) {
+  auto issue = [&](int s, int slot) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      g2lds16(wsrc[q] + s * UP_KS, lds_w[buf] + (wave * 4 + q) * 1024);
-      g2lds16(csrc[q] + s * UP_KS, lds_c[buf] + (wave * 4 + q) * 1024);
+    for (int i = 0; i < 2; ++i) {
+      g2lds16_untracked(wsrc[i] + s * UP_KS, lds_w + slot * UP_STAGE + (wave * 2 + i) * 1024);
+      g2lds16_untracked(csrc[i] + s * UP_KS, lds_c + slot * UP_STAGE + (wave * 2 + i) * 1024);
     }
   };
   // wave (wm, wn) computes output columns [64 wm, 64 wm + 64) x rows [64 wn, 64 wn + 64)
@@ -105,28 +123,36 @@ __global__ __launch_bounds__(256) void upproj_kernel(UpprojParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
-  issue(0, 0);
-  wait_vmem();
-  __syncthreads();
   constexpr int NSTAGE = LAT_D / UP_KS;
+  issue(0, 0);
+  issue(1, 1);
+  asm volatile("s_waitcnt vmcnt(4)" ::: "memory");  // this wave's stage-0 copies have landed
+  ring_barrier();
   for (int s = 0; s < NSTAGE; ++s) {
-    const int buf = s & 1;
-    if (s + 1 < NSTAGE) issue(s + 1, buf ^ 1);
+    const int slot = s % UP_NBUF;
+    if (s + 2 < NSTAGE) issue(s + 2, (s + 2) % UP_NBUF);
+    const char* wb = lds_w + slot * UP_STAGE;
+    const char* cb = lds_c + slot * UP_STAGE;
 #pragma unroll
     for (int kk = 0; kk < UP_KS / 16; ++kk) {
       bf16x8 a[2], bb[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        a[i] = lds_read_b128(lds_w[buf] + swz_pos(wm * 64 + i * 32 + l32, 2 * kk + hl));
-        bb[i] = lds_read_b128(lds_c[buf] + swz_pos(wn * 64 + i * 32 + l32, 2 * kk + hl));
+        a[i] = lds_read_b128(wb + swz_pos(wm * 64 + i * 32 + l32, 2 * kk + hl));
+        bb[i] = lds_read_b128(cb + swz_pos(wn * 64 + i * 32 + l32, 2 * kk + hl));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(a[i], bb[j], acc[i][j]);
     }
-    wait_vmem();
-    __syncthreads();
+    // stage s + 1 must have landed for the next iteration (stage s + 2 may stay in flight)
+    if (s + 2 < NSTAGE) {
+      asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+    } else {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    }
+    ring_barrier();
   }
   // accumulator (i, j): lane holds output columns 64 wm + 32 i + 8 (e / 4) + 4 hl + e % 4 of tile
   // row 64 wn + 32 j + l32
@@ -193,7 +219,7 @@ hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int
 hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream) {
   const int tiles = (p.w + UP_TILE - 1) / UP_TILE;
   if (tiles == 0 || p.batch == 0) return hipSuccess;
-  hipLaunchKernelGGL(upproj_kernel, dim3(tiles, p.batch, 2 * p.num_heads), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(upproj_kernel, dim3(tiles, p.batch, 2 * p.num_heads), dim3(UP_THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
