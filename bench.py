@@ -242,7 +242,7 @@ def chunked_context_case(steps, warmup, chunk_tokens=4096):
         step()
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / steps
-    kern = {name: mla.profile_read(name) for name in ("dense", "upproj", "merge", "combine")}
+    kern = {name: mla.profile_read(name) for name in ("dense", "upproj", "combine")}
     mla.profile_enable(False)
     att = dense_flops(new, [c + n for c, n in zip(ctx, new)], h, True)
     up = 2.0 * sum(ctx) * h * 256 * 512

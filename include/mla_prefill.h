@@ -266,8 +266,9 @@ mla_status_t mla_prefill_sparse_paged(
  *
  * The context is processed in chunks of chunk_tokens positions per sequence through a bounded
  * buffer (batch * chunk_tokens rows of K and V, in the workspace): per chunk, the rows are
- * up-projected (mla_latent_upproject), attended without a mask into an fp32 partial result and
- * merged into the running one; the sink is folded in once at the end.
+ * up-projected (mla_latent_upproject) and attended without a mask, and the chunk's result is
+ * merged into the running fp32 result by the attention kernel as it writes it; the sink is
+ * folded in once at the end.
  *
  *   q, k, v        : the new tokens, bf16 [total_q, H, 192] / [total_q, H, 192] / [total_q, H, 128].
  *   cu_seqlens_q   : device int32 [batch + 1] (new tokens of each sequence).
@@ -348,11 +349,11 @@ mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num
  * Enabling clears the totals. Events are created on first use and reused; at most 65536
  * launches are held between two reads (later ones are not timed).
  *   kernel: MLA_KERNEL_PLAN, MLA_KERNEL_DENSE, MLA_KERNEL_COMBINE, MLA_KERNEL_SPARSE,
- *           MLA_KERNEL_UPPROJ (latent up-projection) or MLA_KERNEL_MERGE (chunk merge).
+ *           or MLA_KERNEL_UPPROJ (latent up-projection).
  * Errors: INVALID_ARG (unknown kernel, null outputs); HIP (event calls failed).
  * ------------------------------------------------------------------------------------------ */
 enum { MLA_KERNEL_PLAN = 0, MLA_KERNEL_DENSE = 1, MLA_KERNEL_COMBINE = 2, MLA_KERNEL_SPARSE = 3,
-       MLA_KERNEL_UPPROJ = 4, MLA_KERNEL_MERGE = 5 };
+       MLA_KERNEL_UPPROJ = 4 };
 mla_status_t mla_profile_enable(int32_t enable);
 mla_status_t mla_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
 

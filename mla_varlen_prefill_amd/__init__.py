@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "mla_combine",
     "mla_profile_enable", "mla_profile_read",
 )
-KERNEL_IDS = {"plan": 0, "dense": 1, "combine": 2, "sparse": 3, "upproj": 4, "merge": 5}
+KERNEL_IDS = {"plan": 0, "dense": 1, "combine": 2, "sparse": 3, "upproj": 4}
 
 _c_i32, _c_i64, _c_f32, _c_sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
 
@@ -393,7 +393,7 @@ def profile_enable(enable: bool = True) -> None:
 
 def profile_read(kernel: str) -> Tuple[float, int]:
     """(total device ms, launches) of one kernel kind since profile_enable(): plan, dense,
-    combine, sparse, upproj or merge. Waits for the recorded events."""
+    combine, sparse or upproj. Waits for the recorded events."""
     ms, n = ctypes.c_double(), _c_i64()
     _check("mla_profile_read", load_library().mla_profile_read(KERNEL_IDS[kernel], ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value

@@ -50,7 +50,7 @@ const DeviceInfo* device_info() {
 }
 
 // ---- launch timing (measurement aid) ------------------------------------------------------
-constexpr int kNumKernels = 6;
+constexpr int kNumKernels = 5;
 constexpr size_t kMaxPending = 65536;
 
 struct Profiler {
@@ -256,9 +256,10 @@ static mla_status_t varlen_call(
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream,
-    float* part_o = nullptr, float* part_lse = nullptr) {
+    float* part_o = nullptr, float* part_lse = nullptr, bool accumulate = false) {
   // part_o / part_lse (internal use): write the normalised fp32 result [total_q, H, 128] and its
-  // LSE [total_q, H] there instead of `out` / `lse`, unsplit and without the sink.
+  // LSE [total_q, H] there instead of `out` / `lse`, unsplit and without the sink; with
+  // `accumulate`, merge it into the running result already held there.
   if (part_o != nullptr) num_splits = 1;
   if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
       cu_seqlens_k == nullptr || out == nullptr)
@@ -333,6 +334,7 @@ static mla_status_t varlen_call(
   } else if (part_o != nullptr) {
     dp.o_part = part_o;
     dp.lse_part = part_lse;
+    dp.accumulate = accumulate ? 1 : 0;
   }
   {
     dp.wgs_per_xcd = L.wgs_per_xcd;
@@ -413,7 +415,7 @@ namespace {
 // Workspace of mla_prefill_chunked_context: the dense workspace, then the chunk's row offsets,
 // the bounded K/V buffer and the fp32 accumulators.
 struct ChunkedLayout {
-  size_t dense, off_cu, off_k, off_v, off_acc, off_part, off_la, off_lb, off_lp, total;
+  size_t dense, off_cu, off_k, off_v, off_acc, off_la, total;
 };
 
 ChunkedLayout chunked_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_t heads, int32_t chunk) {
@@ -425,11 +427,8 @@ ChunkedLayout chunked_layout(int32_t batch, int32_t total_q, int32_t max_q, int3
   C.off_k = align256(C.off_cu + (size_t)(batch + 1) * 4);
   C.off_v = align256(C.off_k + rows * heads * kDenseDqk * 2);
   C.off_acc = align256(C.off_v + rows * heads * kDenseDv * 2);
-  C.off_part = align256(C.off_acc + th * kDenseDv * 4);
-  C.off_la = align256(C.off_part + th * kDenseDv * 4);
-  C.off_lb = align256(C.off_la + th * 4);
-  C.off_lp = align256(C.off_lb + th * 4);
-  C.total = align256(C.off_lp + th * 4);
+  C.off_la = align256(C.off_acc + th * kDenseDv * 4);
+  C.total = align256(C.off_la + th * 4);
   return C;
 }
 
@@ -506,10 +505,7 @@ mla_status_t mla_prefill_chunked_context(
   hipStream_t stream = (hipStream_t)hip_stream;
   char* ws = static_cast<char*>(workspace);
   float* acc = reinterpret_cast<float*>(ws + C.off_acc);
-  float* part = reinterpret_cast<float*>(ws + C.off_part);
   float* la = reinterpret_cast<float*>(ws + C.off_la);
-  float* lb = reinterpret_cast<float*>(ws + C.off_lb);
-  float* lp = reinterpret_cast<float*>(ws + C.off_lp);
   int32_t* cu_chunk = reinterpret_cast<int32_t*>(ws + C.off_cu);
   void* kbuf = ws + C.off_k;
   void* vbuf = ws + C.off_v;
@@ -520,7 +516,8 @@ mla_status_t mla_prefill_chunked_context(
                                 nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws, C.dense,
                                 hip_stream, acc, la);
   if (st != MLA_OK) return st;
-  // 2. each context chunk: up-project into the bounded buffer, attend without a mask, merge
+  // 2. each context chunk: up-project into the bounded buffer, attend without a mask and merge the
+  //    chunk's result into the running one in the attention kernel's epilogue
   const int64_t kst = (int64_t)num_heads * kDenseDqk, vst = (int64_t)num_heads * kDenseDv;
   const int32_t rows = total_q * num_heads;
   for (int64_t c0 = 0; c0 < max_seqlen_ctx; c0 += chunk_tokens) {
@@ -530,12 +527,8 @@ mla_status_t mla_prefill_chunked_context(
     st = varlen_call(q, q_stride_tok, q_stride_head, kbuf, kst, kDenseDqk, vbuf, vst, kDenseDv, cu_seqlens_q,
                      cu_chunk, batch, total_q, max_seqlen_q, chunk_tokens, num_heads, kDenseDqk, kDenseDv,
                      softmax_scale, 0, -1, -1, 1, nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws,
-                     C.dense, hip_stream, part, lp);
+                     C.dense, hip_stream, acc, la, true);
     if (st != MLA_OK) return st;
-    mla::MergeParams mp{acc, la, part, lp, lb, rows, kDenseDv};
-    if (timed_launch(MLA_KERNEL_MERGE, stream, [&] { return mla::launch_merge_partial(mp, stream); }) != hipSuccess)
-      return MLA_ERR_HIP;
-    std::swap(la, lb);
   }
   // 3. the accumulated result to bf16, with the sink folded in once
   mla::CombineParams cp{};

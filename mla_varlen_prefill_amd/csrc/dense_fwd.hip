@@ -393,6 +393,7 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it
   const float scale = p.scale;
   float* const o_part = p.o_part;
   float* const lse_part = p.lse_part;
+  const bool accumulate = p.accumulate != 0;
   const int64_t part_row = (int64_t)it.split * p.total_q;  // split-mode row base
   const int num_heads = p.num_heads;
   __bf16* const out_h = p.out + (int64_t)h * p.o_sh;
@@ -425,16 +426,39 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it
       const int tok = it.cq0 + it.row0 + r;
       if (o_part != nullptr) {
         float* op = o_part + ((part_row + tok) * num_heads + h) * DV;
+        float* lp = lse_part + (part_row + tok) * num_heads + h;
+        float w_new = inv, w_old = 0.f;
+        f32x4 old[DV / 32][4];
+        if (accumulate) {
+          // merge with the running result of this row (read in full before any write):
+          // LSE = log(e^L_old + e^L_new), O = (e^L_old O_old + e^L_new O_new) / e^LSE
+          const float l_old = *lp;
+#pragma unroll
+          for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; ++g4) old[dt][g4] = *reinterpret_cast<const f32x4*>(op + dt * 32 + 8 * g4 + 4 * c.hl);
+          const float mx = fmaxf(l_old, lse_v);
+          if (mx == -INFINITY) {
+            w_new = 0.f;
+          } else {
+            const float eo = __expf(l_old - mx), en = __expf(lse_v - mx);
+            const float rt = 1.f / (eo + en);
+            w_old = eo * rt;
+            w_new = inv * en * rt;
+            lse_v = mx + __logf(eo + en);
+          }
+        }
 #pragma unroll
         for (int dt = 0; dt < DV / 32; ++dt)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
             const int dv = dt * 32 + 8 * g4 + 4 * c.hl;
-            f32x4 v = {o[nq][dt][g4 * 4 + 0] * inv, o[nq][dt][g4 * 4 + 1] * inv,
-                       o[nq][dt][g4 * 4 + 2] * inv, o[nq][dt][g4 * 4 + 3] * inv};
+            f32x4 v = {o[nq][dt][g4 * 4 + 0] * w_new, o[nq][dt][g4 * 4 + 1] * w_new,
+                       o[nq][dt][g4 * 4 + 2] * w_new, o[nq][dt][g4 * 4 + 3] * w_new};
+            if (accumulate) v += old[dt][g4] * w_old;
             *reinterpret_cast<f32x4*>(op + dv) = v;
           }
-        if (c.hl == 0) lse_part[(part_row + tok) * num_heads + h] = lse_v;
+        if (c.hl == 0) *lp = lse_v;
       } else if (lse != nullptr && c.hl == 0) {
         lse[(int64_t)tok * l_st + (int64_t)h * l_sh] = lse_v;
       }

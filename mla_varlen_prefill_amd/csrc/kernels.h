@@ -46,6 +46,7 @@ struct DenseParams {
   float* lse; int64_t l_st, l_sh;
   float* o_part;         // split mode: [S][total_q][H][128] fp32, else null
   float* lse_part;       // split mode: [S][total_q][H]
+  int32_t accumulate;    // with one split: merge into o_part / lse_part (running result) in place
   int32_t total_q;
   int32_t wgs_per_xcd;   // persistent grid: 8 * wgs_per_xcd work-groups
   int32_t group_units;   // (head, split) units per scheduling group
@@ -99,18 +100,10 @@ struct UpprojParams {
   __bf16* vbuf; int64_t v_st, v_sh;        // [rows, H, 128]
 };
 
-struct MergeParams {
-  float* o_acc; const float* lse_acc;      // [rows, dv], [rows]; o_acc updated in place
-  const float* o_part; const float* lse_part;
-  float* lse_out;                          // [rows], must not alias lse_acc
-  int32_t rows, dv;
-};
-
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int32_t w, int32_t* cu_chunk,
                            hipStream_t stream);
 hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream);
-hipError_t launch_merge_partial(const MergeParams& p, hipStream_t stream);
 hipError_t launch_dense_fwd(const DenseParams& p, int nq, hipStream_t stream);
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);

@@ -1,6 +1,6 @@
 // Context from the latent cache, chunk by chunk: the kernels that turn a window of cached latent
-// rows into per-head K/V in a bounded buffer, and the merge of a chunk's partial result into the
-// running one.
+// rows into per-head K/V in a bounded buffer. (A chunk's partial result is merged into the running
+// one by the attention kernel's epilogue.)
 //
 // The pages run the new tokens causally against themselves and every context chunk without a
 // mask, always returning the LSE, and merge the parts (page "FlashAttention backend for MLA
@@ -185,31 +185,6 @@ __global__ __launch_bounds__(UP_THREADS) void upproj_kernel(UpprojParams p) {
   }
 }
 
-// Running merge of a chunk's partial result into the accumulated one, rows of dv columns:
-// LSE = log(exp(L_acc) + exp(L_part)), O = w_acc O_acc + w_part O_part with w = exp(L - LSE);
-// the accumulated O is updated in place, the new LSE goes to lse_out (other threads of the row
-// still read lse_acc). Rows empty on both sides keep O = 0 and LSE = -inf.
-__global__ __launch_bounds__(256) void merge_partial_kernel(MergeParams p) {
-  const int c4_per_row = p.dv >> 2;
-  const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (t >= (int64_t)p.rows * c4_per_row) return;
-  const int64_t row = t / c4_per_row;
-  const int c4 = (int)(t - row * c4_per_row);
-  const float la = p.lse_acc[row], lp = p.lse_part[row];
-  const float mx = fmaxf(la, lp);
-  f32x4* oa = reinterpret_cast<f32x4*>(p.o_acc + row * p.dv + c4 * 4);
-  if (mx == -INFINITY) {
-    if (c4 == 0) p.lse_out[row] = -INFINITY;
-    return;
-  }
-  const float wa = __expf(la - mx), wp = __expf(lp - mx);
-  const float tot = wa + wp;
-  const f32x4 op = *reinterpret_cast<const f32x4*>(p.o_part + row * p.dv + c4 * 4);
-  const f32x4 cur = *oa;
-  *oa = (cur * wa + op * wp) * (1.f / tot);
-  if (c4 == 0) p.lse_out[row] = mx + __logf(tot);
-}
-
 hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int32_t w, int32_t* cu_chunk,
                            hipStream_t stream) {
   hipLaunchKernelGGL(chunk_cu_kernel, dim3(1), dim3(1024), 0, stream, cu_ctx, batch, c0, w, cu_chunk);
@@ -220,13 +195,6 @@ hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream) {
   const int tiles = (p.w + UP_TILE - 1) / UP_TILE;
   if (tiles == 0 || p.batch == 0) return hipSuccess;
   hipLaunchKernelGGL(upproj_kernel, dim3(tiles, p.batch, 2 * p.num_heads), dim3(UP_THREADS), 0, stream, p);
-  return hipGetLastError();
-}
-
-hipError_t launch_merge_partial(const MergeParams& p, hipStream_t stream) {
-  const int64_t threads = (int64_t)p.rows * (p.dv >> 2);
-  if (threads == 0) return hipSuccess;
-  hipLaunchKernelGGL(merge_partial_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
