@@ -94,6 +94,11 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
  * varlen API's I/O contract and num_splits (0 = heuristic, 1 = no split) follow page
  * "Sgl project Sglang FA4 Interface" (Signature, I/O Contract).
  *
+ * Head dimensions (head_dim_qk, head_dim_v): (192, 128), the layout above, and the other MLA
+ * layouts the same backend lists (supports_mla_dimensions): nope 64 + rope 64 with v 128 =
+ * (128, 128); nope 192 + rope 64 and nope 256 + rope 0, both with v 256 = (256, 256). Written
+ * below for (192, 128); Dqk / Dv stand for the pair in use.
+ *
  *   q   : bf16 [total_q, H, 192], strides (q_stride_tok, q_stride_head)
  *   k   : bf16 [total_k, H, 192], strides (k_stride_tok, k_stride_head)
  *   v   : bf16 [total_k, H, 128], strides (v_stride_tok, v_stride_head); V may be a strided view
@@ -108,19 +113,21 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
  *   out  : bf16 [total_q, H, 128], strides (o_stride_tok, o_stride_head), written.
  *   lse  : nullable float32 [total_q, H], strides (lse_stride_tok, lse_stride_head), written.
  *   workspace : device memory of at least mla_prefill_varlen_workspace_size(...) bytes with the
- *         same batch/total_q/max_seqlen/H/num_splits; scratch only, contents undefined after.
+ *         same batch/total_q/max_seqlen/H/head_dim_v/num_splits (it returns 0 for arguments it
+ *         rejects, a head_dim_v other than 128 or 256 included); scratch only, contents undefined
+ *         after.
  *         It holds the plan and the work-ticket counters of the call: calls that may overlap in
  *         time (other streams) must not share a workspace.
  * Tuning (environment, read by the library): MLA_DENSE_NQ=2 selects 256-row query tiles (one
- * work-group per CU); MLA_DENSE_GROUP=n schedules n (head, split) units per XCD at a time
+ * work-group per CU; (192, 128) with bf16 output only, other instances keep 128 rows); MLA_DENSE_GROUP=n schedules n (head, split) units per XCD at a time
  * (default 1); MLA_DENSE_WGS_PER_XCD=n caps the persistent grid at 8*n work-groups (default: all
  * resident slots). The last two leave results bitwise unchanged (each work item is computed the
  * same way whichever work-group runs it); the tile height may change them within rounding.
  * With num_splits == 1 a sequence's result does not depend on the other sequences in the batch,
  * and repeated calls are bitwise identical.
  * Errors: INVALID_ARG (null q/k/v/cu/out, sizes <= 0 where a count is required, strides smaller
- * than the row they hold, num_splits outside [0, 64]); UNSUPPORTED (head dims other than
- * 192/128, H > 65535, max_seqlen_k beyond 2^24, K or V token stride of 2^23 elements or more);
+ * than the row they hold, num_splits outside [0, 64]); UNSUPPORTED (head dims other than the
+ * three pairs above, H > 65535, max_seqlen_k beyond 2^24, K or V token stride of 2^23 elements or more);
  * ALIGNMENT; WORKSPACE; HIP.
  * ------------------------------------------------------------------------------------------ */
 size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
@@ -162,6 +169,37 @@ mla_status_t mla_prefill_varlen_window(
     int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
     float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
     int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
+ * Dense varlen MLA prefill with FP8 output under a static per-tensor scale.
+ *
+ * The FA4 path of the MLA prefill backend can emit its output already quantised to FP8 with a
+ * static, symmetric per-tensor scale (page "FlashAttention backend for MLA prefill",
+ * supports_quant_output with kFp8StaticTensorSym). Reading: the stored value is the OCP FP8
+ * E4M3 (finite-only, bias 7, max 448) encoding, rounded to nearest even, of O / out_scale, where
+ * O is the fp32 normalised attention output; values beyond +-448 saturate to +-448. The LSE
+ * stays float32 and unscaled.
+ *
+ * Arguments are those of mla_prefill_varlen_window, except:
+ *   out_scale : device float32 [1], > 0 (read on the device; not validated).
+ *   out       : fp8 e4m3 bytes [total_q, H, Dv], strides in elements (bytes) that are multiples
+ *               of 16; 16-byte aligned.
+ * The workspace is sized by mla_prefill_varlen_workspace_size with the same head_dim_v.
+ * Errors: as mla_prefill_varlen_window; INVALID_ARG also for a null out_scale; ALIGNMENT for an
+ * output stride that is not a multiple of 16 or an out_scale not 4-byte aligned.
+ * ------------------------------------------------------------------------------------------ */
+mla_status_t mla_prefill_varlen_fp8(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+    int32_t num_splits, const float* sink, const float* out_scale,
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream);

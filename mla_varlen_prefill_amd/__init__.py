@@ -8,7 +8,9 @@ gfx950 GPU, every call raises.
 
 Entry points (same names as the C ABI):
   mla_prefill_varlen  dense varlen prefill, q/k 192 = 128 nope + 64 rope, v 128, causal or not
+                      (also the other MLA layouts: q/k 128 with v 128, q/k 256 with v 256)
   mla_prefill_varlen_window  the same with a (left, right) sliding-window band mask
+  mla_prefill_varlen_fp8  the same with FP8 e4m3 output under a static per-tensor scale
   mla_prefill_sparse  sparse top-k prefill over one shared 576-wide latent KV (v = first 512)
   mla_prefill_sparse_paged  the same over a paged latent cache with logical indices
   mla_prefill_chunked_context  new tokens over an up-projected latent context, chunk by chunk
@@ -34,7 +36,7 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 EXPORTED_SYMBOLS = (
     "mla_status_string", "mla_abi_version", "mla_dense_tile_shape", "mla_prefill_plan",
     "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_window",
-    "mla_prefill_varlen_num_splits",
+    "mla_prefill_varlen_fp8", "mla_prefill_varlen_num_splits",
     "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_prefill_sparse_paged",
     "mla_prefill_chunked_context_workspace_size", "mla_prefill_chunked_context", "mla_latent_upproject",
     "mla_combine",
@@ -84,6 +86,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
         _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
         _c_f32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp,
+        _c_sz, _vp]
+    lib.mla_prefill_varlen_fp8.restype = ctypes.c_int
+    lib.mla_prefill_varlen_fp8.argtypes = [
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+        _c_f32, _c_i32, _c_i32, _c_i32, _c_i32, _vp, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp,
         _c_sz, _vp]
     lib.mla_prefill_sparse_workspace_size.restype = _c_sz
     lib.mla_prefill_sparse_workspace_size.argtypes = [_c_i32] * 4
@@ -185,11 +193,14 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                        return_lse: bool = True, lse: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None,
-                       window: Optional[Tuple[int, int]] = None):
-    """Dense varlen MLA prefill. q [Tq,H,192], k [Tk,H,192], v [Tk,H,128] bf16 (last dim
-    contiguous; V may be strided); cu_seqlens int32 [B+1]. With ``window`` = (left, right)
-    (-1 = unlimited) the sliding-window entry point mla_prefill_varlen_window is called. Returns
-    out [Tq,H,128] bf16 and, when ``return_lse``, lse float32 [Tq,H]."""
+                       window: Optional[Tuple[int, int]] = None,
+                       out_scale: Optional[torch.Tensor] = None):
+    """Dense varlen MLA prefill. q [Tq,H,Dqk], k [Tk,H,Dqk], v [Tk,H,Dv] bf16 with (Dqk, Dv) one
+    of (192, 128), (128, 128), (256, 256) (last dim contiguous; V may be strided); cu_seqlens
+    int32 [B+1]. With ``window`` = (left, right) (-1 = unlimited) the sliding-window entry point
+    mla_prefill_varlen_window is called; with ``out_scale`` (float32 [1] on the device) the
+    output is FP8 e4m3 of O / out_scale through mla_prefill_varlen_fp8. Returns out [Tq,H,Dv]
+    (bf16, or float8_e4m3fn) and, when ``return_lse``, lse float32 [Tq,H]."""
     lib = load_library()
     _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, sink, out, lse, workspace)
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -200,8 +211,16 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     total_q, heads, dqk = q.shape
     dv = v.shape[2]
     batch = cu_seqlens_q.numel() - 1
+    fp8 = out_scale is not None
+    if fp8:
+        _require_cuda(out_scale)
+        if out_scale.dtype != torch.float32 or out_scale.numel() != 1:
+            raise ValueError("out_scale must be a float32 tensor of one element")
     if out is None:
-        out = torch.empty((total_q, heads, dv), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((total_q, heads, dv), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16,
+                          device=q.device)
+    elif out.element_size() != (1 if fp8 else 2):
+        raise ValueError("out must be float8_e4m3fn with out_scale, else bf16")
     if return_lse and lse is None:
         lse = torch.empty((total_q, heads), dtype=torch.float32, device=q.device)
     ws_bytes = lib.mla_prefill_varlen_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k,
@@ -217,7 +236,12 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     tail = (num_splits, _ptr(sink), _ptr(out), out.stride(0), out.stride(1),
             _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
             _ptr(workspace), workspace.numel() * workspace.element_size(), _stream())
-    if window is None:
+    if fp8:
+        left, right = window if window is not None else (-1, -1)
+        _check("mla_prefill_varlen_fp8",
+               lib.mla_prefill_varlen_fp8(*head, int(left), int(right), num_splits, _ptr(sink), _ptr(out_scale),
+                                          *tail[2:]))
+    elif window is None:
         _check("mla_prefill_varlen", lib.mla_prefill_varlen(*head, *tail))
     else:
         _check("mla_prefill_varlen_window",
@@ -232,6 +256,16 @@ def mla_prefill_varlen_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     """Dense varlen MLA prefill with a (left, right) sliding window, -1 = unlimited."""
     return mla_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                               softmax_scale, causal=causal, window=(window_left, window_right), **kw)
+
+
+def mla_prefill_varlen_fp8(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                           max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                           out_scale: torch.Tensor, causal: bool = True, **kw):
+    """Dense varlen MLA prefill with FP8 e4m3 output of O / out_scale (static per-tensor scale,
+    float32 [1] on the device); the LSE stays float32."""
+    return mla_prefill_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                              softmax_scale, causal=causal, out_scale=out_scale, **kw)
 
 
 def mla_prefill_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,

@@ -102,6 +102,24 @@ int dense_nq() {
 }
 int dense_bm() { return 128 * dense_nq(); }
 
+// Head dimensions the dense kernels are built for: (q/k head, v head) = (192, 128), the default
+// MLA layout 128 nope + 64 rope with v 128, and the other layouts (64 + 64, v 128) = (128, 128),
+// (192 + 64, v 256) and (256 + 0, v 256) = (256, 256).
+bool dense_dims_ok(int dqk, int dv) {
+  return (dqk == 192 && dv == 128) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256);
+}
+
+// Instance of a dense call: its tile height (nq * 128 rows) and resident work-groups per CU.
+struct DenseShape {
+  int dqk, dv, nq, occ;
+  bool fp8;
+};
+DenseShape dense_shape(int dqk, int dv, bool fp8) {
+  DenseShape d{dqk, dv, (dqk == 192 && dv == 128 && !fp8) ? dense_nq() : 1, 1, fp8};
+  d.occ = mla::dense_occupancy_of(d.nq, dqk, dv);
+  return d;
+}
+
 // Dense scheduling groups: each XCD works through `n` (head, split) units at a time (longest
 // item first within a group). MLA_DENSE_GROUP overrides the default.
 int dense_group_per_xcd() {
@@ -125,15 +143,15 @@ struct VarlenLayout {
 };
 
 int32_t resolve_splits(int32_t batch, int32_t max_q, int32_t max_k, int32_t heads,
-                       int32_t num_splits) {
+                       int32_t num_splits, const DenseShape& ds) {
   if (num_splits >= 1) return num_splits;
   // Heuristic (our own; the pages name a num_splits_heuristic over M-blocks and SM count): split
-  // the keys only when the (tile, head) work items cannot fill every CU with two resident
+  // the keys only when the (tile, head) work items cannot fill every CU with its resident
   // work-groups, and keep at least four key blocks per split.
   const DeviceInfo* di = device_info();
   const int cus = (di != nullptr && di->cus > 0) ? di->cus : 256;
-  const int64_t conc = (int64_t)cus * (dense_nq() == 1 ? 2 : 1);
-  const int64_t items = (int64_t)batch * cdiv(max_q, dense_bm()) * heads;
+  const int64_t conc = (int64_t)cus * ds.occ;
+  const int64_t items = (int64_t)batch * cdiv(max_q, 128 * ds.nq) * heads;
   if (items <= 0 || items >= conc) return 1;
   const int64_t max_blocks = cdiv(max_k, kDenseBN);
   int64_t s = cdiv(conc, items);
@@ -143,19 +161,19 @@ int32_t resolve_splits(int32_t batch, int32_t max_q, int32_t max_k, int32_t head
 }
 
 VarlenLayout varlen_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_t max_k,
-                           int32_t heads, int32_t num_splits) {
+                           int32_t heads, int32_t num_splits, const DenseShape& ds) {
   VarlenLayout L{};
-  L.bm = dense_bm();
+  L.bm = 128 * ds.nq;
   L.mt = (int32_t)cdiv(std::max(max_q, 0), L.bm);
   L.n_slots = batch * L.mt;
-  L.splits = resolve_splits(batch, max_q, max_k, heads, num_splits);
+  L.splits = resolve_splits(batch, max_q, max_k, heads, num_splits, ds);
   {
-    // Persistent dense grid: every resident work-group slot (two per CU with 128-row tiles), but
-    // no more work-groups than work items.
+    // Persistent dense grid: every resident work-group slot, but no more work-groups than work
+    // items.
     const DeviceInfo* di = device_info();
     const int cus = (di != nullptr && di->cus > 0) ? di->cus : 256;
-    const int occ = dense_nq() == 1 ? 2 : 1;
-    const int64_t max_work = (int64_t)L.n_slots * heads * L.splits;
+    const int occ = ds.occ;
+    const int64_t max_work = (int64_t)L.n_slots * heads * L.splits * (ds.dv / 128);
     const int64_t per_xcd = std::max<int64_t>(1, (int64_t)(cus / 8) * occ);
     int64_t want = per_xcd;
     if (const char* e = std::getenv("MLA_DENSE_WGS_PER_XCD")) want = std::max(1, std::atoi(e));
@@ -170,7 +188,7 @@ VarlenLayout varlen_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_
   L.off_lpart = off;
   if (L.splits > 1) {
     L.off_opart = off;
-    off = align256(off + (size_t)L.splits * total_q * heads * kDenseDv * sizeof(float));
+    off = align256(off + (size_t)L.splits * total_q * heads * ds.dv * sizeof(float));
     L.off_lpart = off;
     off = align256(off + (size_t)L.splits * total_q * heads * sizeof(float));
   }
@@ -230,18 +248,27 @@ int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32
                                       int32_t num_heads, int32_t causal, int32_t num_splits) {
   (void)causal;
   if (num_splits < 0 || num_splits > kMaxSplits) return -1;
-  return resolve_splits(batch, max_seqlen_q, max_seqlen_k, num_heads, num_splits);
+  return resolve_splits(batch, max_seqlen_q, max_seqlen_k, num_heads, num_splits,
+                        dense_shape(kDenseDqk, kDenseDv, false));
 }
 
 size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
                                          int32_t max_seqlen_k, int32_t num_heads,
                                          int32_t head_dim_v, int32_t causal, int32_t num_splits) {
   (void)causal;
-  (void)head_dim_v;
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads <= 0 ||
-      num_splits < 0 || num_splits > kMaxSplits)
+      num_splits < 0 || num_splits > kMaxSplits || (head_dim_v != 128 && head_dim_v != 256))
     return 0;
-  return varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits).total;
+  // enough for every instance with this v head (tile height and output type vary the layout)
+  size_t need = 0;
+  const int dqks[2] = {head_dim_v == 128 ? 192 : 256, 128};
+  for (int dqk : dqks) {
+    if (!dense_dims_ok(dqk, head_dim_v)) continue;
+    for (bool fp8 : {false, true})
+      need = std::max(need, varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits,
+                                          dense_shape(dqk, head_dim_v, fp8)).total);
+  }
+  return need;
 }
 
 static mla_status_t varlen_call(
@@ -252,12 +279,13 @@ static mla_status_t varlen_call(
     int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
     int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
     float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
-    int32_t num_splits, const float* sink,
+    int32_t num_splits, const float* sink, const float* out_scale,
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream,
     float* part_o = nullptr, float* part_lse = nullptr, bool accumulate = false) {
-  // part_o / part_lse (internal use): write the normalised fp32 result [total_q, H, 128] and its
+  // out_scale: null for bf16 output, else fp8 e4m3 output of O / *out_scale.
+  // part_o / part_lse (internal use): write the normalised fp32 result [total_q, H, Dv] and its
   // LSE [total_q, H] there instead of `out` / `lse`, unsplit and without the sink; with
   // `accumulate`, merge it into the running result already held there.
   if (part_o != nullptr) num_splits = 1;
@@ -269,26 +297,32 @@ static mla_status_t varlen_call(
       window_left < -1 || window_right < -1)
     return MLA_ERR_INVALID_ARG;
   const int32_t right = causal ? 0 : window_right;  // causal is the right window 0
-  if (head_dim_qk != kDenseDqk || head_dim_v != kDenseDv || num_heads > 65535 ||
+  if (!dense_dims_ok(head_dim_qk, head_dim_v) || num_heads > 65535 ||
       max_seqlen_k > (1 << 24) || k_stride_tok >= (1 << 23) || v_stride_tok >= (1 << 23))
     return MLA_ERR_UNSUPPORTED;  // key-block byte offsets are kept in 31 bits
+  const bool fp8 = out_scale != nullptr && part_o == nullptr;
+  const DenseShape ds = dense_shape(head_dim_qk, head_dim_v, fp8);
+  // fp8 rows are written in 16-byte pieces: strides in whole 16-element units
+  const bool ostride_ok = fp8 ? ((o_stride_tok & 15) == 0 && (o_stride_head & 15) == 0)
+                              : (stride_ok(o_stride_tok) && stride_ok(o_stride_head));
   const int64_t H = num_heads;
   auto rows_ok = [H](int64_t st, int64_t sh, int64_t width) {
     return sh >= 0 && st >= 0 && (H == 1 || sh >= width) && st >= (H - 1) * sh + width;
   };
-  if (!rows_ok(q_stride_tok, q_stride_head, kDenseDqk) || !rows_ok(k_stride_tok, k_stride_head, kDenseDqk) ||
-      !rows_ok(v_stride_tok, v_stride_head, kDenseDv) || !rows_ok(o_stride_tok, o_stride_head, kDenseDv))
+  if (!rows_ok(q_stride_tok, q_stride_head, head_dim_qk) || !rows_ok(k_stride_tok, k_stride_head, head_dim_qk) ||
+      !rows_ok(v_stride_tok, v_stride_head, head_dim_v) || !rows_ok(o_stride_tok, o_stride_head, head_dim_v))
     return MLA_ERR_INVALID_ARG;
   if (lse != nullptr && (lse_stride_tok < 0 || lse_stride_head < 0)) return MLA_ERR_INVALID_ARG;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out) ||
       !stride_ok(q_stride_tok) || !stride_ok(q_stride_head) || !stride_ok(k_stride_tok) ||
-      !stride_ok(k_stride_head) || !stride_ok(v_stride_tok) || !stride_ok(v_stride_head) ||
-      !stride_ok(o_stride_tok) || !stride_ok(o_stride_head) ||
-      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0))
+      !stride_ok(k_stride_head) || !stride_ok(v_stride_tok) || !stride_ok(v_stride_head) || !ostride_ok ||
+      (lse != nullptr && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) ||
+      (out_scale != nullptr && (reinterpret_cast<uintptr_t>(out_scale) & 3u) != 0))
     return MLA_ERR_ALIGNMENT;
   if (batch == 0 || total_q == 0) return MLA_OK;
-  const VarlenLayout L = varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits);
-  if ((int64_t)L.n_slots * num_heads * L.splits > INT32_MAX - 8) return MLA_ERR_UNSUPPORTED;
+  const VarlenLayout L = varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits, ds);
+  const int dv_tiles = head_dim_v / 128;  // work items per (row tile, head, split): 128 columns each
+  if ((int64_t)L.n_slots * num_heads * L.splits * dv_tiles > INT32_MAX - 8) return MLA_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   const DeviceInfo* di = device_info();
@@ -325,7 +359,8 @@ static mla_status_t varlen_call(
   dp.scale = softmax_scale;
   dp.scale_log2 = softmax_scale * 1.4426950408889634f;
   dp.sink = sink;
-  dp.out = static_cast<__bf16*>(out); dp.o_st = o_stride_tok; dp.o_sh = o_stride_head;
+  dp.out = out; dp.o_st = o_stride_tok; dp.o_sh = o_stride_head;
+  dp.out_scale = fp8 ? out_scale : nullptr;
   dp.lse = lse; dp.l_st = lse_stride_tok; dp.l_sh = lse_stride_head;
   dp.total_q = total_q;
   if (L.splits > 1) {
@@ -338,7 +373,7 @@ static mla_status_t varlen_call(
   }
   {
     dp.wgs_per_xcd = L.wgs_per_xcd;
-    const int units = num_heads * L.splits;
+    const int units = num_heads * L.splits * dv_tiles;
     const char* map = std::getenv("MLA_DENSE_XCD_MAP");
     const bool contiguous = units % 8 == 0 && !(map != nullptr && std::string(map) == "interleave");
     if (contiguous) {
@@ -352,7 +387,7 @@ static mla_status_t varlen_call(
     }
     dp.counters = tickets;
   }
-  if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, dense_nq(), stream); }) !=
+  if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, ds.nq, ds.dqk, ds.dv, ds.fp8, stream); }) !=
       hipSuccess)
     return MLA_ERR_HIP;
 
@@ -363,9 +398,10 @@ static mla_status_t varlen_call(
     cp.num_splits = L.splits;
     cp.rows = total_q * num_heads;
     cp.num_heads = num_heads;
-    cp.dv = kDenseDv;
+    cp.dv = head_dim_v;
     cp.sink = sink;
     cp.out = dp.out; cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
+    cp.out_scale = dp.out_scale;
     cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
     if (timed_launch(MLA_KERNEL_COMBINE, stream, [&] { return mla::launch_combine(cp, stream); }) != hipSuccess)
       return MLA_ERR_HIP;
@@ -387,7 +423,7 @@ mla_status_t mla_prefill_varlen(
   return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
                      v_stride_head, cu_seqlens_q, cu_seqlens_k, batch, total_q, max_seqlen_q,
                      max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal, -1, -1,
-                     num_splits, sink, out, o_stride_tok, o_stride_head, lse, lse_stride_tok,
+                     num_splits, sink, nullptr, out, o_stride_tok, o_stride_head, lse, lse_stride_tok,
                      lse_stride_head, workspace, workspace_bytes, hip_stream);
 }
 
@@ -406,7 +442,27 @@ mla_status_t mla_prefill_varlen_window(
   return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
                      v_stride_head, cu_seqlens_q, cu_seqlens_k, batch, total_q, max_seqlen_q,
                      max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal,
-                     window_left, window_right, num_splits, sink, out, o_stride_tok, o_stride_head,
+                     window_left, window_right, num_splits, sink, nullptr, out, o_stride_tok, o_stride_head,
+                     lse, lse_stride_tok, lse_stride_head, workspace, workspace_bytes, hip_stream);
+}
+
+mla_status_t mla_prefill_varlen_fp8(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t window_left, int32_t window_right,
+    int32_t num_splits, const float* sink, const float* out_scale,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
+    void* workspace, size_t workspace_bytes, void* hip_stream) {
+  if (out_scale == nullptr) return MLA_ERR_INVALID_ARG;
+  return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
+                     v_stride_head, cu_seqlens_q, cu_seqlens_k, batch, total_q, max_seqlen_q,
+                     max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal,
+                     window_left, window_right, num_splits, sink, out_scale, out, o_stride_tok, o_stride_head,
                      lse, lse_stride_tok, lse_stride_head, workspace, workspace_bytes, hip_stream);
 }
 
@@ -420,7 +476,8 @@ struct ChunkedLayout {
 
 ChunkedLayout chunked_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_t heads, int32_t chunk) {
   ChunkedLayout C{};
-  C.dense = align256(varlen_layout(batch, total_q, max_q, std::max(max_q, chunk), heads, 1).total);
+  C.dense = align256(varlen_layout(batch, total_q, max_q, std::max(max_q, chunk), heads, 1,
+                                   dense_shape(kDenseDqk, kDenseDv, false)).total);
   const size_t rows = (size_t)batch * chunk;
   const size_t th = (size_t)total_q * heads;
   C.off_cu = C.dense;
@@ -513,7 +570,7 @@ mla_status_t mla_prefill_chunked_context(
   mla_status_t st = varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
                                 v_stride_head, cu_seqlens_q, cu_seqlens_q, batch, total_q, max_seqlen_q,
                                 max_seqlen_q, num_heads, kDenseDqk, kDenseDv, softmax_scale, 1, -1, -1, 1,
-                                nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws, C.dense,
+                                nullptr, nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws, C.dense,
                                 hip_stream, acc, la);
   if (st != MLA_OK) return st;
   // 2. each context chunk: up-project into the bounded buffer, attend without a mask and merge the
@@ -526,7 +583,7 @@ mla_status_t mla_prefill_chunked_context(
     if (st != MLA_OK) return st;
     st = varlen_call(q, q_stride_tok, q_stride_head, kbuf, kst, kDenseDqk, vbuf, vst, kDenseDv, cu_seqlens_q,
                      cu_chunk, batch, total_q, max_seqlen_q, chunk_tokens, num_heads, kDenseDqk, kDenseDv,
-                     softmax_scale, 0, -1, -1, 1, nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws,
+                     softmax_scale, 0, -1, -1, 1, nullptr, nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws,
                      C.dense, hip_stream, acc, la, true);
     if (st != MLA_OK) return st;
   }
@@ -539,7 +596,7 @@ mla_status_t mla_prefill_chunked_context(
   cp.num_heads = num_heads;
   cp.dv = kDenseDv;
   cp.sink = sink;
-  cp.out = static_cast<__bf16*>(out); cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
+  cp.out = out; cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
   cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
   return timed_launch(MLA_KERNEL_COMBINE, stream, [&] { return mla::launch_combine(cp, stream); }) == hipSuccess
              ? MLA_OK
@@ -697,7 +754,7 @@ mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num
   cp.num_heads = num_heads;
   cp.dv = head_dim_v;
   cp.sink = sink;
-  cp.out = static_cast<__bf16*>(out); cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
+  cp.out = out; cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
   cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
   return timed_launch(MLA_KERNEL_COMBINE, (hipStream_t)hip_stream,
                       [&] { return mla::launch_combine(cp, (hipStream_t)hip_stream); }) == hipSuccess

@@ -1,5 +1,6 @@
 // Split-KV combine: merges S normalised partial results of disjoint key sets (and optionally a
-// sink logit with a zero value vector) into the final bf16 output and float32 LSE.
+// sink logit with a zero value vector) into the final output (bf16, or fp8 e4m3 with a static
+// scale) and float32 LSE.
 //
 // Prior art: per-partition partial outputs reduced into the final result (page "Mojo module
 // mla", mla_splitk_reduce; page "Sgl project Sglang FA4 Interface", Description: split-KV with
@@ -43,9 +44,20 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
       acc += wgt * v;
     }
   }
-  __bf16* op = p.out + (int64_t)tok * p.o_st + (int64_t)h * p.o_sh + c4 * 4;
-  u32x2 ov = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
-  *reinterpret_cast<u32x2*>(op) = ov;
+  const int64_t off = (int64_t)tok * p.o_st + (int64_t)h * p.o_sh + c4 * 4;
+  if (p.out_scale != nullptr) {
+    // fp8 e4m3 (round to nearest even) of O / out_scale, saturated at +-448
+    const float w = 1.f / p.out_scale[0];
+    float x[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = fminf(fmaxf(acc[i] * w, -448.f), 448.f);
+    int v = __builtin_amdgcn_cvt_pk_fp8_f32(x[0], x[1], 0, false);
+    v = __builtin_amdgcn_cvt_pk_fp8_f32(x[2], x[3], v, true);
+    *reinterpret_cast<int*>(static_cast<uint8_t*>(p.out) + off) = v;
+  } else {
+    u32x2 ov = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3])};
+    *reinterpret_cast<u32x2*>(static_cast<__bf16*>(p.out) + off) = ov;
+  }
   if (p.lse != nullptr && c4 == 0) p.lse[(int64_t)tok * p.l_st + (int64_t)h * p.l_sh] = lse_v;
 }
 

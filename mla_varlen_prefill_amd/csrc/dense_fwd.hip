@@ -42,30 +42,54 @@ namespace mla {
 namespace {
 
 constexpr int BN = 64;
-constexpr int DQK = 192;
-constexpr int DV = 128;
-constexpr int K_STAGE_BYTES = BN * DQK * 2;   // 24576
-constexpr int V_STAGE_BYTES = BN * DV * 2;    // 16384
-constexpr int K_CHUNKS_PER_WAVE = BN * (DQK / 8) / 256;  // 6 wave-wide 1 KiB copies
-constexpr int V_CHUNKS_PER_WAVE = BN * (DV / 8) / 256;   // 4
 
 constexpr float kRescaleLog2 = 8.f;  // rescale O only when a row max grows by more than 2^8
-// Bytes of a wave's K copy region used by the epilogue's output turn-around (32 rows x 128 B);
-// the rest of the region holds the work ticket handed between waves.
+// Bytes of a wave's K copy region used by the epilogue's output turn-around (32 rows x 128 B).
 constexpr int kEpilogueBytes = 32 * 128;
-static_assert(kEpilogueBytes + 4 <= K_CHUNKS_PER_WAVE * 1024, "ticket slot past the region");
+
+// Head dimensions (q/k head DQK, v head DV) and output type of a kernel instance. A work item
+// computes DVT = 128 of the DV output columns (DVH = DV / DVT items per row tile and head, all
+// computing the same scores): a wave's 32 x 256 fp32 output tile would not fit the registers
+// beside its Q fragments.
+template <int DQK_, int DV_, bool FP8_>
+struct Shape {
+  static constexpr int DQK = DQK_, DV = DV_;
+  static constexpr int DVT = 128, DVH = DV / DVT;
+  static constexpr bool FP8 = FP8_;                         // fp8 e4m3 output with a static scale
+  static constexpr int K_STAGE_BYTES = BN * DQK * 2;
+  static constexpr int V_STAGE_BYTES = BN * DVT * 2;
+  static constexpr int KCH = BN * (DQK / 8) / 256;          // wave-wide 1 KiB copies per K block
+  static constexpr int VCH = BN * (DVT / 8) / 256;
+  // K operand addressing: the swizzle permutes 16-byte chunks inside groups of KA_GROUP bytes;
+  // KA_N per-lane offsets cover one group's MFMA steps.
+  static constexpr int KA_GROUP = DQK == 192 ? 128 : 256;
+  static constexpr int KA_N = KA_GROUP / 32;
+  // The work ticket handed between waves sits past the epilogue area of the wave's K copy region
+  // when it fits there, else at the start of the wave's V copy region (which the epilogue never uses).
+  static constexpr bool TICKET_IN_K = kEpilogueBytes + 4 <= KCH * 1024;
+  static_assert((BN * DQK / 8) % 256 == 0 && DV % DVT == 0, "shape");
+};
+
+// K swizzle: chunk c of row r is stored at chunk c ^ kswz(r). 384-byte rows (an odd multiple of
+// 128 bytes) use row_swz; rows that are a multiple of 256 bytes start on bank 0, and XOR-ing the
+// low four bits with r & 15 gives the 16 rows of every operand read cycle 16 distinct 16-byte bank
+// groups.
+template <class S>
+__device__ __forceinline__ int kswz(int r) {
+  return S::DQK == 192 ? row_swz(r) : (r & 15);
+}
 
 // Per-lane constants of a work-group (the same for every work item it runs).
-template <int NQ>
+template <int NQ, class S>
 struct DenseCtx {
   int lane, wave, l32, hl;
   int k_st_b, v_st_b;  // token strides in bytes (validated to keep 64-row offsets in 31 bits)
-  uint32_t koff[K_CHUNKS_PER_WAVE];  // byte offset of this lane's 16-byte chunk inside a block
-  uint32_t voff[V_CHUNKS_PER_WAVE];
+  uint32_t koff[S::KCH];  // byte offset of this lane's 16-byte chunk inside a block
+  uint32_t voff[S::VCH];
   int kdst, vdst;                    // this wave's first 1 KiB slot in a stage (bytes)
   // LDS operand addresses (bytes, relative to a stage)
-  int ka[4];                         // K rows: + g*128 + mt*32*384 per 4-step group g
-  int va[DV / 32];                   // V rows: + (mt*32 + cc*16 [+8]) * 256 per step
+  int ka[S::KA_N];                   // K rows: + g*KA_GROUP + mt*32*DQK*2 per step group g
+  int va[S::DVT / 32];               // V rows: + (mt*32 + cc*16 [+8]) * DVT*2 per step
 };
 
 // One work item (wave-uniform): query tile `row0` of sequence b, head h, key blocks [blo, bhi).
@@ -73,6 +97,7 @@ struct Item {
   const char* kbase;  // K of this sequence/head at key 0 (bytes)
   const char* vbase;
   int cq0, sq, sk, row0, rows, blo, bhi, h, split;
+  int dvh;            // output column tile: columns [dvh * DVT, (dvh + 1) * DVT)
 };
 
 // 32-bit value the optimiser must treat as opaque (keeps precomputed offsets 32-bit at their use
@@ -82,30 +107,30 @@ __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   return x;
 }
 
-template <int NQ>
-__device__ __forceinline__ void issue_block_load(const DenseCtx<NQ>& c, const Item& it, int j, char* kst,
+template <int NQ, class S>
+__device__ __forceinline__ void issue_block_load(const DenseCtx<NQ, S>& c, const Item& it, int j, char* kst,
                                                  char* vst) {
   const int key0 = j * BN;
   const char* kb = it.kbase + (int64_t)key0 * c.k_st_b;
   const char* vb = it.vbase + (int64_t)key0 * c.v_st_b;
   if (key0 + BN <= it.sk) {
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) g2lds16(kb + opaque(c.koff[i]), kst + c.kdst + i * 1024);
+    for (int i = 0; i < S::KCH; ++i) g2lds16(kb + opaque(c.koff[i]), kst + c.kdst + i * 1024);
 #pragma unroll
-    for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) g2lds16(vb + opaque(c.voff[i]), vst + c.vdst + i * 1024);
+    for (int i = 0; i < S::VCH; ++i) g2lds16(vb + opaque(c.voff[i]), vst + c.vdst + i * 1024);
   } else {
     // tail block: rows past the sequence re-read its last key (finite values, masked later)
     const int last = it.sk - 1 - key0;
     const int lane = (int)opaque((uint32_t)c.lane);
 #pragma unroll
-    for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) {
-      const int r = ((c.wave * K_CHUNKS_PER_WAVE + i) * 64 + lane) / 24;
+    for (int i = 0; i < S::KCH; ++i) {
+      const int r = (int)((uint32_t)((c.wave * S::KCH + i) * 64 + lane) / (uint32_t)(S::DQK / 8));
       const int shift = (min(r, last) - r) * c.k_st_b;
       g2lds16(kb + (uint32_t)((int)c.koff[i] + shift), kst + c.kdst + i * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) {
-      const int r = ((c.wave * V_CHUNKS_PER_WAVE + i) * 64 + lane) >> 4;
+    for (int i = 0; i < S::VCH; ++i) {
+      const int r = (int)((uint32_t)((c.wave * S::VCH + i) * 64 + lane) / (uint32_t)(S::DVT / 8));
       const int shift = (min(r, last) - r) * c.v_st_b;
       g2lds16(vb + (uint32_t)((int)c.voff[i] + shift), vst + c.vdst + i * 1024);
     }
@@ -124,12 +149,13 @@ __device__ __forceinline__ const DenseParams& kargs() {
   return *(const DenseParams*)kp;
 }
 
-template <int NQ, int NMT, bool MASK, class QDone>
-__device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item& it, int j,
+template <int NQ, int NMT, bool MASK, class S, class QDone>
+__device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const Item& it, int j,
                                               const char* ks, const char* vs,
-                                              bf16x8 (&qf)[NQ][DQK / 16], float (&m_run)[NQ],
-                                              float (&l_run)[NQ], f32x16 (&o)[NQ][DV / 32],
+                                              bf16x8 (&qf)[NQ][S::DQK / 16], float (&m_run)[NQ],
+                                              float (&l_run)[NQ], f32x16 (&o)[NQ][S::DVT / 32],
                                               float scale_log2, bool causal, QDone&& q_done) {
+  constexpr int DQK = S::DQK, DV = S::DVT, KA_N = S::KA_N, KA_GROUP = S::KA_GROUP;
   // ---- S^T = K_blk * Q^T: the 32-key tiles are independent accumulator chains, issued
   // alternately, with the K fragments read from LDS PF steps ahead of their MFMA.
   f32x16 s[NQ][2];
@@ -142,13 +168,13 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item&
 #pragma unroll
     for (int st = 0; st < PF; ++st) {
       const int kk = st / NMT, mt = st % NMT;
-      a[st] = lds_read_b128(ks + c.ka[kk & 3] + (kk >> 2) * 128 + mt * 32 * (DQK * 2));
+      a[st] = lds_read_b128(ks + c.ka[kk % KA_N] + (kk / KA_N) * KA_GROUP + mt * 32 * (DQK * 2));
     }
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st) {
       if (st + PF < NSTEP) {
         const int kk2 = (st + PF) / NMT, mt2 = (st + PF) % NMT;
-        a[st + PF] = lds_read_b128(ks + c.ka[kk2 & 3] + (kk2 >> 2) * 128 + mt2 * 32 * (DQK * 2));
+        a[st + PF] = lds_read_b128(ks + c.ka[kk2 % KA_N] + (kk2 / KA_N) * KA_GROUP + mt2 * 32 * (DQK * 2));
       }
       const int kk = st / NMT, mt = st % NMT;
 #pragma unroll
@@ -261,13 +287,13 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ>& c, const Item&
 // compute block j of item it from the current stage. The stage pointers are restrict-qualified:
 // the two stages never overlap, and saying so lets the compiler order the operand reads of the
 // current stage freely against the copy in flight into the other one.
-template <int NQ, int NMT, bool MASK, class QDone>
-__device__ __forceinline__ void block_step(const DenseCtx<NQ>& c, const Item& it, int j, const Item& ld,
+template <int NQ, int NMT, bool MASK, class S, class QDone>
+__device__ __forceinline__ void block_step(const DenseCtx<NQ, S>& c, const Item& it, int j, const Item& ld,
                                            int ld_j, bool do_load, char* __restrict__ kn,
                                            char* __restrict__ vn, const char* __restrict__ kc,
-                                           const char* __restrict__ vc, bf16x8 (&qf)[NQ][DQK / 16],
+                                           const char* __restrict__ vc, bf16x8 (&qf)[NQ][S::DQK / 16],
                                            float (&m_run)[NQ], float (&l_run)[NQ],
-                                           f32x16 (&o)[NQ][DV / 32], float scale_log2, bool causal,
+                                           f32x16 (&o)[NQ][S::DVT / 32], float scale_log2, bool causal,
                                            QDone&& q_done) {
   if (do_load) issue_block_load(c, ld, ld_j, kn, vn);
   compute_block<NQ, NMT, MASK>(c, it, j, kc, vc, qf, m_run, l_run, o, scale_log2, causal, q_done);
@@ -282,15 +308,17 @@ __device__ __forceinline__ T ld_const(const T* ptr, int64_t i) {
 }
 
 // Decodes position i of the work list of XCD `xcd` (the positions are handed out by that XCD's
-// ticket counter). Work items are (plan item, unit) pairs with units u = h * num_splits + split.
+// ticket counter). Work items are (plan item, unit) pairs with units
+// u = (h * num_splits + split) * DVH + dvh (the column tiles of a head and split are neighbours).
 // When the units divide evenly over the XCDs, XCD k owns the contiguous units
 // [k * units/8, (k+1) * units/8) (neighbouring heads, whose rows sit side by side in memory) and
 // lists them in groups of group_units, group-major, then plan item (longest first), then unit
 // within the group. Otherwise the lists interleave one global order of the same form: XCD k holds
 // its positions t = 8*i + k. Returns false past the end of the list.
-__device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& item, int& h, int& split) {
+template <class S>
+__device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& item, int& h, int& split, int& dvh) {
   const DenseParams& p = kargs();
-  const int units = p.num_heads * p.num_splits;
+  const int units = p.num_heads * p.num_splits * S::DVH;
   const int gu = p.group_units;
   int u;
   if (p.xcd_units > 0) {
@@ -312,13 +340,15 @@ __device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& ite
     item = r / gu;
     u = grp * gu + (r - item * gu);
   }
-  h = u / p.num_splits;
-  split = u - h * p.num_splits;
+  const int hs = S::DVH == 1 ? u : u / S::DVH;
+  dvh = u - hs * S::DVH;
+  h = hs / p.num_splits;
+  split = hs - h * p.num_splits;
   return true;
 }
 
-template <int NQ>
-__device__ __forceinline__ Item make_item(int item, int h, int split) {
+template <int NQ, class S>
+__device__ __forceinline__ Item make_item(int item, int h, int split, int dvh) {
   const DenseParams& p = kargs();
   Item it;
   // two independent loads: the plan entry and the sequence's row ranges the planner stored beside it
@@ -338,15 +368,16 @@ __device__ __forceinline__ Item make_item(int item, int h, int split) {
   it.bhi = blk0 + (int)(((int64_t)(split + 1) * nb) / p.num_splits);
   it.h = h;
   it.split = split;
+  it.dvh = dvh;
   it.kbase = reinterpret_cast<const char*>(p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh);
-  it.vbase = reinterpret_cast<const char*>(p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh);
+  it.vbase = reinterpret_cast<const char*>(p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh + dvh * S::DVT);
   return it;
 }
 
 // Q^T fragments of this wave's query columns. Rows past the tile re-read its last row: their
 // scores stay finite and their outputs are never stored, so no zeroing (and no wait) is needed.
-template <int NQ>
-__device__ __forceinline__ void q_rows(const DenseCtx<NQ>& c, const Item& it, const __bf16* (&qp)[NQ]) {
+template <int NQ, class S>
+__device__ __forceinline__ void q_rows(const DenseCtx<NQ, S>& c, const Item& it, const __bf16* (&qp)[NQ]) {
   const DenseParams& p = kargs();
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
@@ -356,37 +387,48 @@ __device__ __forceinline__ void q_rows(const DenseCtx<NQ>& c, const Item& it, co
   }
 }
 
-template <int NQ>
-__device__ __forceinline__ void load_q(const DenseCtx<NQ>& c, const Item& it, bf16x8 (&qf)[NQ][DQK / 16]) {
+template <int NQ, class S>
+__device__ __forceinline__ void load_q(const DenseCtx<NQ, S>& c, const Item& it, bf16x8 (&qf)[NQ][S::DQK / 16]) {
   const __bf16* qp[NQ];
   q_rows(c, it, qp);
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq)
 #pragma unroll
-    for (int kk = 0; kk < DQK / 16; ++kk) qf[nq][kk] = *reinterpret_cast<const bf16x8*>(qp[nq] + kk * 16);
+    for (int kk = 0; kk < S::DQK / 16; ++kk) qf[nq][kk] = *reinterpret_cast<const bf16x8*>(qp[nq] + kk * 16);
 }
 
-// Pulls an item's Q tile into L2 ahead of its loads: the tile's rows are 384-byte runs (3
-// cache lines of 128 bytes); each thread touches 2 of its 3*BM lines. The two values must be
-// passed to touch_done() once they may have arrived (it makes no wait of its own after a
-// wait_vmem()).
-template <int NQ>
+// Pulls an item's Q tile into L2 ahead of its loads: the tile's rows are runs of DQK*2/128 cache
+// lines of 128 bytes; each thread touches 2 of the tile's lines (lines past the tile repeat). The
+// two values must be passed to touch_done() once they may have arrived (it makes no wait of its
+// own after a wait_vmem()).
+template <int NQ, class S>
 __device__ __forceinline__ void touch_q(const Item& it, int (&t)[2]) {
   const DenseParams& p = kargs();
+  constexpr int LPR = S::DQK * 2 / 128;  // cache lines per row
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
-    const int line = (int)opaque(threadIdx.x) + i * 256;  // 0 .. 3*128*NQ-1 (NQ = 1), beyond: repeat
-    const int r = min((line / 3) % (128 * NQ), it.rows - 1);
-    const __bf16* qp = p.q + (int64_t)(it.cq0 + it.row0 + r) * p.q_st + (int64_t)it.h * p.q_sh + (line % 3) * 64;
+    const int line = (int)opaque(threadIdx.x) + i * 256;
+    const int r = min((line / LPR) % (128 * NQ), it.rows - 1);
+    const __bf16* qp = p.q + (int64_t)(it.cq0 + it.row0 + r) * p.q_st + (int64_t)it.h * p.q_sh + (line % LPR) * 64;
     t[i] = *reinterpret_cast<const int*>(qp);
   }
 }
 __device__ __forceinline__ void touch_done(const int (&t)[2]) { asm volatile("" ::"v"(t[0]), "v"(t[1])); }
 
-template <int NQ>
-__device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it, const float (&m_run)[NQ],
-                                           const float (&l_run)[NQ], const f32x16 (&o)[NQ][DV / 32],
+// fp32 -> four OCP fp8 e4m3 bytes (round to nearest even), saturated at +-448 first so that no
+// value overflows to NaN; byte i of the result encodes x[i].
+__device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, float x3) {
+  auto sat = [](float x) { return fminf(fmaxf(x, -448.f), 448.f); };
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat(x0), sat(x1), 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat(x2), sat(x3), lo, true);
+}
+
+template <int NQ, class S>
+__device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item& it, const float (&m_run)[NQ],
+                                           const float (&l_run)[NQ], const f32x16 (&o)[NQ][S::DVT / 32],
                                            char* stage) {
+  constexpr int DV = S::DVT;  // the columns this item computes: [dvh * DVT, (dvh + 1) * DVT)
+  constexpr int ESZ = S::FP8 ? 1 : 2;  // output element bytes
   // The arguments are read once, before any store (a store could otherwise be taken to change them).
   const DenseParams& p = kargs();
   const int h = it.h;
@@ -396,11 +438,16 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it
   const bool accumulate = p.accumulate != 0;
   const int64_t part_row = (int64_t)it.split * p.total_q;  // split-mode row base
   const int num_heads = p.num_heads;
-  __bf16* const out_h = p.out + (int64_t)h * p.o_sh;
-  const int64_t o_st = p.o_st;
+  char* const out_h = static_cast<char*>(p.out) + ((int64_t)h * p.o_sh + it.dvh * DV) * ESZ;
+  // every column tile of a row computes the same LSE; the first one stores it (the running
+  // merge of accumulate mode is used with a single tile only)
+  const bool store_lse = it.dvh == 0;
+  const int64_t o_st_b = p.o_st * ESZ;
   float* const lse = p.lse;
   const int64_t l_st = p.l_st, l_sh = p.l_sh;
   const float sink_v = (p.sink != nullptr && o_part == nullptr) ? ld_const(p.sink, h) : -INFINITY;
+  // fp8 output: O / out_scale (multiplied by the reciprocal)
+  const float q_mul = (S::FP8 && o_part == nullptr) ? 1.f / ld_const(p.out_scale, 0) : 1.f;
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
     const float l_tot = xhalf_sum(l_run[nq]);
@@ -425,7 +472,7 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it
     if (r < it.rows) {
       const int tok = it.cq0 + it.row0 + r;
       if (o_part != nullptr) {
-        float* op = o_part + ((part_row + tok) * num_heads + h) * DV;
+        float* op = o_part + ((part_row + tok) * num_heads + h) * S::DV + it.dvh * DV;
         float* lp = lse_part + (part_row + tok) * num_heads + h;
         float w_new = inv, w_old = 0.f;
         f32x4 old[DV / 32][4];
@@ -458,31 +505,42 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it
             if (accumulate) v += old[dt][g4] * w_old;
             *reinterpret_cast<f32x4*>(op + dv) = v;
           }
-        if (c.hl == 0) *lp = lse_v;
-      } else if (lse != nullptr && c.hl == 0) {
+        if (c.hl == 0 && store_lse) *lp = lse_v;
+      } else if (lse != nullptr && c.hl == 0 && store_lse) {
         lse[(int64_t)tok * l_st + (int64_t)h * l_sh] = lse_v;
       }
     }
     if (o_part == nullptr) {
-      // bf16 output through LDS: the lane layout holds 8-byte pieces of a row, so the tile is
-      // turned around in this wave's own copy region of a free stage (rows of 64 dv, 16-byte
-      // chunks XOR-swizzled by row) and written as whole 128-byte row segments.
+      // Output through LDS: the lane layout holds pieces of 4 consecutive columns of a row, so the
+      // tile is turned around in this wave's own copy region of a free stage, one 128-byte row
+      // segment at a time (64 bf16 or 128 fp8 columns; 16-byte chunks XOR-swizzled by row), and
+      // written as whole 128-byte row segments.
       char* buf = stage + c.kdst;
       const int r0 = c.wave * 32 * NQ + nq * 32;  // first tile row of this 32-row slab
       // lane-derived addresses are computed here, not hoisted into long-lived registers
       const int lane = (int)opaque((uint32_t)c.lane), l32 = lane & 31, hl = lane >> 5;
       const int cc = lane & 7;
+      constexpr int SEG_DT = 128 / (32 * ESZ);  // 32-column MFMA tiles per 128-byte segment
+      const float w = inv * q_mul;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
+      for (int seg = 0; seg < DV / (32 * SEG_DT); ++seg) {
 #pragma unroll
-        for (int dd = 0; dd < 2; ++dd) {
-          const int dt = half * 2 + dd;
+        for (int dd = 0; dd < SEG_DT; ++dd) {
+          const int dt = seg * SEG_DT + dd;
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const int chunk = dd * 4 + g4;  // 16-byte chunk of the 64-dv row segment
-            u32x2 v = {pack_bf16x2(o[nq][dt][g4 * 4 + 0] * inv, o[nq][dt][g4 * 4 + 1] * inv),
-                       pack_bf16x2(o[nq][dt][g4 * 4 + 2] * inv, o[nq][dt][g4 * 4 + 3] * inv)};
-            *reinterpret_cast<u32x2*>(buf + l32 * 128 + ((chunk ^ (l32 & 7)) * 16) + hl * 8) = v;
+            // columns dd*32 + 8*g4 + 4*hl .. +3 of the segment
+            if (S::FP8) {
+              const uint32_t v = pack_fp8x4(o[nq][dt][g4 * 4 + 0] * w, o[nq][dt][g4 * 4 + 1] * w,
+                                            o[nq][dt][g4 * 4 + 2] * w, o[nq][dt][g4 * 4 + 3] * w);
+              const int chunk = dd * 2 + (g4 >> 1);
+              *reinterpret_cast<uint32_t*>(buf + l32 * 128 + ((chunk ^ (l32 & 7)) * 16) + (g4 & 1) * 8 + hl * 4) = v;
+            } else {
+              const int chunk = dd * 4 + g4;
+              u32x2 v = {pack_bf16x2(o[nq][dt][g4 * 4 + 0] * w, o[nq][dt][g4 * 4 + 1] * w),
+                         pack_bf16x2(o[nq][dt][g4 * 4 + 2] * w, o[nq][dt][g4 * 4 + 3] * w)};
+              *reinterpret_cast<u32x2*>(buf + l32 * 128 + ((chunk ^ (l32 & 7)) * 16) + hl * 8) = v;
+            }
           }
         }
         u32x4 v[4];
@@ -495,7 +553,7 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it
         for (int i = 0; i < 4; ++i) {
           const int rr = i * 8 + (lane >> 3);
           if (r0 + rr < it.rows)
-            *reinterpret_cast<u32x4*>(out_h + (int64_t)(it.cq0 + it.row0 + r0 + rr) * o_st + half * 64 + cc * 8) = v[i];
+            *reinterpret_cast<u32x4*>(out_h + (int64_t)(it.cq0 + it.row0 + r0 + rr) * o_st_b + seg * 128 + cc * 16) = v[i];
         }
       }
     }
@@ -504,12 +562,19 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ>& c, const Item& it
 
 }  // namespace
 
-template <int NQ>
-__global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(DenseParams p) {
-  __shared__ __attribute__((aligned(1024))) char lds_k0[K_STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_v0[V_STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_k1[K_STAGE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char lds_v1[V_STAGE_BYTES];
+// Two work-groups per CU when their registers and LDS fit, else one.
+template <int NQ, class S>
+constexpr int dense_occupancy() {
+  return (NQ == 1 && 2 * (S::K_STAGE_BYTES + S::V_STAGE_BYTES) <= 80 * 1024) ? 2 : 1;
+}
+
+template <int NQ, class S>
+__global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_kernel(DenseParams p) {
+  constexpr int DQK = S::DQK, DV = S::DVT, KCH = S::KCH, VCH = S::VCH;
+  __shared__ __attribute__((aligned(1024))) char lds_k0[S::K_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_v0[S::V_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_k1[S::K_STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char lds_v1[S::V_STAGE_BYTES];
 
   // Work-groups are dispatched to the XCDs round-robin (work-group x runs on XCD x % 8). The
   // work-groups of one XCD take the positions of its list from a ticket counter, each ticket
@@ -520,20 +585,24 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
   int* const counter = p.counters + xcd * 32;  // one 128-byte line per counter
   const int n_items = min(ld_const(p.num_items, 0), p.n_slots);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Thread 0 hands a ticket to every wave through a K stage that is free at that moment: one
-  // copy in each wave's own copy region, which only that wave's next block copy overwrites (after
-  // the wave has read it). The copy sits past the first kEpilogueBytes of the region, which the
+  auto stage_k = [&](int s) { return s ? lds_k1 : lds_k0; };
+  auto stage_v = [&](int s) { return s ? lds_v1 : lds_v0; };
+  // Thread 0 hands a ticket to every wave through a stage that is free at that moment: one copy
+  // in each wave's own copy region, which only that wave's next block copy overwrites (after the
+  // wave has read it). In the K region the copy sits past the first kEpilogueBytes, which the
   // epilogue of the previous item may still be using in that stage (a wave can still be turning
-  // its output around there while thread 0 shares the ticket of the next item).
-  auto share_ticket = [&](char* kfree, int tk) -> int {
+  // its output around there while thread 0 shares the ticket of the next item); the V region is
+  // never used by the epilogue.
+  auto ticket_slot = [&](int s, int w) -> char* {
+    return S::TICKET_IN_K ? stage_k(s) + w * KCH * 1024 + kEpilogueBytes : stage_v(s) + w * VCH * 1024;
+  };
+  auto share_ticket = [&](int sfree, int tk) -> int {
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        *reinterpret_cast<int*>(kfree + w * K_CHUNKS_PER_WAVE * 1024 + kEpilogueBytes) = tk;
+      for (int w = 0; w < 4; ++w) *reinterpret_cast<int*>(ticket_slot(sfree, w)) = tk;
     }
     __syncthreads();
-    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int*>(
-        kfree + wave * K_CHUNKS_PER_WAVE * 1024 + kEpilogueBytes));
+    return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int*>(ticket_slot(sfree, wave)));
   };
   int fetched = 0;
   auto fetch = [&] {
@@ -543,35 +612,35 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
     if (threadIdx.x == 0) fetched = atomicAdd(counter + (int)opaque(0u), 1);
   };
   fetch();
-  int wi, wh, wsplit;
-  if (!decode_pos(n_items, xcd, share_ticket(lds_k1, fetched), wi, wh, wsplit)) return;
+  int wi, wh, wsplit, wdvh;
+  if (!decode_pos<S>(n_items, xcd, share_ticket(1, fetched), wi, wh, wsplit, wdvh)) return;
 
-  DenseCtx<NQ> c;
+  DenseCtx<NQ, S> c;
   c.lane = threadIdx.x & 63;
   c.wave = wave;
   c.l32 = c.lane & 31;
   c.hl = c.lane >> 5;
   c.k_st_b = (int)(p.k_st * 2);
   c.v_st_b = (int)(p.v_st * 2);
-  c.kdst = c.wave * K_CHUNKS_PER_WAVE * 1024;
-  c.vdst = c.wave * V_CHUNKS_PER_WAVE * 1024;
+  c.kdst = c.wave * KCH * 1024;
+  c.vdst = c.wave * VCH * 1024;
 #pragma unroll
-  for (int i = 0; i < K_CHUNKS_PER_WAVE; ++i) {
-    const int pch = (c.wave * K_CHUNKS_PER_WAVE + i) * 64 + c.lane;
-    const int row = pch / 24, pc = pch % 24;
-    c.koff[i] = (uint32_t)(row * c.k_st_b + ((pc ^ row_swz(row)) * 16));
+  for (int i = 0; i < KCH; ++i) {
+    const int pch = (c.wave * KCH + i) * 64 + c.lane;
+    const int row = (int)((uint32_t)pch / (DQK / 8)), pc = (int)((uint32_t)pch % (DQK / 8));
+    c.koff[i] = (uint32_t)(row * c.k_st_b + ((pc ^ kswz<S>(row)) * 16));
   }
 #pragma unroll
-  for (int i = 0; i < V_CHUNKS_PER_WAVE; ++i) {
-    const int pch = (c.wave * V_CHUNKS_PER_WAVE + i) * 64 + c.lane;
-    const int row = pch >> 4, pc = pch & 15;
+  for (int i = 0; i < VCH; ++i) {
+    const int pch = (c.wave * VCH + i) * 64 + c.lane;
+    const int row = (int)((uint32_t)pch / (DV / 8)), pc = (int)((uint32_t)pch % (DV / 8));
     c.voff[i] = (uint32_t)(row * c.v_st_b + ((pc ^ ((row & 3) << 2)) * 16));
   }
-  // K operand rows: lane reads row (mt*32 + l32), chunk (kk*2 + hl) stored at chunk ^ row_swz(row)
-  // (row_swz(mt*32 + l32) == row_swz(l32)); for kk = 4g + u this is byte
-  // row*384 + g*128 + (((2u + hl) ^ row_swz(l32)) * 16).
+  // K operand rows: lane reads row (mt*32 + l32), chunk (kk*2 + hl) stored at chunk ^ kswz(row)
+  // (kswz(mt*32 + l32) == kswz(l32); the swizzle stays inside a KA_GROUP-byte group); for
+  // kk = KA_N*g + u this is byte row*DQK*2 + g*KA_GROUP + (((2u + hl) ^ kswz(l32)) * 16).
 #pragma unroll
-  for (int u = 0; u < 4; ++u) c.ka[u] = c.l32 * (DQK * 2) + (((2 * u + c.hl) ^ row_swz(c.l32)) * 16);
+  for (int u = 0; u < S::KA_N; ++u) c.ka[u] = c.l32 * (DQK * 2) + (((2 * u + c.hl) ^ kswz<S>(c.l32)) * 16);
   // V^T operand: 16-lane group gg reads rows k0..k0+3 (k0 = 4*hl + (r >> 2) + step offset) at
   // columns dt*32 + (gg & 1)*16 + 4*(r & 3); row k0 & 3 == (r >> 2) & 3 fixes the swizzle per lane.
   {
@@ -589,10 +658,8 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
   float m_run[NQ], l_run[NQ];
   f32x16 o[NQ][DV / 32];
   int st = 0;  // stage holding the next block to compute
-  auto stage_k = [&](int s) { return s ? lds_k1 : lds_k0; };
-  auto stage_v = [&](int s) { return s ? lds_v1 : lds_v0; };
 
-  Item cur = make_item<NQ>(wi, wh, wsplit);
+  Item cur = make_item<NQ, S>(wi, wh, wsplit, wdvh);
   load_q(c, cur, qf);
   if (cur.blo < cur.bhi) issue_block_load(c, cur, cur.blo, stage_k(st), stage_v(st));
   wait_vmem();
@@ -637,11 +704,11 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
       auto prepare = [&](int jj) {  // at the start of block jj, before its copy
         if (jj == fetch_j) fetch();
         if (jj == share_j) {
-          has_next = decode_pos(n_items, xcd, share_ticket(stage_k(st ^ 1), fetched), wi, wh, wsplit);
+          has_next = decode_pos<S>(n_items, xcd, share_ticket(st ^ 1, fetched), wi, wh, wsplit, wdvh);
           if (has_next) {
-            nxt = make_item<NQ>(wi, wh, wsplit);
+            nxt = make_item<NQ, S>(wi, wh, wsplit, wdvh);
             // (in the last block itself the fragment loads follow at once: no use touching)
-            if (jj + 1 < cur.bhi) touch_q<NQ>(nxt, touched);
+            if (jj + 1 < cur.bhi) touch_q<NQ, S>(nxt, touched);
           }
         }
       };
@@ -706,13 +773,13 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
       }
     } else {
       fetch();
-      has_next = decode_pos(n_items, xcd, share_ticket(stage_k(st ^ 1), fetched), wi, wh, wsplit);
+      has_next = decode_pos<S>(n_items, xcd, share_ticket(st ^ 1, fetched), wi, wh, wsplit, wdvh);
     }
     // Free stage for the epilogue: the one the last block read (the next item's first block sits
     // in the other), or, for an item without blocks, the one the next item will be copied into.
     store_item(c, cur, m_run, l_run, o, had_blocks ? stage_k(st ^ 1) : stage_k(st));
     if (!has_next) break;
-    cur = had_blocks ? nxt : make_item<NQ>(wi, wh, wsplit);
+    cur = had_blocks ? nxt : make_item<NQ, S>(wi, wh, wsplit, wdvh);
     if (!had_blocks) {  // nothing was handed over: start the next item from scratch
       load_q(c, cur, qf);
       if (cur.blo < cur.bhi) issue_block_load(c, cur, cur.blo, stage_k(st), stage_v(st));
@@ -722,16 +789,48 @@ __global__ __launch_bounds__(256, (NQ == 1 ? 2 : 1)) void dense_fwd_kernel(Dense
   }
 }
 
-template __global__ void dense_fwd_kernel<1>(DenseParams);
-template __global__ void dense_fwd_kernel<2>(DenseParams);
+using Shape192 = Shape<192, 128, false>;
+using Shape192F8 = Shape<192, 128, true>;
+using Shape128 = Shape<128, 128, false>;
+using Shape128F8 = Shape<128, 128, true>;
+using Shape256 = Shape<256, 256, false>;
+using Shape256F8 = Shape<256, 256, true>;
 
-hipError_t launch_dense_fwd(const DenseParams& p, int nq, hipStream_t stream) {
+template __global__ void dense_fwd_kernel<1, Shape192>(DenseParams);
+template __global__ void dense_fwd_kernel<2, Shape192>(DenseParams);
+template __global__ void dense_fwd_kernel<1, Shape192F8>(DenseParams);
+template __global__ void dense_fwd_kernel<1, Shape128>(DenseParams);
+template __global__ void dense_fwd_kernel<1, Shape128F8>(DenseParams);
+template __global__ void dense_fwd_kernel<1, Shape256>(DenseParams);
+template __global__ void dense_fwd_kernel<1, Shape256F8>(DenseParams);
+
+template <int NQ, class S>
+static void launch_one(const DenseParams& p, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL((dense_fwd_kernel<NQ, S>), dim3(grid), dim3(256), 0, stream, p);
+}
+
+int dense_occupancy_of(int nq, int dqk, int dv) {
+  if (nq == 2) return dense_occupancy<2, Shape192>();
+  if (dqk == 256 && dv == 256) return dense_occupancy<1, Shape256>();
+  if (dqk == 128 && dv == 128) return dense_occupancy<1, Shape128>();
+  return dense_occupancy<1, Shape192>();
+}
+
+hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool fp8_out, hipStream_t stream) {
   const int grid = 8 * p.wgs_per_xcd;
   if (grid <= 0) return hipSuccess;
-  if (nq == 2) {
-    hipLaunchKernelGGL(dense_fwd_kernel<2>, dim3(grid), dim3(256), 0, stream, p);
+  if (dqk == 192 && dv == 128) {
+    if (fp8_out) launch_one<1, Shape192F8>(p, grid, stream);
+    else if (nq == 2) launch_one<2, Shape192>(p, grid, stream);
+    else launch_one<1, Shape192>(p, grid, stream);
+  } else if (dqk == 128 && dv == 128) {
+    if (fp8_out) launch_one<1, Shape128F8>(p, grid, stream);
+    else launch_one<1, Shape128>(p, grid, stream);
+  } else if (dqk == 256 && dv == 256) {
+    if (fp8_out) launch_one<1, Shape256F8>(p, grid, stream);
+    else launch_one<1, Shape256>(p, grid, stream);
   } else {
-    hipLaunchKernelGGL(dense_fwd_kernel<1>, dim3(grid), dim3(256), 0, stream, p);
+    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

@@ -42,9 +42,10 @@ struct DenseParams {
   float scale;           // softmax scale
   float scale_log2;      // softmax scale * log2(e)
   const float* sink;     // nullable [H]; applied here only when unsplit
-  __bf16* out; int64_t o_st, o_sh;
+  void* out; int64_t o_st, o_sh;  // bf16, or fp8 e4m3 for the fp8-output instances (element strides)
+  const float* out_scale;         // fp8 output: device [1], stored value = O / out_scale
   float* lse; int64_t l_st, l_sh;
-  float* o_part;         // split mode: [S][total_q][H][128] fp32, else null
+  float* o_part;         // split mode: [S][total_q][H][DV] fp32, else null
   float* lse_part;       // split mode: [S][total_q][H]
   int32_t accumulate;    // with one split: merge into o_part / lse_part (running result) in place
   int32_t total_q;
@@ -84,7 +85,8 @@ struct CombineParams {
   int32_t num_heads;
   int32_t dv;
   const float* sink;
-  __bf16* out; int64_t o_st, o_sh;
+  void* out; int64_t o_st, o_sh;   // bf16, or fp8 e4m3 when out_scale is set (element strides)
+  const float* out_scale;          // nullable device [1]: fp8 output of O / out_scale
   float* lse; int64_t l_st, l_sh;
 };
 
@@ -104,7 +106,11 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int32_t w, int32_t* cu_chunk,
                            hipStream_t stream);
 hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream);
-hipError_t launch_dense_fwd(const DenseParams& p, int nq, hipStream_t stream);
+// Dense kernel instances: (dqk, dv) in {(192, 128), (128, 128), (256, 256)}, bf16 or fp8 output;
+// nq = 2 (256-row query tiles) only for (192, 128) with bf16 output.
+hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool fp8_out, hipStream_t stream);
+// Resident work-groups per CU of the instance.
+int dense_occupancy_of(int nq, int dqk, int dv);
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 

@@ -67,6 +67,16 @@ Readings taken where the pages are silent (each also listed with the design note
   R20 The up-projected context K/V are materialised in bf16 (round-to-nearest-even of the fp32
      products), the type the attention takes its K/V in; the parity tests compare with the
      oracle evaluated on the same rounded K/V, so that the attention is what is measured.
+  R21 FP8 output (page "FlashAttention backend for MLA prefill": ``supports_quant_output`` with
+     a static, symmetric per-tensor FP8 key, kFp8StaticTensorSym). The stored value is the OCP
+     FP8 E4M3 encoding (the finite-only variant: bias 7, no infinities, S.1111.111 = NaN, largest
+     magnitude 448) of O / scale, rounded to the nearest representable value with ties to the
+     even code, after clamping to [-448, 448] (saturation, as static FP8 quantisation does; the
+     pages do not say). The LSE is not quantised.
+  R22 Other MLA head layouts (same page, ``supports_mla_dimensions``: (nope, rope, v) =
+     (128, 64, 128), (64, 64, 128), (192, 64, 256), (256, 0, 256)). The attention sees q/k heads
+     of nope + rope columns, so the layouts are (Dqk, Dv) = (192, 128), (128, 128), (256, 256);
+     the definition above is the same for every width.
 """
 from __future__ import annotations
 
@@ -331,6 +341,44 @@ def combine_partials(o_parts: np.ndarray, lse_parts: np.ndarray,
     w = np.where(empty[None, :], 0.0, np.exp(lse_parts - np.where(empty, 0.0, lse)[None, :]))
     out = (w[:, :, None] * o_parts).sum(axis=0)
     return out, lse
+
+
+FP8_E4M3_MAX = 448.0
+
+
+def fp8_e4m3_decode(codes) -> np.ndarray:
+    """Values of OCP FP8 E4M3 codes (reading R21): bit 7 sign, bits 6..3 exponent e (bias 7),
+    bits 2..0 mantissa m; e = 0 gives m * 2^-9, otherwise (1 + m/8) * 2^(e-7); e = 15 with m = 7
+    is NaN. Returns float64."""
+    c = np.asarray(codes).astype(np.int64) & 0xFF
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, m * 2.0 ** -9, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where(c & 0x80, -mag, mag)
+
+
+def fp8_e4m3_encode(x) -> np.ndarray:
+    """Saturating round-to-nearest-even into OCP FP8 E4M3 (reading R21): |x| is clamped to 448,
+    then the nearest of the 127 non-negative finite values is taken, a tie going to the even
+    code (the one whose mantissa ends in 0); the sign bit is x's (so -0.0 and negatives that
+    round to zero give 0x80). NaN inputs are not allowed. Returns uint8 codes."""
+    x = np.asarray(x, dtype=np.float64)
+    if np.isnan(x).any():
+        raise ValueError("NaN has no saturating encoding here")
+    grid = fp8_e4m3_decode(np.arange(0x7F))          # increasing with the code
+    a = np.minimum(np.abs(x), FP8_E4M3_MAX)
+    hi = np.minimum(np.searchsorted(grid, a, side="left"), 0x7E)   # first value >= a
+    lo = np.maximum(hi - 1, 0)
+    d_lo, d_hi = a - grid[lo], grid[hi] - a
+    code = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(hi % 2 == 0, hi, lo)))
+    code = np.where(a == grid[hi], hi, code)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_output_fp8(out: np.ndarray, scale: float) -> np.ndarray:
+    """FP8 output of an attention result under a static per-tensor scale (reading R21)."""
+    return fp8_e4m3_encode(np.asarray(out, dtype=np.float64) / float(scale))
 
 
 def _as_f64(x: np.ndarray) -> np.ndarray:

@@ -72,7 +72,7 @@ def test_varlen_window_argument_errors():
     lib = mla.load_library()
     assert _varlen_window(lib, -2, 0) == 1
     assert _varlen_window(lib, 5, -3) == 1
-    assert _varlen_window(lib, 256, 0, dqk=128) == 2
+    assert _varlen_window(lib, 256, 0, dqk=256) == 2
     assert _varlen_window(lib, 256, 0, q=P + 2) == 3
     assert _varlen_window(lib, 256, 0, batch=0) == 0
 
@@ -86,7 +86,8 @@ def test_varlen_argument_errors():
     assert _varlen(lib, splits=65) == 1
     assert _varlen(lib, scale=float("nan")) == 1
     assert _varlen(lib, qsh=100) == 1                      # head stride smaller than the row
-    assert _varlen(lib, dqk=128) == 2                      # only 192/128 is built
+    assert _varlen(lib, dqk=256) == 2                      # (256, 128) is not an MLA layout
+    assert _varlen(lib, dv=256) == 2                       # nor (192, 256)
     assert _varlen(lib, dv=192) == 2
     assert _varlen(lib, max_k=(1 << 24) + 1) == 2
     assert _varlen(lib, q=P + 8) == 3                      # misaligned base
@@ -97,6 +98,38 @@ def test_varlen_argument_errors():
     # vLLM-style strided V view (token stride H*256, head stride 256) passes validation up to the
     # workspace check
     assert _varlen(lib, vst=128 * 256, vsh=256, ws_bytes=64) == 4
+    # the other layouts pass validation up to the workspace check
+    assert _varlen(lib, dqk=128, qst=128 * 128, qsh=128, kst=128 * 128, ksh=128, ws_bytes=64) == 4
+    assert _varlen(lib, dqk=256, dv=256, qst=128 * 256, qsh=256, kst=128 * 256, ksh=256,
+                   vst=128 * 256, vsh=256, ost=128 * 256, osh=256, ws_bytes=64) == 4
+    assert _varlen(lib, dqk=256, dv=256, qst=128 * 256, qsh=256, kst=128 * 256, ksh=256,
+                   vst=128 * 256, vsh=256, ost=128 * 128, osh=128) == 1   # output rows overlap
+
+
+def _varlen_fp8(lib, scale_ptr=P, **kw):
+    a = dict(q=P, qst=128 * 192, qsh=192, k=P, kst=128 * 192, ksh=192, v=P, vst=128 * 128, vsh=128,
+             cuq=P, cuk=P, batch=1, total_q=16, max_q=16, max_k=16, heads=128, dqk=192, dv=128,
+             scale=0.07, causal=1, splits=1, sink=None, out=P, ost=128 * 128, osh=128, lse=None,
+             lst=128, lsh=1, ws=P, ws_bytes=1 << 20, stream=None)
+    a.update(kw)
+    return lib.mla_prefill_varlen_fp8(
+        a["q"], a["qst"], a["qsh"], a["k"], a["kst"], a["ksh"], a["v"], a["vst"], a["vsh"], a["cuq"],
+        a["cuk"], a["batch"], a["total_q"], a["max_q"], a["max_k"], a["heads"], a["dqk"], a["dv"],
+        a["scale"], a["causal"], -1, -1, a["splits"], a["sink"], scale_ptr, a["out"], a["ost"], a["osh"],
+        a["lse"], a["lst"], a["lsh"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_varlen_fp8_argument_errors():
+    """FP8 output needs a scale, 16-element output strides and a 4-byte aligned scale; the rest
+    is validated as for bf16 output."""
+    lib = mla.load_library()
+    assert _varlen_fp8(lib, scale_ptr=None) == 1
+    assert _varlen_fp8(lib, ost=128 * 128 + 8) == 3
+    assert _varlen_fp8(lib, osh=136, ost=128 * 136) == 3
+    assert _varlen_fp8(lib, scale_ptr=P + 2) == 3
+    assert _varlen_fp8(lib, dqk=256) == 2
+    assert _varlen_fp8(lib, ws_bytes=64) == 4
+    assert _varlen_fp8(lib, batch=0) == 0
 
 
 def test_workspace_size_grows_with_splits():
@@ -105,6 +138,11 @@ def test_workspace_size_grows_with_splits():
     w4 = lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 128, 1, 4)
     assert w1 > 0 and w4 >= w1 + 4 * 300 * 8 * 128 * 4
     assert lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 128, 1, 99) == 0
+    # a 256-column v head: partials twice as wide; other widths are rejected
+    w1b = lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 256, 1, 1)
+    w4b = lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 256, 1, 4)
+    assert w1b > 0 and w4b >= w1b + 4 * 300 * 8 * 256 * 4
+    assert lib.mla_prefill_varlen_workspace_size(2, 300, 200, 200, 8, 64, 1, 1) == 0
 
 
 def _sparse(lib, **kw):

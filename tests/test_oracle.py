@@ -552,3 +552,67 @@ def test_bf16_rounding_is_round_to_nearest_even():
     # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins (1.0).
     np.testing.assert_array_equal(back[:4], np.array([1.0, 1.0, 1.0 + 2**-6, -2.5], dtype=np.float32))
     np.testing.assert_array_equal(torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16), bits)
+
+
+# ---------------------------------------------------------------- FP8 output (reading R21)
+def test_fp8_decode_closed_form_values():
+    """Code values fixed by the E4M3 format: bias 7, 3 mantissa bits, subnormals below 2^-6,
+    448 the largest finite value, S.1111.111 NaN, sign in the top bit."""
+    d = O.fp8_e4m3_decode
+    assert d(0x00) == 0.0 and d(0x01) == 2.0 ** -9 and d(0x07) == 7 * 2.0 ** -9
+    assert d(0x08) == 2.0 ** -6 and d(0x38) == 1.0 and d(0x39) == 1.125 and d(0x40) == 2.0
+    assert d(0x7E) == 448.0 and d(0xFE) == -448.0 and d(0xB8) == -1.0
+    assert np.isnan(d(0x7F)) and np.isnan(d(0xFF))
+    pos = d(np.arange(0x7F))
+    assert np.all(np.diff(pos) > 0)                              # increasing, no duplicates
+    assert np.all(d(np.arange(0x80, 0xFF)) == -pos)
+
+
+def test_fp8_encode_round_trip_and_ties():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)])
+    assert np.array_equal(O.fp8_e4m3_encode(O.fp8_e4m3_decode(codes)), codes)
+    e = O.fp8_e4m3_encode
+    assert e(1 + 2.0 ** -4) == 0x38            # halfway between 1 and 1.125: to even (1.0)
+    assert e(1 + 3 * 2.0 ** -4) == 0x3A        # halfway between 1.125 and 1.25: to even (1.25)
+    assert e(2.0 ** -10) == 0x00               # half the smallest subnormal: to even (zero)
+    assert e(3 * 2.0 ** -10) == 0x02           # halfway between codes 1 and 2: to 2
+    assert e(15 * 2.0 ** -10) == 0x08          # halfway between 7*2^-9 and 2^-6: to even (2^-6)
+    assert e(1.0625 + 1e-9) == 0x39            # just above a tie: up
+    assert e(464.0) == 0x7E and e(1e9) == 0x7E and e(-500.0) == 0xFE   # saturation at 448
+    assert e(-1e-6) == 0x80 and e(0.0) == 0x00
+
+
+def test_fp8_encode_is_nearest_by_brute_force():
+    """Every encoding is a nearest finite value to the clamped input (brute force over all
+    codes), carries the input's sign bit, and between two equally near values is the even code."""
+    rng = np.random.default_rng(21)
+    pos = O.fp8_e4m3_decode(np.arange(0x7F))
+    x = rng.standard_normal(4000) * np.exp2(rng.uniform(-12, 9, 4000))
+    x = np.concatenate([x, pos[:-1] + np.diff(pos) / 2, -(pos[:-1] + np.diff(pos) / 2)])  # with every tie
+    got = O.fp8_e4m3_encode(x)
+    grid = O.fp8_e4m3_decode(np.arange(256))
+    dist_all = np.abs(grid[None, :] - np.clip(x, -448, 448)[:, None])
+    dist_all[:, np.isnan(grid)] = np.inf
+    best = dist_all.min(axis=1)
+    assert np.array_equal(dist_all[np.arange(x.size), got], best)
+    assert np.array_equal(got >> 7, np.signbit(x).astype(np.uint8))
+    ties = (np.sort(dist_all, axis=1)[:, 1] == best) & (best > 0)
+    n_tie_values = [len({abs(grid[c]) for c in np.flatnonzero(dist_all[i] == best[i])}) for i in np.flatnonzero(ties)]
+    tied = np.flatnonzero(ties)[np.array(n_tie_values) > 1]
+    assert tied.size > 200 and np.all(got[tied] % 2 == 0)
+
+
+def test_fp8_encode_matches_torch_cast():
+    """In range, the encoding equals PyTorch's CPU float8_e4m3fn cast (a library routine the
+    oracle does not call)."""
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal(200000) * np.exp2(rng.uniform(-14, 9, 200000))).astype(np.float32)
+    x = np.clip(x, -448, 448).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(O.fp8_e4m3_encode(x), ref)
+
+
+def test_quantize_output_divides_by_the_scale():
+    out = np.array([[0.5, -0.25, 3.0, 1000.0]])
+    q = O.quantize_output_fp8(out, 2.0 ** -4)
+    assert np.array_equal(O.fp8_e4m3_decode(q), [[8.0, -4.0, 48.0, 448.0]])
