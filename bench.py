@@ -57,13 +57,13 @@ def dense_pairs(lens_q, lens_k, causal: bool, window=(-1, -1)) -> int:
     return total
 
 
-def dense_flops(lens_q, lens_k, heads, causal, window=(-1, -1)) -> float:
-    return float(2 * (DQK + DV) * heads * dense_pairs(lens_q, lens_k, causal, window))
+def dense_flops(lens_q, lens_k, heads, causal, window=(-1, -1), dqk=DQK, dv=DV) -> float:
+    return float(2 * (dqk + dv) * heads * dense_pairs(lens_q, lens_k, causal, window))
 
 
-def dense_bytes(lens_q, lens_k, heads, lse=True) -> float:
+def dense_bytes(lens_q, lens_k, heads, lse=True, dqk=DQK, dv=DV, out_bytes=2) -> float:
     tq, tk = sum(lens_q), sum(lens_k)
-    return float(tq * heads * DQK * 2 + tk * heads * (DQK + DV) * 2 + tq * heads * DV * 2
+    return float(tq * heads * dqk * 2 + tk * heads * (dqk + dv) * 2 + tq * heads * dv * out_bytes
                  + (tq * heads * 4 if lse else 0))
 
 
@@ -142,29 +142,35 @@ def warm_cold(step, reps: int):
     return res
 
 
-def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_splits=0, window=None):
+def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_splits=0, window=None,
+                      dqk=DQK, dv=DV, fp8_out=False):
+    """One dense workload timed through the C ABI; (dqk, dv) picks the head layout and fp8_out the
+    FP8 output (static scale 2^-8)."""
     import torch
     import mla_varlen_prefill_amd as mla
     from workloads import device_dense
-    q, k, v, cu_q, cu_k = device_dense(lens_q, lens_k, heads, seed)
+    q, k, v, cu_q, cu_k = device_dense(lens_q, lens_k, heads, seed, dqk=dqk, dv=dv)
     max_q, max_k = max(lens_q), max(lens_k)
-    out = torch.empty((q.shape[0], heads, DV), dtype=torch.bfloat16, device="cuda")
+    out = torch.empty((q.shape[0], heads, dv), dtype=torch.float8_e4m3fn if fp8_out else torch.bfloat16,
+                      device="cuda")
+    out_scale = torch.tensor([2.0 ** -8], dtype=torch.float32, device="cuda") if fp8_out else None
     lse = torch.empty((q.shape[0], heads), dtype=torch.float32, device="cuda")
-    ws_bytes = mla.varlen_workspace_bytes(len(lens_q), q.shape[0], max_q, max_k, heads, True, num_splits)
+    ws_bytes = mla.varlen_workspace_bytes(len(lens_q), q.shape[0], max_q, max_k, heads, True, num_splits, dv)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    scale = DQK ** -0.5
+    scale = dqk ** -0.5
 
     def step():
         mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal=True,
-                               num_splits=num_splits, out=out, lse=lse, workspace=ws, window=window)
+                               num_splits=num_splits, out=out, lse=lse, workspace=ws, window=window,
+                               out_scale=out_scale)
 
     settle(step)
     ms, kms, _ = time_steps(step, steps, warmup, "dense")
     wc = warm_cold(step, max(3, min(steps, 7)))
-    fl = dense_flops(lens_q, lens_k, heads, True, window if window is not None else (-1, -1))
-    by = dense_bytes(lens_q, lens_k, heads)
+    fl = dense_flops(lens_q, lens_k, heads, True, window if window is not None else (-1, -1), dqk, dv)
+    by = dense_bytes(lens_q, lens_k, heads, True, dqk, dv, 1 if fp8_out else 2)
     splits = mla.varlen_num_splits(len(lens_q), max_q, max_k, heads, True, num_splits)
-    del q, k, v, out, lse, ws
+    del q, k, v, out, lse, ws, out_scale
     torch.cuda.empty_cache()
     res = {"workload": name, "ms_per_call": round(ms, 4), "dense_kernel_ms": round(kms, 4),
            "splits": splits, "tflops": round(fl / ms / 1e9, 2),
@@ -174,6 +180,14 @@ def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_spli
     if CALIB:
         res["frac_measured_mfma"] = round(fl / kms / 1e9 / CALIB["mfma_loop_tflops"], 4)
     return res
+
+
+def dense_varlen_variant(name, steps, warmup, **kw):
+    """The headline varlen batch (8 sequences, lengths in [64, 2048], 128 heads, causal) with
+    another head layout or FP8 output."""
+    from workloads import varlen_lens
+    lens = varlen_lens(2, 8, 64, 2048)
+    return dense_device_case(name, lens, lens, 128, 2, steps, warmup, **kw)
 
 
 def sparse_case(steps, warmup):
@@ -338,8 +352,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
     ap.add_argument("--only", default=None,
                     help="run one workload and print its line: dense_varlen, dense_long, dense_chunked, "
-                         "dense_small, dense_window, chunked_context, sparse, sparse_paged, copy (a plain 1 GiB device copy for counter "
-                         "calibration)")
+                         "dense_small, dense_window, dense_dims128, dense_dims256, dense_fp8, chunked_context, "
+                         "sparse, sparse_paged, copy (a plain 1 GiB device copy for counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -370,8 +384,8 @@ def main():
         return
 
     if not args.no_calib and args.only in (None, "dense_varlen", "dense_long", "dense_chunked",
-                                           "dense_small", "dense_window", "chunked_context", "sparse",
-                                           "sparse_paged"):
+                                           "dense_small", "dense_window", "dense_dims128", "dense_dims256",
+                                           "dense_fp8", "chunked_context", "sparse", "sparse_paged"):
         from mla_varlen_prefill_amd import calib
         CALIB["mfma_loop_tflops"] = round(calib.mfma_tflops(), 1)
         CALIB["stream_read_gbps"] = round(calib.stream_read_gbps(), 1)
@@ -390,6 +404,12 @@ def main():
             "chunked_context": lambda: chunked_context_case(args.steps, args.warmup),
             "dense_window": lambda: dense_device_case("dense_window_1x32768_h128_w4096", [32768], [32768], 128,
                                                       3, args.steps, args.warmup, window=(4096, -1)),
+            "dense_dims128": lambda: dense_varlen_variant("dense_varlen_b8_h128_qk128_v128", args.steps,
+                                                          args.warmup, dqk=128, dv=128),
+            "dense_dims256": lambda: dense_varlen_variant("dense_varlen_b8_h128_qk256_v256", args.steps,
+                                                          args.warmup, dqk=256, dv=256),
+            "dense_fp8": lambda: dense_varlen_variant("dense_varlen_b8_h128_fp8_out", args.steps, args.warmup,
+                                                      fp8_out=True),
         }
         print(json.dumps(sec_runs[args.only]()), flush=True)
         return
@@ -460,6 +480,10 @@ def main():
                                      128, 4, ss, sw))
         sec.append(dense_device_case("dense_window_1x32768_h128_w4096", [32768], [32768], 128, 3, ss, sw,
                                      window=(4096, -1)))
+        for name, kw in (("dense_varlen_b8_h128_qk128_v128", dict(dqk=128, dv=128)),
+                         ("dense_varlen_b8_h128_qk256_v256", dict(dqk=256, dv=256)),
+                         ("dense_varlen_b8_h128_fp8_out", dict(fp8_out=True))):
+            sec.append(dense_varlen_variant(name, max(5, min(args.steps, 50)), 10, **kw))
         sec.append(chunked_context_case(ss, sw))
         sec.append(sparse_case(ss, sw))
         sec.append(sparse_paged_case(ss, sw))

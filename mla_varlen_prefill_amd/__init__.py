@@ -175,9 +175,9 @@ def mla_prefill_plan(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max
 
 
 def varlen_workspace_bytes(batch: int, total_q: int, max_seqlen_q: int, max_seqlen_k: int,
-                           num_heads: int, causal: bool, num_splits: int) -> int:
+                           num_heads: int, causal: bool, num_splits: int, head_dim_v: int = 128) -> int:
     return load_library().mla_prefill_varlen_workspace_size(
-        batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, 128, int(bool(causal)), num_splits)
+        batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, head_dim_v, int(bool(causal)), num_splits)
 
 
 def varlen_num_splits(batch: int, max_seqlen_q: int, max_seqlen_k: int, num_heads: int,
