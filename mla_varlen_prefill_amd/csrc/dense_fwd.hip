@@ -315,6 +315,15 @@ __device__ __forceinline__ T ld_const(const T* ptr, int64_t i) {
 // lists them in groups of group_units, group-major, then plan item (longest first), then unit
 // within the group. Otherwise the lists interleave one global order of the same form: XCD k holds
 // its positions t = 8*i + k. Returns false past the end of the list.
+// Positions in the work list of XCD `xcd` (see decode_pos).
+template <class S>
+__device__ __forceinline__ int list_len(int n_items, int xcd) {
+  const DenseParams& p = kargs();
+  if (p.xcd_units > 0) return n_items * p.xcd_units;
+  const int total = n_items * p.num_heads * p.num_splits * S::DVH;
+  return total > xcd ? (total - xcd + 7) / 8 : 0;
+}
+
 template <class S>
 __device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& item, int& h, int& split, int& dvh) {
   const DenseParams& p = kargs();
@@ -581,8 +590,9 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
   // shortly before the item it names starts (about two key blocks ahead, to hide the atomic's
   // latency). The items in flight on an XCD thus always form a short window of its list, as in
   // the dispatch order of a non-persistent grid, and their K/V rows are shared in that XCD's L2.
+  // When an XCD's list is used up, its work-groups go on with the other XCDs' lists in turn
+  // (the XCDs do not run at quite the same speed; this evens out their finishing times).
   const int xcd = blockIdx.x & 7;
-  int* const counter = p.counters + xcd * 32;  // one 128-byte line per counter
   const int n_items = min(ld_const(p.num_items, 0), p.n_slots);
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   auto stage_k = [&](int s) { return s ? lds_k1 : lds_k0; };
@@ -605,15 +615,43 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
     return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int*>(ticket_slot(sfree, wave)));
   };
   int fetched = 0;
+  int lst = xcd;  // the list tickets are taken from (one 128-byte counter line per list)
   auto fetch = [&] {
     // The zero offset the optimiser cannot see through keeps this a plain per-lane atomic: at a
     // provably uniform address it would be rewritten into a wave-level form that reads its result
     // at once, waiting for the round trip here instead of where the ticket is shared.
-    if (threadIdx.x == 0) fetched = atomicAdd(counter + (int)opaque(0u), 1);
+    if (threadIdx.x == 0) fetched = atomicAdd(p.counters + lst * 32 + (int)opaque(0u), 1);
+  };
+  int wi, wh, wsplit, wdvh;
+  // Shares the fetched ticket (list in bits 28..30, position below) and decodes it. Past the end
+  // of its list, thread 0 reads every list's counter (a hint: reading takes no ticket), takes a
+  // ticket from the list with the most positions left and shares that, until one decodes or no
+  // list has positions left. The barrier before a re-share lets every wave read the previous
+  // ticket first.
+  auto take = [&](int sfree) -> bool {
+    int tk = share_ticket(sfree, fetched | (lst << 28));
+    while (true) {
+      lst = tk >> 28;
+      if (decode_pos<S>(n_items, lst, tk & 0x0FFFFFFF, wi, wh, wsplit, wdvh)) return true;
+      __syncthreads();
+      if (threadIdx.x == 0) {
+        int best = -1, best_left = 0;
+        for (int l = 0; l < 8; ++l) {
+          const int taken = __hip_atomic_load(p.counters + l * 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          const int left = list_len<S>(n_items, l) - taken;
+          if (left > best_left) {
+            best_left = left;
+            best = l;
+          }
+        }
+        fetched = best < 0 ? -1 : ((best << 28) | atomicAdd(p.counters + best * 32, 1));
+      }
+      tk = share_ticket(sfree, fetched);
+      if (tk < 0) return false;
+    }
   };
   fetch();
-  int wi, wh, wsplit, wdvh;
-  if (!decode_pos<S>(n_items, xcd, share_ticket(1, fetched), wi, wh, wsplit, wdvh)) return;
+  if (!take(1)) return;
 
   DenseCtx<NQ, S> c;
   c.lane = threadIdx.x & 63;
@@ -704,7 +742,7 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
       auto prepare = [&](int jj) {  // at the start of block jj, before its copy
         if (jj == fetch_j) fetch();
         if (jj == share_j) {
-          has_next = decode_pos<S>(n_items, xcd, share_ticket(st ^ 1, fetched), wi, wh, wsplit, wdvh);
+          has_next = take(st ^ 1);
           if (has_next) {
             nxt = make_item<NQ, S>(wi, wh, wsplit, wdvh);
             // (in the last block itself the fragment loads follow at once: no use touching)
@@ -773,7 +811,7 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
       }
     } else {
       fetch();
-      has_next = decode_pos<S>(n_items, xcd, share_ticket(st ^ 1, fetched), wi, wh, wsplit, wdvh);
+      has_next = take(st ^ 1);
     }
     // Free stage for the epilogue: the one the last block read (the next item's first block sits
     // in the other), or, for an item without blocks, the one the next item will be copied into.
