@@ -406,23 +406,6 @@ __device__ __forceinline__ void load_q(const DenseCtx<NQ, S>& c, const Item& it,
     for (int kk = 0; kk < S::DQK / 16; ++kk) qf[nq][kk] = *reinterpret_cast<const bf16x8*>(qp[nq] + kk * 16);
 }
 
-// Pulls an item's Q tile into L2 ahead of its loads: the tile's rows are runs of DQK*2/128 cache
-// lines of 128 bytes; each thread touches 2 of the tile's lines (lines past the tile repeat). The
-// two values must be passed to touch_done() once they may have arrived (it makes no wait of its
-// own after a wait_vmem()).
-template <int NQ, class S>
-__device__ __forceinline__ void touch_q(const Item& it, int (&t)[2]) {
-  const DenseParams& p = kargs();
-  constexpr int LPR = S::DQK * 2 / 128;  // cache lines per row
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int line = (int)opaque(threadIdx.x) + i * 256;
-    const int r = min((line / LPR) % (128 * NQ), it.rows - 1);
-    const __bf16* qp = p.q + (int64_t)(it.cq0 + it.row0 + r) * p.q_st + (int64_t)it.h * p.q_sh + (line % LPR) * 64;
-    t[i] = *reinterpret_cast<const int*>(qp);
-  }
-}
-__device__ __forceinline__ void touch_done(const int (&t)[2]) { asm volatile("" ::"v"(t[0]), "v"(t[1])); }
 
 // fp32 -> four OCP fp8 e4m3 bytes (round to nearest even), saturated at +-448 first so that no
 // value overflows to NaN; byte i of the result encodes x[i].
@@ -714,10 +697,10 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
     }
     const bool had_blocks = cur.blo < cur.bhi;
     // Hand-over to the next item: its ticket is fetched at the start of block fetch_j, shared at
-    // the start of block share_j (where its descriptor is built and its Q tile pulled into L2),
-    // and the last block copies its first key block and loads its Q^T fragments. Sharing waits
-    // for the ticket, so it comes at least one block after the fetch whenever the item has two
-    // blocks or more.
+    // the start of block share_j (where its descriptor is built), and the last block copies its
+    // first key block and loads its Q^T fragments. Sharing waits for the ticket, so it comes at
+    // least one block after the fetch whenever the item has two blocks or more. (Pulling the next
+    // Q tile into L2 ahead of its loads measured slower than loading it cold.)
     const int fetch_j = max(cur.blo, cur.bhi - 4);
     const int share_j = cur.bhi - cur.blo >= 3 ? cur.bhi - 2 : cur.bhi - 1;
     Item nxt = cur;
@@ -738,16 +721,11 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
       const int vis_end = min(cur.sk, causal ? qmax + diag + 1 : cur.sk);
 
       auto no_q = [](int) {};
-      int touched[2] = {0, 0};
       auto prepare = [&](int jj) {  // at the start of block jj, before its copy
         if (jj == fetch_j) fetch();
         if (jj == share_j) {
           has_next = take(st ^ 1);
-          if (has_next) {
-            nxt = make_item<NQ, S>(wi, wh, wsplit, wdvh);
-            // (in the last block itself the fragment loads follow at once: no use touching)
-            if (jj + 1 < cur.bhi) touch_q<NQ, S>(nxt, touched);
-          }
+          if (has_next) nxt = make_item<NQ, S>(wi, wh, wsplit, wdvh);
         }
       };
       int j = cur.blo;
@@ -762,7 +740,6 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
                                   stage_v(st), qf, m_run, l_run, o, p.scale_log2, causal, no_q);
           wait_vmem();
           __syncthreads();
-          touch_done(touched);
         }
       }
       for (; j < jm; ++j, st ^= 1) {
@@ -787,7 +764,6 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
           issue_block_load(c, cur, j + 1, stage_k(st ^ 1), stage_v(st ^ 1));
         wait_vmem();
         __syncthreads();
-        touch_done(touched);
       }
       // Last block: hand over to the next item. Its first key block is copied into the other
       // stage, and each of its Q^T fragments is loaded as soon as the matching fragment of this
@@ -806,7 +782,6 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
                                 });
         wait_vmem();
         __syncthreads();
-        touch_done(touched);
         st ^= 1;
       }
     } else {
