@@ -307,14 +307,6 @@ __device__ __forceinline__ T ld_const(const T* ptr, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)ptr)[i];
 }
 
-// Decodes position i of the work list of XCD `xcd` (the positions are handed out by that XCD's
-// ticket counter). Work items are (plan item, unit) pairs with units
-// u = (h * num_splits + split) * DVH + dvh (the column tiles of a head and split are neighbours).
-// When the units divide evenly over the XCDs, XCD k owns the contiguous units
-// [k * units/8, (k+1) * units/8) (neighbouring heads, whose rows sit side by side in memory) and
-// lists them in groups of group_units, group-major, then plan item (longest first), then unit
-// within the group. Otherwise the lists interleave one global order of the same form: XCD k holds
-// its positions t = 8*i + k. Returns false past the end of the list.
 // Positions in the work list of XCD `xcd` (see decode_pos).
 template <class S>
 __device__ __forceinline__ int list_len(int n_items, int xcd) {
@@ -324,6 +316,15 @@ __device__ __forceinline__ int list_len(int n_items, int xcd) {
   return total > xcd ? (total - xcd + 7) / 8 : 0;
 }
 
+// Decodes position i of the work list of XCD `xcd` (the positions are handed out by that XCD's
+// ticket counter). Work items are (plan item, unit) pairs with units
+// u = (h * num_splits + split) * DVH + dvh (the column tiles of a head and split are neighbours).
+// When the units divide evenly over the XCDs, XCD k owns the contiguous units
+// [k * units/8, (k+1) * units/8) (neighbouring heads, whose rows sit side by side in memory) and
+// lists them in groups of group_units, group-major, then plan item (longest first), then unit
+// within the group, except that the shortest eighth of the plan items comes last for all units
+// together. Otherwise the lists interleave one global order of the same form: XCD k holds
+// its positions t = 8*i + k. Returns false past the end of the list.
 template <class S>
 __device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& item, int& h, int& split, int& dvh) {
   const DenseParams& p = kargs();
@@ -331,13 +332,26 @@ __device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& ite
   const int gu = p.group_units;
   int u;
   if (p.xcd_units > 0) {
-    const int n_x = n_items * p.xcd_units;
+    const int xu = p.xcd_units;
+    const int n_x = n_items * xu;
     if (i < 0 || i >= n_x) return false;
-    const int per_group = n_items * gu;
-    const int grp = i / per_group;
-    const int r = i - grp * per_group;
-    item = r / gu;
-    u = xcd * p.xcd_units + grp * gu + (r - item * gu);
+    // The shortest eighth of the plan items (listed last by the planner) closes the list for all
+    // of the XCD's units, item by item, so that the last work to start is short whichever unit
+    // it belongs to; the rest goes group by group as above.
+    const int n_long = n_items - n_items / 8;
+    const int i_tail = n_long * xu;
+    if (i >= i_tail) {
+      const int r = i - i_tail;
+      const int k = r / xu;
+      item = n_long + k;
+      u = xcd * xu + (r - k * xu);
+    } else {
+      const int per_group = n_long * gu;
+      const int grp = i / per_group;
+      const int r = i - grp * per_group;
+      item = r / gu;
+      u = xcd * xu + grp * gu + (r - item * gu);
+    }
   } else {
     const int total = n_items * units;
     const int n_x = total > xcd ? (total - xcd + 7) / 8 : 0;
