@@ -17,7 +17,8 @@
 // a 3-slot LDS ring, copied straight from global memory (global_load_lds, 1 KiB per wave copy)
 // two stages ahead of the compute; a 64-byte operand row keeps its 16-byte chunk c at
 // c ^ ((r >> 2) & 3), which makes the operand reads conflict-free under gfx950's 16-byte read
-// grouping. The key work-groups also copy the rope columns into every head's key.
+// grouping. The output tile is turned around in the (then free) ring and written as whole
+// 128-byte row segments. The key work-groups also copy the rope columns into every head's key.
 #include "common.h"
 #include "kernels.h"
 
@@ -154,24 +155,31 @@ __global__ __launch_bounds__(UP_THREADS) void upproj_kernel(UpprojParams p) {
     }
     ring_barrier();
   }
-  // accumulator (i, j): lane holds output columns 64 wm + 32 i + 8 (e / 4) + 4 hl + e % 4 of tile
-  // row 64 wn + 32 j + l32
+  // Output through LDS (the ring is free now): the wave's 64 x 64 tile goes to its own 8 KiB
+  // (64 rows of 128 bytes, 16-byte chunk c of row r at c ^ (r & 7)) and leaves as whole 128-byte
+  // row segments.
   __bf16* dst = is_key ? p.kbuf : p.vbuf;
   const int64_t dst_st = is_key ? p.k_st : p.v_st;
+  char* ob = ((wave & 1) ? lds_c : lds_w) + (wave >> 1) * 8192;
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int r = wn * 64 + j * 32 + l32;
-    if (r >= rows) continue;
-    __bf16* row = dst + (buf_row0 + r) * dst_st + (int64_t)h * (is_key ? p.k_sh : p.v_sh);
+  for (int j = 0; j < 2; ++j)
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int col = wm * 64 + i * 32 + 8 * g + 4 * hl;
+        const int r = j * 32 + l32;
         const f32x16& v = acc[i][j];
         u32x2 o = {pack_bf16x2(v[4 * g], v[4 * g + 1]), pack_bf16x2(v[4 * g + 2], v[4 * g + 3])};
-        *reinterpret_cast<u32x2*>(row + col) = o;
+        *reinterpret_cast<u32x2*>(ob + r * 128 + (((4 * i + g) ^ (r & 7)) * 16) + 8 * hl) = o;
       }
+  const int cc = lane & 7;
+#pragma unroll
+  for (int ps = 0; ps < 8; ++ps) {
+    const int r = ps * 8 + (lane >> 3);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(ob + r * 128 + ((cc ^ (r & 7)) * 16));
+    const int tr = wn * 64 + r;
+    if (tr < rows)
+      *reinterpret_cast<u32x4*>(dst + (buf_row0 + tr) * dst_st + (int64_t)h * (is_key ? p.k_sh : p.v_sh) + wm * 64 + cc * 8) = v;
   }
   if (is_key) {
     // rope columns 512..575 of the cached row -> key columns 128..191 of head h
