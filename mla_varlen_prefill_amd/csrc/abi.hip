@@ -109,14 +109,15 @@ bool dense_dims_ok(int dqk, int dv) {
   return (dqk == 192 && dv == 128) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256);
 }
 
-// Instance of a dense call: its tile height (nq * 128 rows) and resident work-groups per CU.
+// Instance of a dense call: query tiles per wave, resident work-groups per CU and tile height.
 struct DenseShape {
-  int dqk, dv, nq, occ;
+  int dqk, dv, nq, occ, bm;
   bool fp8;
 };
 DenseShape dense_shape(int dqk, int dv, bool fp8) {
-  DenseShape d{dqk, dv, (dqk == 192 && dv == 128 && !fp8) ? dense_nq() : 1, 1, fp8};
+  DenseShape d{dqk, dv, (dqk == 192 && dv == 128 && !fp8) ? dense_nq() : 1, 1, 128, fp8};
   d.occ = mla::dense_occupancy_of(d.nq, dqk, dv);
+  d.bm = mla::dense_rows_per_tile(d.nq, dqk, dv);
   return d;
 }
 
@@ -151,7 +152,7 @@ int32_t resolve_splits(int32_t batch, int32_t max_q, int32_t max_k, int32_t head
   const DeviceInfo* di = device_info();
   const int cus = (di != nullptr && di->cus > 0) ? di->cus : 256;
   const int64_t conc = (int64_t)cus * ds.occ;
-  const int64_t items = (int64_t)batch * cdiv(max_q, 128 * ds.nq) * heads;
+  const int64_t items = (int64_t)batch * cdiv(max_q, ds.bm) * heads;
   if (items <= 0 || items >= conc) return 1;
   const int64_t max_blocks = cdiv(max_k, kDenseBN);
   int64_t s = cdiv(conc, items);
@@ -163,7 +164,7 @@ int32_t resolve_splits(int32_t batch, int32_t max_q, int32_t max_k, int32_t head
 VarlenLayout varlen_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_t max_k,
                            int32_t heads, int32_t num_splits, const DenseShape& ds) {
   VarlenLayout L{};
-  L.bm = 128 * ds.nq;
+  L.bm = ds.bm;
   L.mt = (int32_t)cdiv(std::max(max_q, 0), L.bm);
   L.n_slots = batch * L.mt;
   L.splits = resolve_splits(batch, max_q, max_k, heads, num_splits, ds);

@@ -56,10 +56,16 @@ struct Shape {
   static constexpr int DQK = DQK_, DV = DV_;
   static constexpr int DVT = 128, DVH = DV / DVT;
   static constexpr bool FP8 = FP8_;                         // fp8 e4m3 output with a static scale
+  // Waves per work-group (32 query rows each). The 256-wide layout needs all of a wave's
+  // registers at two waves per SIMD and 96 KB of LDS per work-group, so its work-groups have
+  // eight waves (one per CU); the others run two four-wave work-groups per CU.
+  static constexpr int NW = DQK == 256 ? 8 : 4;
+  // operand reads run PF MFMA steps ahead (fewer where registers are short)
+  static constexpr int PF = DQK == 256 ? 3 : 6;
   static constexpr int K_STAGE_BYTES = BN * DQK * 2;
   static constexpr int V_STAGE_BYTES = BN * DVT * 2;
-  static constexpr int KCH = BN * (DQK / 8) / 256;          // wave-wide 1 KiB copies per K block
-  static constexpr int VCH = BN * (DVT / 8) / 256;
+  static constexpr int KCH = BN * (DQK / 8) / (64 * NW);    // wave-wide 1 KiB copies per K block
+  static constexpr int VCH = BN * (DVT / 8) / (64 * NW);
   // K operand addressing: the swizzle permutes 16-byte chunks inside groups of KA_GROUP bytes;
   // KA_N per-lane offsets cover one group's MFMA steps.
   static constexpr int KA_GROUP = DQK == 192 ? 128 : 256;
@@ -67,7 +73,7 @@ struct Shape {
   // The work ticket handed between waves sits past the epilogue area of the wave's K copy region
   // when it fits there, else at the start of the wave's V copy region (which the epilogue never uses).
   static constexpr bool TICKET_IN_K = kEpilogueBytes + 4 <= KCH * 1024;
-  static_assert((BN * DQK / 8) % 256 == 0 && DV % DVT == 0, "shape");
+  static_assert((BN * DQK / 8) % (64 * NW) == 0 && (BN * DVT / 8) % (64 * NW) == 0 && DV % DVT == 0, "shape");
 };
 
 // K swizzle: chunk c of row r is stored at chunk c ^ kswz(r). 384-byte rows (an odd multiple of
@@ -163,7 +169,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
   for (int nq = 0; nq < NQ; ++nq) s[nq][0] = s[nq][1] = f32x16{};
   {
     constexpr int NSTEP = NMT * (DQK / 16);  // (kk, mt) steps
-    constexpr int PF = 6;
+    constexpr int PF = S::PF;
     bf16x8 a[NSTEP];
 #pragma unroll
     for (int st = 0; st < PF; ++st) {
@@ -260,7 +266,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
   // run PF steps ahead of their MFMA.
   {
     constexpr int NSTEP = 2 * NMT * (DV / 32);   // (mt, cc) x dt
-    constexpr int PF = 6;
+    constexpr int PF = S::PF;
     bf16x8 a[NSTEP];
     // The wave issues these products at raised priority: the other wave on the SIMD, in its
     // softmax or S phase, then takes the issue slots the matrix core leaves (measured +2.5% on
@@ -388,8 +394,8 @@ __device__ __forceinline__ Item make_item(int item, int h, int split, int dvh) {
   it.sq = f[1];
   const int ck0 = f[2];
   it.sk = f[3];
-  it.row0 = m * 128 * NQ;
-  it.rows = min(128 * NQ, it.sq - it.row0);
+  it.row0 = m * 32 * S::NW * NQ;
+  it.rows = min(32 * S::NW * NQ, it.sq - it.row0);
   // with a left window the item's blocks start at the block of the first key its first row sees
   const int blk0 = p.win_left >= 0 ? min(max(it.row0 + it.sk - it.sq - p.win_left, 0), it.sk) / BN : 0;
   it.blo = blk0 + (int)(((int64_t)split * nb) / p.num_splits);
@@ -580,7 +586,7 @@ constexpr int dense_occupancy() {
 }
 
 template <int NQ, class S>
-__global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_kernel(DenseParams p) {
+__global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_fwd_kernel(DenseParams p) {
   constexpr int DQK = S::DQK, DV = S::DVT, KCH = S::KCH, VCH = S::VCH;
   __shared__ __attribute__((aligned(1024))) char lds_k0[S::K_STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char lds_v0[S::V_STAGE_BYTES];
@@ -611,7 +617,7 @@ __global__ __launch_bounds__(256, (dense_occupancy<NQ, S>())) void dense_fwd_ker
   auto share_ticket = [&](int sfree, int tk) -> int {
     if (threadIdx.x == 0) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) *reinterpret_cast<int*>(ticket_slot(sfree, w)) = tk;
+      for (int w = 0; w < S::NW; ++w) *reinterpret_cast<int*>(ticket_slot(sfree, w)) = tk;
     }
     __syncthreads();
     return __builtin_amdgcn_readfirstlane(*reinterpret_cast<const volatile int*>(ticket_slot(sfree, wave)));
@@ -838,7 +844,7 @@ template __global__ void dense_fwd_kernel<1, Shape256F8>(DenseParams);
 
 template <int NQ, class S>
 static void launch_one(const DenseParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((dense_fwd_kernel<NQ, S>), dim3(grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL((dense_fwd_kernel<NQ, S>), dim3(grid), dim3(64 * S::NW), 0, stream, p);
 }
 
 int dense_occupancy_of(int nq, int dqk, int dv) {
@@ -846,6 +852,13 @@ int dense_occupancy_of(int nq, int dqk, int dv) {
   if (dqk == 256 && dv == 256) return dense_occupancy<1, Shape256>();
   if (dqk == 128 && dv == 128) return dense_occupancy<1, Shape128>();
   return dense_occupancy<1, Shape192>();
+}
+
+int dense_rows_per_tile(int nq, int dqk, int dv) {
+  if (nq == 2) return 32 * Shape192::NW * 2;
+  if (dqk == 256 && dv == 256) return 32 * Shape256::NW;
+  if (dqk == 128 && dv == 128) return 32 * Shape128::NW;
+  return 32 * Shape192::NW;
 }
 
 hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool fp8_out, hipStream_t stream) {

@@ -111,6 +111,8 @@ hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream);
 hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool fp8_out, hipStream_t stream);
 // Resident work-groups per CU of the instance.
 int dense_occupancy_of(int nq, int dqk, int dv);
+// Query rows per work item (tile height) of the instance.
+int dense_rows_per_tile(int nq, int dqk, int dv);
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 
