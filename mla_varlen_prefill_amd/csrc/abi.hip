@@ -284,11 +284,12 @@ static mla_status_t varlen_call(
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream,
-    float* part_o = nullptr, float* part_lse = nullptr, bool accumulate = false) {
+    float* part_o = nullptr, float* part_lse = nullptr, int accumulate = 0) {
   // out_scale: null for bf16 output, else fp8 e4m3 output of O / *out_scale.
   // part_o / part_lse (internal use): write the normalised fp32 result [total_q, H, Dv] and its
   // LSE [total_q, H] there instead of `out` / `lse`, unsplit and without the sink; with
-  // `accumulate`, merge it into the running result already held there.
+  // accumulate = 1, merge it into the running result already held there; with 2, merge it with
+  // that result and write the final `out` / `lse` (sink folded in) instead.
   if (part_o != nullptr) num_splits = 1;
   if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
       cu_seqlens_k == nullptr || out == nullptr)
@@ -301,7 +302,7 @@ static mla_status_t varlen_call(
   if (!dense_dims_ok(head_dim_qk, head_dim_v) || num_heads > 65535 ||
       max_seqlen_k > (1 << 24) || k_stride_tok >= (1 << 23) || v_stride_tok >= (1 << 23))
     return MLA_ERR_UNSUPPORTED;  // key-block byte offsets are kept in 31 bits
-  const bool fp8 = out_scale != nullptr && part_o == nullptr;
+  const bool fp8 = out_scale != nullptr && (part_o == nullptr || accumulate == 2);
   const DenseShape ds = dense_shape(head_dim_qk, head_dim_v, fp8);
   // fp8 rows are written in 16-byte pieces: strides in whole 16-element units
   const bool ostride_ok = fp8 ? ((o_stride_tok & 15) == 0 && (o_stride_head & 15) == 0)
@@ -370,7 +371,7 @@ static mla_status_t varlen_call(
   } else if (part_o != nullptr) {
     dp.o_part = part_o;
     dp.lse_part = part_lse;
-    dp.accumulate = accumulate ? 1 : 0;
+    dp.accumulate = accumulate;
   }
   {
     dp.wgs_per_xcd = L.wgs_per_xcd;
@@ -567,6 +568,12 @@ mla_status_t mla_prefill_chunked_context(
   int32_t* cu_chunk = reinterpret_cast<int32_t*>(ws + C.off_cu);
   void* kbuf = ws + C.off_k;
   void* vbuf = ws + C.off_v;
+  // Without context the result is the causal prefill of the new tokens.
+  if (max_seqlen_ctx == 0)
+    return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
+                       v_stride_head, cu_seqlens_q, cu_seqlens_q, batch, total_q, max_seqlen_q, max_seqlen_q,
+                       num_heads, kDenseDqk, kDenseDv, softmax_scale, 1, -1, -1, 1, sink, nullptr, out,
+                       o_stride_tok, o_stride_head, lse, lse_stride_tok, lse_stride_head, ws, C.dense, hip_stream);
   // 1. the new tokens against themselves, causally: the first accumulated part
   mla_status_t st = varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
                                 v_stride_head, cu_seqlens_q, cu_seqlens_q, batch, total_q, max_seqlen_q,
@@ -575,33 +582,22 @@ mla_status_t mla_prefill_chunked_context(
                                 hip_stream, acc, la);
   if (st != MLA_OK) return st;
   // 2. each context chunk: up-project into the bounded buffer, attend without a mask and merge the
-  //    chunk's result into the running one in the attention kernel's epilogue
+  //    chunk's result into the running one in the attention kernel's epilogue; the last chunk's
+  //    epilogue writes the final output, with the sink folded in once
   const int64_t kst = (int64_t)num_heads * kDenseDqk, vst = (int64_t)num_heads * kDenseDv;
-  const int32_t rows = total_q * num_heads;
   for (int64_t c0 = 0; c0 < max_seqlen_ctx; c0 += chunk_tokens) {
     st = mla_latent_upproject(latent, latent_stride_row, cu_seqlens_ctx, batch, (int32_t)c0, chunk_tokens, w_kv,
                               w_stride_row, num_heads, cu_chunk, kbuf, vbuf, hip_stream);
     if (st != MLA_OK) return st;
+    const bool last = c0 + chunk_tokens >= max_seqlen_ctx;
     st = varlen_call(q, q_stride_tok, q_stride_head, kbuf, kst, kDenseDqk, vbuf, vst, kDenseDv, cu_seqlens_q,
                      cu_chunk, batch, total_q, max_seqlen_q, chunk_tokens, num_heads, kDenseDqk, kDenseDv,
-                     softmax_scale, 0, -1, -1, 1, nullptr, nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws,
-                     C.dense, hip_stream, acc, la, true);
+                     softmax_scale, 0, -1, -1, 1, last ? sink : nullptr, nullptr, out, o_stride_tok, o_stride_head,
+                     last ? lse : nullptr, lse_stride_tok, lse_stride_head, ws, C.dense, hip_stream, acc, la,
+                     last ? 2 : 1);
     if (st != MLA_OK) return st;
   }
-  // 3. the accumulated result to bf16, with the sink folded in once
-  mla::CombineParams cp{};
-  cp.o_part = acc;
-  cp.lse_part = la;
-  cp.num_splits = 1;
-  cp.rows = rows;
-  cp.num_heads = num_heads;
-  cp.dv = kDenseDv;
-  cp.sink = sink;
-  cp.out = out; cp.o_st = o_stride_tok; cp.o_sh = o_stride_head;
-  cp.lse = lse; cp.l_st = lse_stride_tok; cp.l_sh = lse_stride_head;
-  return timed_launch(MLA_KERNEL_COMBINE, stream, [&] { return mla::launch_combine(cp, stream); }) == hipSuccess
-             ? MLA_OK
-             : MLA_ERR_HIP;
+  return MLA_OK;
 }
 
 size_t mla_prefill_sparse_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,

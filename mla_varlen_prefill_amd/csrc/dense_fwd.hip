@@ -442,7 +442,7 @@ __device__ __forceinline__ uint32_t pack_fp8x4(float x0, float x1, float x2, flo
 
 template <int NQ, class S>
 __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item& it, const float (&m_run)[NQ],
-                                           const float (&l_run)[NQ], const f32x16 (&o)[NQ][S::DVT / 32],
+                                           const float (&l_run)[NQ], f32x16 (&o)[NQ][S::DVT / 32],
                                            char* stage) {
   constexpr int DV = S::DVT;  // the columns this item computes: [dvh * DVT, (dvh + 1) * DVT)
   constexpr int ESZ = S::FP8 ? 1 : 2;  // output element bytes
@@ -452,7 +452,11 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
   const float scale = p.scale;
   float* const o_part = p.o_part;
   float* const lse_part = p.lse_part;
+  // accumulate 1: merge into the running result held in o_part / lse_part; 2: merge with it and
+  // write the final output (sink folded into the merged result) instead
   const bool accumulate = p.accumulate != 0;
+  const bool final_merge = p.accumulate == 2;
+  const bool to_part = o_part != nullptr && !final_merge;
   const int64_t part_row = (int64_t)it.split * p.total_q;  // split-mode row base
   const int num_heads = p.num_heads;
   char* const out_h = static_cast<char*>(p.out) + ((int64_t)h * p.o_sh + it.dvh * DV) * ESZ;
@@ -463,8 +467,9 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
   float* const lse = p.lse;
   const int64_t l_st = p.l_st, l_sh = p.l_sh;
   const float sink_v = (p.sink != nullptr && o_part == nullptr) ? ld_const(p.sink, h) : -INFINITY;
+  const float sink_f = (p.sink != nullptr && final_merge) ? ld_const(p.sink, h) : -INFINITY;
   // fp8 output: O / out_scale (multiplied by the reciprocal)
-  const float q_mul = (S::FP8 && o_part == nullptr) ? 1.f / ld_const(p.out_scale, 0) : 1.f;
+  const float q_mul = (S::FP8 && !to_part) ? 1.f / ld_const(p.out_scale, 0) : 1.f;
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
     const float l_tot = xhalf_sum(l_run[nq]);
@@ -488,7 +493,44 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
     }
     if (r < it.rows) {
       const int tok = it.cq0 + it.row0 + r;
-      if (o_part != nullptr) {
+      if (final_merge) {
+        // the running result merged with this one, normalised, then the sink folded in; the
+        // merged values replace the accumulators for the output path below
+        const float* op = o_part + ((int64_t)tok * num_heads + h) * S::DV + it.dvh * DV;
+        const float l_old = lse_part[(int64_t)tok * num_heads + h];
+        f32x4 old[DV / 32][4];
+#pragma unroll
+        for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) old[dt][g4] = *reinterpret_cast<const f32x4*>(op + dt * 32 + 8 * g4 + 4 * c.hl);
+        float w_new = 0.f, w_old = 0.f, lse_m = -INFINITY;
+        const float mx = fmaxf(l_old, lse_v);
+        if (mx != -INFINITY) {
+          const float eo = __expf(l_old - mx), en = __expf(lse_v - mx);
+          const float rt = 1.f / (eo + en);
+          w_old = eo * rt;
+          w_new = inv * en * rt;
+          lse_m = mx + __logf(eo + en);
+        }
+        float fin = 1.f;
+        lse_v = lse_m;
+        if (sink_f != -INFINITY) {
+          const float ms = fmaxf(lse_m, sink_f);
+          const float a = __expf(lse_m - ms);
+          const float z = a + __expf(sink_f - ms);
+          fin = a / z;
+          lse_v = ms + __logf(z);
+        }
+#pragma unroll
+        for (int dt = 0; dt < DV / 32; ++dt)
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              o[nq][dt][g4 * 4 + e] = (o[nq][dt][g4 * 4 + e] * w_new + old[dt][g4][e] * w_old) * fin;
+        inv = 1.f;
+      }
+      if (to_part) {
         float* op = o_part + ((part_row + tok) * num_heads + h) * S::DV + it.dvh * DV;
         float* lp = lse_part + (part_row + tok) * num_heads + h;
         float w_new = inv, w_old = 0.f;
@@ -527,7 +569,7 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
         lse[(int64_t)tok * l_st + (int64_t)h * l_sh] = lse_v;
       }
     }
-    if (o_part == nullptr) {
+    if (!to_part) {
       // Output through LDS: the lane layout holds pieces of 4 consecutive columns of a row, so the
       // tile is turned around in this wave's own copy region of a free stage, one 128-byte row
       // segment at a time (64 bf16 or 128 fp8 columns; 16-byte chunks XOR-swizzled by row), and

@@ -47,7 +47,8 @@ struct DenseParams {
   float* lse; int64_t l_st, l_sh;
   float* o_part;         // split mode: [S][total_q][H][DV] fp32, else null
   float* lse_part;       // split mode: [S][total_q][H]
-  int32_t accumulate;    // with one split: merge into o_part / lse_part (running result) in place
+  int32_t accumulate;    // with one split: 1 = merge into o_part / lse_part (running result) in
+                         // place; 2 = merge with it and write out / lse (with the sink) instead
   int32_t total_q;
   int32_t wgs_per_xcd;   // persistent grid: 8 * wgs_per_xcd work-groups
   int32_t group_units;   // (head, split) units per scheduling group
