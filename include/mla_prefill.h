@@ -18,8 +18,15 @@
  *  - `sink` (nullable) is one float32 logit per head, used as-is (not scaled) as an extra key
  *    whose value vector is zero.
  *  - Errors are returned as mla_status_t; nothing is launched when a call returns an error.
- *    Per-element contents (cu_seqlens values, index values) are not validated: out-of-range
- *    sparse indices are skipped, which is memory-safe; malformed cu_seqlens are the caller's bug.
+ *    Per-element contents (cu_seqlens values, index values) are not validated by default:
+ *    out-of-range sparse indices are skipped, which is memory-safe; malformed cu_seqlens are the
+ *    caller's bug. With the environment variable MLA_VALIDATE set to a nonzero integer (read at
+ *    every call), the dense and chunked-context entry points and the paged sparse entry point
+ *    first copy their cu_seqlens to the host, SYNCHRONISING the stream, and return
+ *    MLA_ERR_INVALID_ARG unless every array starts at 0 and is non-decreasing with no length
+ *    above its max_seqlen, cu_seqlens_q ends at total_q (dense, chunked context) or at most at
+ *    num_tokens (paged sparse); MLA_ERR_HIP if the copy fails. It is a debugging aid, not for
+ *    graph capture.
  *  - `out`/`lse` must not alias any input or the workspace.
  */
 #ifndef MLA_PREFILL_H

@@ -133,6 +133,29 @@ int dense_group_per_xcd() {
 }
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// MLA_VALIDATE (nonzero): check cu_seqlens contents on the host before launching (synchronises).
+bool validate_inputs() {
+  const char* e = std::getenv("MLA_VALIDATE");
+  return e != nullptr && std::atoi(e) != 0;
+}
+
+// cu [batch + 1] starts at 0 and is non-decreasing with lengths <= max_len; its last entry equals
+// `last` (exact) or is at most `last` (!exact); last < 0: not checked.
+mla_status_t check_cu(const int32_t* cu, int32_t batch, int64_t last, bool exact, int32_t max_len,
+                      hipStream_t stream) {
+  std::vector<int32_t> h((size_t)batch + 1);
+  if (hipMemcpyAsync(h.data(), cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return MLA_ERR_HIP;
+  if (h[0] != 0) return MLA_ERR_INVALID_ARG;
+  for (int32_t b = 0; b < batch; ++b) {
+    const int64_t len = (int64_t)h[b + 1] - h[b];
+    if (len < 0 || len > max_len) return MLA_ERR_INVALID_ARG;
+  }
+  if (last >= 0 && (exact ? h[batch] != last : h[batch] > last)) return MLA_ERR_INVALID_ARG;
+  return MLA_OK;
+}
 inline bool stride_ok(int64_t s) { return s >= 0 && (s & 7) == 0; }
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
@@ -284,12 +307,13 @@ static mla_status_t varlen_call(
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream,
-    float* part_o = nullptr, float* part_lse = nullptr, int accumulate = 0) {
+    float* part_o = nullptr, float* part_lse = nullptr, int accumulate = 0, bool check = true) {
   // out_scale: null for bf16 output, else fp8 e4m3 output of O / *out_scale.
   // part_o / part_lse (internal use): write the normalised fp32 result [total_q, H, Dv] and its
   // LSE [total_q, H] there instead of `out` / `lse`, unsplit and without the sink; with
   // accumulate = 1, merge it into the running result already held there; with 2, merge it with
-  // that result and write the final `out` / `lse` (sink folded in) instead.
+  // that result and write the final `out` / `lse` (sink folded in) instead. check = false skips
+  // the MLA_VALIDATE checks (cu_seqlens built by the library itself).
   if (part_o != nullptr) num_splits = 1;
   if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
       cu_seqlens_k == nullptr || out == nullptr)
@@ -332,6 +356,11 @@ static mla_status_t varlen_call(
   if (!di->gfx950) return MLA_ERR_UNSUPPORTED;
 
   hipStream_t stream = (hipStream_t)hip_stream;
+  if (check && validate_inputs()) {
+    mla_status_t st = check_cu(cu_seqlens_q, batch, total_q, true, max_seqlen_q, stream);
+    if (st == MLA_OK) st = check_cu(cu_seqlens_k, batch, -1, true, max_seqlen_k, stream);
+    if (st != MLA_OK) return st;
+  }
   char* ws = static_cast<char*>(workspace);
   int32_t* num_items = reinterpret_cast<int32_t*>(ws + L.off_count);
   int32_t* plan = reinterpret_cast<int32_t*>(ws + L.off_plan);
@@ -562,6 +591,11 @@ mla_status_t mla_prefill_chunked_context(
   if (workspace == nullptr || workspace_bytes < C.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   hipStream_t stream = (hipStream_t)hip_stream;
+  if (validate_inputs()) {
+    mla_status_t vs = check_cu(cu_seqlens_q, batch, total_q, true, max_seqlen_q, stream);
+    if (vs == MLA_OK) vs = check_cu(cu_seqlens_ctx, batch, -1, true, max_seqlen_ctx, stream);
+    if (vs != MLA_OK) return vs;
+  }
   char* ws = static_cast<char*>(workspace);
   float* acc = reinterpret_cast<float*>(ws + C.off_acc);
   float* la = reinterpret_cast<float*>(ws + C.off_la);
@@ -573,13 +607,14 @@ mla_status_t mla_prefill_chunked_context(
     return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
                        v_stride_head, cu_seqlens_q, cu_seqlens_q, batch, total_q, max_seqlen_q, max_seqlen_q,
                        num_heads, kDenseDqk, kDenseDv, softmax_scale, 1, -1, -1, 1, sink, nullptr, out,
-                       o_stride_tok, o_stride_head, lse, lse_stride_tok, lse_stride_head, ws, C.dense, hip_stream);
+                       o_stride_tok, o_stride_head, lse, lse_stride_tok, lse_stride_head, ws, C.dense, hip_stream,
+                       nullptr, nullptr, 0, false);
   // 1. the new tokens against themselves, causally: the first accumulated part
   mla_status_t st = varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
                                 v_stride_head, cu_seqlens_q, cu_seqlens_q, batch, total_q, max_seqlen_q,
                                 max_seqlen_q, num_heads, kDenseDqk, kDenseDv, softmax_scale, 1, -1, -1, 1,
                                 nullptr, nullptr, out, o_stride_tok, o_stride_head, nullptr, 0, 0, ws, C.dense,
-                                hip_stream, acc, la);
+                                hip_stream, acc, la, 0, false);
   if (st != MLA_OK) return st;
   // 2. each context chunk: up-project into the bounded buffer, attend without a mask and merge the
   //    chunk's result into the running one in the attention kernel's epilogue; the last chunk's
@@ -594,7 +629,7 @@ mla_status_t mla_prefill_chunked_context(
                      cu_chunk, batch, total_q, max_seqlen_q, chunk_tokens, num_heads, kDenseDqk, kDenseDv,
                      softmax_scale, 0, -1, -1, 1, last ? sink : nullptr, nullptr, out, o_stride_tok, o_stride_head,
                      last ? lse : nullptr, lse_stride_tok, lse_stride_head, ws, C.dense, hip_stream, acc, la,
-                     last ? 2 : 1);
+                     last ? 2 : 1, false);
     if (st != MLA_OK) return st;
   }
   return MLA_OK;
@@ -712,6 +747,10 @@ mla_status_t mla_prefill_sparse_paged(
       (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) != 0 ||
       (seqused_kv != nullptr && (reinterpret_cast<uintptr_t>(seqused_kv) & 3u) != 0))
     return MLA_ERR_ALIGNMENT;
+  if (validate_inputs() && num_tokens > 0) {
+    const mla_status_t vs = check_cu(cu_seqlens_q, batch, num_tokens, false, INT32_MAX, (hipStream_t)hip_stream);
+    if (vs != MLA_OK) return vs;
+  }
   mla::SparseParams sp{};
   sp.block_table = block_table; sp.bt_st = bt_stride_seq;
   sp.max_blocks = max_blocks_per_seq; sp.block_size = block_size; sp.num_blocks = num_blocks;
