@@ -56,13 +56,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
   __shared__ int wave_tot[16];
   __shared__ int count_sh;
   const int tid = threadIdx.x;
+  const int nthr = blockDim.x;  // 1024, or fewer for small plans (sorting path only)
   const int n_slots = p.batch * p.mt;
   if (p.counters != nullptr && tid < 8) p.counters[tid * 32] = 0;
 
   if (n_slots <= kPlanSortCapacity) {
     int P = 1;
     while (P < n_slots) P <<= 1;
-    for (int s = tid; s < P; s += 1024) {
+    for (int s = tid; s < P; s += nthr) {
       uint32_t key = 0xFFFFFFFFu;
       if (s < n_slots) {
         const Item it = slot_item(p, s);
@@ -78,7 +79,7 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
     // bitonic sort, ascending: longest first, ties by slot; invalid (all ones) last
     for (int k = 2; k <= P; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < P; i += 1024) {
+        for (int i = tid; i < P; i += nthr) {
           const int ixj = i ^ j;
           if (ixj > i) {
             const uint32_t a = keys[i], c = keys[ixj];
@@ -92,14 +93,14 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
         __syncthreads();
       }
     }
-    for (int i = tid; i < P; i += 1024) {
+    for (int i = tid; i < P; i += nthr) {
       const bool v = keys[i] != 0xFFFFFFFFu;
       const bool next_v = (i + 1 < P) && keys[i + 1] != 0xFFFFFFFFu;
       if (v && !next_v) count_sh = i + 1;  // the single last valid entry
     }
     __syncthreads();
     const int count = count_sh;
-    for (int i = tid; i < p.capacity; i += 1024) {
+    for (int i = tid; i < p.capacity; i += nthr) {
       if (i < count) {
         write_item(p, i, slot_item(p, (int)(keys[i] & 0x3FFFu)));
       } else {
@@ -136,7 +137,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
 }
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, stream, p);
+  // A plan of up to 1024 slots is sorted by as many threads as its padded size (at least one
+  // wave, and at least the 8 that clear the ticket counters): fewer waves to synchronise.
+  const int64_t n_slots = (int64_t)p.batch * p.mt;
+  int threads = 1024;
+  if (n_slots <= 1024) {
+    threads = 64;
+    while (threads < n_slots) threads <<= 1;
+  }
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(threads), 0, stream, p);
   return hipGetLastError();
 }
 
