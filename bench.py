@@ -103,7 +103,7 @@ def time_steps(step, steps: int, warmup: int, kernel: str):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    mla.profile_enable(True)
+    mla.profile_enable(True, kinds=[kernel])  # events around the measured kernel only
     t0 = time.perf_counter()
     for _ in range(steps):
         step()

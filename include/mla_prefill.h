@@ -400,6 +400,9 @@ mla_status_t mla_combine(const float* o_part, const float* lse_part, int32_t num
 enum { MLA_KERNEL_PLAN = 0, MLA_KERNEL_DENSE = 1, MLA_KERNEL_COMBINE = 2, MLA_KERNEL_SPARSE = 3,
        MLA_KERNEL_UPPROJ = 4 };
 mla_status_t mla_profile_enable(int32_t enable);
+/* Restricts the timing to the kernel kinds whose bit (1 << MLA_KERNEL_x) is set in `kinds`
+ * (default: all); kinds left out are launched without events. Never fails. */
+mla_status_t mla_profile_select(uint32_t kinds);
 mla_status_t mla_profile_read(int32_t kernel, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus

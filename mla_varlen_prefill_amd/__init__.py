@@ -40,7 +40,7 @@ EXPORTED_SYMBOLS = (
     "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_prefill_sparse_paged",
     "mla_prefill_chunked_context_workspace_size", "mla_prefill_chunked_context", "mla_latent_upproject",
     "mla_combine",
-    "mla_profile_enable", "mla_profile_read",
+    "mla_profile_enable", "mla_profile_select", "mla_profile_read",
 )
 KERNEL_IDS = {"plan": 0, "dense": 1, "combine": 2, "sparse": 3, "upproj": 4}
 
@@ -121,6 +121,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                                 _vp, _c_i64, _c_i64, _vp]
     lib.mla_profile_enable.restype = ctypes.c_int
     lib.mla_profile_enable.argtypes = [_c_i32]
+    lib.mla_profile_select.restype = ctypes.c_int
+    lib.mla_profile_select.argtypes = [ctypes.c_uint32]
     lib.mla_profile_read.restype = ctypes.c_int
     lib.mla_profile_read.argtypes = [_c_i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_c_i64)]
     _lib = lib
@@ -420,9 +422,13 @@ def mla_combine(o_part: torch.Tensor, lse_part: torch.Tensor, num_heads: int,
     return (out, lse) if return_lse else out
 
 
-def profile_enable(enable: bool = True) -> None:
-    """Bracket every library kernel launch with HIP events on its stream (clears totals)."""
-    _check("mla_profile_enable", load_library().mla_profile_enable(int(bool(enable))))
+def profile_enable(enable: bool = True, kinds=None) -> None:
+    """Bracket library kernel launches with HIP events on their stream (clears totals): every
+    kind, or only the named ones (e.g. ["dense"])."""
+    lib = load_library()
+    mask = 0xFFFFFFFF if kinds is None else sum(1 << KERNEL_IDS[k] for k in kinds)
+    _check("mla_profile_select", lib.mla_profile_select(mask))
+    _check("mla_profile_enable", lib.mla_profile_enable(int(bool(enable))))
 
 
 def profile_read(kernel: str) -> Tuple[float, int]:

@@ -56,6 +56,7 @@ constexpr size_t kMaxPending = 65536;
 struct Profiler {
   std::mutex mu;
   std::atomic<bool> enabled{false};
+  std::atomic<uint32_t> kinds{0xFFFFFFFFu};  // bit k: time kernel kind k
   struct Rec {
     int kind;
     hipEvent_t a, b;
@@ -70,7 +71,8 @@ Profiler g_prof;
 // Launch `fn` (which enqueues one kernel on `stream`), bracketed by timing events when enabled.
 template <typename F>
 hipError_t timed_launch(int kind, hipStream_t stream, F&& fn) {
-  if (!g_prof.enabled.load(std::memory_order_relaxed)) return fn();
+  if (!g_prof.enabled.load(std::memory_order_relaxed) || ((g_prof.kinds.load(std::memory_order_relaxed) >> kind) & 1u) == 0)
+    return fn();
   std::pair<hipEvent_t, hipEvent_t> ev{nullptr, nullptr};
   {
     std::lock_guard<std::mutex> lk(g_prof.mu);
@@ -805,6 +807,11 @@ mla_status_t mla_profile_enable(int32_t enable) {
     g_prof.count[i] = 0;
   }
   g_prof.enabled.store(enable != 0);
+  return MLA_OK;
+}
+
+mla_status_t mla_profile_select(uint32_t kinds) {
+  g_prof.kinds.store(kinds);
   return MLA_OK;
 }
 
