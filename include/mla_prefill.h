@@ -74,8 +74,10 @@ void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n);
  * row and r the right window, 0 when causal). With a left window l >= 0 the first key any row
  * may see is kv_start = clamp(m * block_m + Sk_b - Sq_b - l, 0, Sk_b), else 0; n_blocks counts
  * the blocks from kv_start / block_n to ceil(kv_end / block_n) (0 when kv_end <= kv_start).
- * Items are ordered by n_blocks descending, then by slot (b * Mt + m) ascending; with more than
- * 16384 slots they stay in slot order. Words of unused items up to plan_capacity are set to -1.
+ * Items are ordered sequence by sequence, sequences with more key blocks first
+ * (min(ceil(Sk_b / block_n), 0x3FFFE) descending, ties by b ascending), and within a sequence
+ * from its last query tile to its first (m descending); with more than 16384 slots they stay in
+ * slot order. Words of unused items up to plan_capacity are set to -1.
  *
  *   cu_seqlens_q, cu_seqlens_k : device int32 [batch + 1], non-decreasing, starting at 0.
  *   causal, window_left, window_right : the mask rule of mla_prefill_varlen_window.

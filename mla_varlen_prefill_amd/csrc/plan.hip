@@ -5,9 +5,11 @@
 // helper that zeroes its counters (page "Mojo module mla", mla_prefill_plan_kernel,
 // set_buffer_lengths_to_zero); a metadata call producing a fixed-size int32 task split before
 // the attention call (page "SparseFlashMla", Description). The format is this library's own:
-// items (b, m, n_blocks, kv_end), longest first (n_blocks descending, then slot ascending),
-// unused entries -1. With a left window n_blocks counts from the block of the first key the
-// tile's first row sees (the dense kernel recomputes that block). Longest-first dispatch keeps causal and varlen batches load-balanced.
+// items (b, m, n_blocks, kv_end), sequence by sequence (sequences with more key blocks first,
+// ties by b) and within a sequence from its last query tile to its first, unused entries -1.
+// With a left window n_blocks counts from the block of the first key the tile's first row sees
+// (the dense kernel recomputes that block). Long work goes first, and the tiles in flight at
+// any time come from few sequences, whose keys and values then stay in L2.
 #include "common.h"
 #include "kernels.h"
 
@@ -68,8 +70,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
       if (s < n_slots) {
         const Item it = slot_item(p, s);
         if (it.valid) {
-          const uint32_t nb = (uint32_t)min(it.nb, kPlanMaxBlocks);
-          key = ((uint32_t)(kPlanMaxBlocks - nb) << 14) | (uint32_t)s;
+          // sequences with more key blocks first (ties by b), each from its last tile to its first
+          const uint32_t nbs = (uint32_t)min((it.sk + p.bn - 1) / p.bn, kPlanMaxBlocks);
+          key = ((uint32_t)(kPlanMaxBlocks - nbs) << 14) | (uint32_t)(it.b * p.mt + (p.mt - 1 - it.m));
         }
       }
       keys[s] = key;
@@ -102,7 +105,8 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
     const int count = count_sh;
     for (int i = tid; i < p.capacity; i += nthr) {
       if (i < count) {
-        write_item(p, i, slot_item(p, (int)(keys[i] & 0x3FFFu)));
+        const int kb = (int)(keys[i] & 0x3FFFu) / p.mt;  // key low bits: b * Mt + (Mt - 1 - m)
+        write_item(p, i, slot_item(p, kb * p.mt + (p.mt - 1 - ((int)(keys[i] & 0x3FFFu) - kb * p.mt))));
       } else {
         reinterpret_cast<int4*>(p.plan)[i] = make_int4(-1, -1, -1, -1);
       }

@@ -38,7 +38,9 @@ def test_plan_items_cover_and_order(lens_q, lens_k, causal, bm, bn):
     for (b, m, nb, kv_end) in items:
         assert kv_end == _brute_kv_end(lens_q[b], lens_k[b], m, bm, causal)
         assert nb == -(-kv_end // bn)
-    keys = [(-it[2], it[0] * mt + it[1]) for it in items]
+    # sequence by sequence (more key blocks first, ties by b), each from its last tile to its first
+    seq_blocks = [-(-n // bn) for n in lens_k]
+    keys = [(-seq_blocks[it[0]], it[0], -it[1]) for it in items]
     assert keys == sorted(keys)
 
 
@@ -76,7 +78,8 @@ def test_plan_buffer_fill_and_capacity():
     buf, n = plan_ref.plan_buffer(cu, cu, 200, 64, 64, True, capacity=10)
     assert n == 5 and buf.shape == (10, 4)
     assert np.all(buf[n:] == -1)
-    assert buf[0].tolist() == [1, 3, 4, 200]   # the last tile of the long sequence is longest
+    assert buf[0].tolist() == [1, 3, 4, 200]   # the sequence with more keys first, from its last tile
+    assert buf[1:4, 1].tolist() == [2, 1, 0] and buf[4].tolist()[:2] == [0, 0]
     with pytest.raises(ValueError):
         plan_ref.plan_buffer(cu, cu, 200, 64, 64, True, capacity=4)
 
