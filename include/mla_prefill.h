@@ -76,8 +76,9 @@ void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n);
  * the blocks from kv_start / block_n to ceil(kv_end / block_n) (0 when kv_end <= kv_start).
  * Items are ordered sequence by sequence, sequences with more key blocks first
  * (min(ceil(Sk_b / block_n), 0x3FFFE) descending, ties by b ascending), and within a sequence
- * from its last query tile to its first (m descending); with more than 16384 slots they stay in
- * slot order. Words of unused items up to plan_capacity are set to -1.
+ * from its last query tile to its first (m descending); with a left window (window_left >= 0)
+ * by n_blocks descending, then slot (b * Mt + m) ascending. With more than 16384 slots they stay
+ * in slot order. Words of unused items up to plan_capacity are set to -1.
  *
  *   cu_seqlens_q, cu_seqlens_k : device int32 [batch + 1], non-decreasing, starting at 0.
  *   causal, window_left, window_right : the mask rule of mla_prefill_varlen_window.

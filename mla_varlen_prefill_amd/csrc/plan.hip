@@ -6,7 +6,8 @@
 // set_buffer_lengths_to_zero); a metadata call producing a fixed-size int32 task split before
 // the attention call (page "SparseFlashMla", Description). The format is this library's own:
 // items (b, m, n_blocks, kv_end), sequence by sequence (sequences with more key blocks first,
-// ties by b) and within a sequence from its last query tile to its first, unused entries -1.
+// ties by b) and within a sequence from its last query tile to its first (with a left window:
+// n_blocks descending, then slot ascending), unused entries -1.
 // With a left window n_blocks counts from the block of the first key the tile's first row sees
 // (the dense kernel recomputes that block). Long work goes first, and the tiles in flight at
 // any time come from few sequences, whose keys and values then stay in L2.
@@ -70,9 +71,15 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
       if (s < n_slots) {
         const Item it = slot_item(p, s);
         if (it.valid) {
-          // sequences with more key blocks first (ties by b), each from its last tile to its first
-          const uint32_t nbs = (uint32_t)min((it.sk + p.bn - 1) / p.bn, kPlanMaxBlocks);
-          key = ((uint32_t)(kPlanMaxBlocks - nbs) << 14) | (uint32_t)(it.b * p.mt + (p.mt - 1 - it.m));
+          if (p.win_left < 0) {
+            // sequences with more key blocks first (ties by b), each from its last tile to its first
+            const uint32_t nbs = (uint32_t)min((it.sk + p.bn - 1) / p.bn, kPlanMaxBlocks);
+            key = ((uint32_t)(kPlanMaxBlocks - nbs) << 14) | (uint32_t)(it.b * p.mt + (p.mt - 1 - it.m));
+          } else {
+            // with a left window: longest item first, ties by slot
+            const uint32_t nb = (uint32_t)min(it.nb, kPlanMaxBlocks);
+            key = ((uint32_t)(kPlanMaxBlocks - nb) << 14) | (uint32_t)s;
+          }
         }
       }
       keys[s] = key;
@@ -105,8 +112,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(PlanParams p) {
     const int count = count_sh;
     for (int i = tid; i < p.capacity; i += nthr) {
       if (i < count) {
-        const int kb = (int)(keys[i] & 0x3FFFu) / p.mt;  // key low bits: b * Mt + (Mt - 1 - m)
-        write_item(p, i, slot_item(p, kb * p.mt + (p.mt - 1 - ((int)(keys[i] & 0x3FFFu) - kb * p.mt))));
+        const int low = (int)(keys[i] & 0x3FFFu);  // b * Mt + (Mt - 1 - m), or the slot with a left window
+        const int kb = low / p.mt;
+        write_item(p, i, slot_item(p, p.win_left < 0 ? kb * p.mt + (p.mt - 1 - (low - kb * p.mt)) : low));
       } else {
         reinterpret_cast<int4*>(p.plan)[i] = make_int4(-1, -1, -1, -1);
       }

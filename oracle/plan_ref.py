@@ -28,7 +28,9 @@ from ``(m, Sq_b, Sk_b, l)``.
 Each item is four int32 words ``(b, m, n_blocks, kv_end)``. Items are ordered sequence by
 sequence, sequences with more key blocks first (``min(ceil(Sk_b / BN), MAX_BLOCKS)`` descending,
 ties by ``b`` ascending), and within a sequence from its last query tile to its first (``m``
-descending). When there are more than ``SORT_CAPACITY`` slots the items stay in slot order.
+descending); with a left window (``l >= 0``) they are ordered longest first instead:
+``n_blocks`` descending, ties by slot ascending. When there are more than ``SORT_CAPACITY``
+slots the items stay in slot order.
 Words past the last item, up to ``capacity`` items, are -1.
 """
 from __future__ import annotations
@@ -64,8 +66,11 @@ def plan_items(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: 
                 kv_end = sk
             kv_start = min(max(m * bm + sk - sq - left, 0), sk) if left >= 0 else 0
             n_blocks = 0 if kv_end <= kv_start else -(-kv_end // bn) - kv_start // bn
-            seq_blocks = min(-(-sk // bn), MAX_BLOCKS)
-            items.append(((-seq_blocks, b, -m), (b, m, n_blocks, kv_end)))
+            if left < 0:
+                order = (-min(-(-sk // bn), MAX_BLOCKS), b, -m)
+            else:
+                order = (-min(n_blocks, MAX_BLOCKS), b * mt + m, 0)
+            items.append((order, (b, m, n_blocks, kv_end)))
     if b_count * mt <= SORT_CAPACITY:
         items.sort(key=lambda it: it[0])
     return [it[1] for it in items]

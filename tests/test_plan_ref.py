@@ -71,6 +71,12 @@ def test_plan_items_window_extent_brute_force(lens_q, lens_k, causal, window, bm
         left = window[0]
         kv_start = min(max(m * bm + sk - sq - left, 0), sk) if left >= 0 else 0
         assert kv_start // bn == lo_blk
+    mt = -(-max(lens_q) // bm)
+    if window[0] >= 0:   # longest first, ties by slot
+        keys = [(-it[2], it[0] * mt + it[1]) for it in items]
+    else:                # sequence by sequence, each from its last tile
+        keys = [(-(-(-lens_k[it[0]] // bn)), it[0], -it[1]) for it in items]
+    assert keys == sorted(keys)
 
 
 def test_plan_buffer_fill_and_capacity():
