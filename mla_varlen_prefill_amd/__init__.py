@@ -188,6 +188,16 @@ def varlen_num_splits(batch: int, max_seqlen_q: int, max_seqlen_k: int, num_head
                                                         int(bool(causal)), num_splits)
 
 
+def _check_out_lse(out, lse, rows: int, heads: int, dv: int, elem: int = 2) -> None:
+    """A caller-supplied output must be [rows, heads, dv] with a contiguous last dim (elements of
+    `elem` bytes) and a caller-supplied LSE float32 [rows, heads]; any other strides are passed on."""
+    if tuple(out.shape) != (rows, heads, dv) or out.stride(-1) != 1 or out.element_size() != elem:
+        raise ValueError(f"out must be a [{rows}, {heads}, {dv}] tensor of {elem}-byte elements with a "
+                         "contiguous last dim")
+    if lse is not None and (lse.dtype != torch.float32 or tuple(lse.shape) != (rows, heads)):
+        raise ValueError(f"lse must be a float32 [{rows}, {heads}] tensor")
+
+
 def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                        cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
                        max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
@@ -225,6 +235,7 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         raise ValueError("out must be float8_e4m3fn with out_scale, else bf16")
     if return_lse and lse is None:
         lse = torch.empty((total_q, heads), dtype=torch.float32, device=q.device)
+    _check_out_lse(out, lse, total_q, heads, dv, 1 if fp8 else 2)
     ws_bytes = lib.mla_prefill_varlen_workspace_size(batch, total_q, max_seqlen_q, max_seqlen_k,
                                                      heads, dv, int(bool(causal)), num_splits)
     if workspace is None:
@@ -288,6 +299,7 @@ def mla_prefill_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
         out = torch.empty((t, heads, dv), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((t, heads), dtype=torch.float32, device=q.device)
+    _check_out_lse(out, lse, t, heads, dv)
     ws_bytes = lib.mla_prefill_sparse_workspace_size(t, heads, topk, dv)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     _check("mla_prefill_sparse", lib.mla_prefill_sparse(
@@ -331,6 +343,7 @@ def mla_prefill_sparse_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_tabl
         out = torch.empty((t, heads, dv), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((t, heads), dtype=torch.float32, device=q.device)
+    _check_out_lse(out, lse, t, heads, dv)
     ws_bytes = lib.mla_prefill_sparse_workspace_size(t, heads, topk, dv)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device) if ws_bytes else None
     _check("mla_prefill_sparse_paged", lib.mla_prefill_sparse_paged(
@@ -370,6 +383,7 @@ def mla_prefill_chunked_context(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
         out = torch.empty((total_q, heads, 128), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
         lse = torch.empty((total_q, heads), dtype=torch.float32, device=q.device)
+    _check_out_lse(out, lse, total_q, heads, 128)
     ws_bytes = lib.mla_prefill_chunked_context_workspace_size(batch, total_q, max_seqlen_q, heads, chunk_tokens)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
@@ -414,6 +428,7 @@ def mla_combine(o_part: torch.Tensor, lse_part: torch.Tensor, num_heads: int,
         out = torch.empty((t, num_heads, dv), dtype=torch.bfloat16, device=o_part.device)
     if return_lse and lse is None:
         lse = torch.empty((t, num_heads), dtype=torch.float32, device=o_part.device)
+    _check_out_lse(out, lse, t, num_heads, dv)
     _check("mla_combine", lib.mla_combine(
         _ptr(o_part), _ptr(lse_part), s, t, num_heads, dv, _ptr(sink),
         _ptr(out), out.stride(0), out.stride(1),

@@ -89,6 +89,38 @@ def test_dense_strided_v_and_no_lse():
     check_parity(o, None, ro, rl, c.name)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+def test_dense_strided_views(splits):
+    """Q, K, the output and the LSE as strided views into larger buffers (Q inside a wider
+    per-head row, K every other head of an interleaved buffer, O inside padded rows, LSE
+    head-major): the result matches the oracle and no byte outside the views changes."""
+    import torch
+    import mla_varlen_prefill_amd as mla
+    c = make_dense(f"views_s{splits}", [200, 77, 513], [260, 77, 513], heads=4, causal=True, seed=35,
+                   with_sink=True)
+    announce(f"dense {c.name}")
+    tq, h, _ = c.q.shape
+    tk = c.k.shape[0]
+    qb = torch.full((tq, h, 256), 5.0, dtype=torch.bfloat16, device="cuda")
+    qb[:, :, 64:] = dev_bf16(c.q)
+    kb = torch.full((tk, 2 * h, 192), -3.0, dtype=torch.bfloat16, device="cuda")
+    kb[:, 1::2] = dev_bf16(c.k)
+    ob = torch.full((tq, h, 160), 9.0, dtype=torch.bfloat16, device="cuda")
+    lb = torch.full((h, tq), 1.5, dtype=torch.float32, device="cuda")
+    q, k, out, lse = qb[:, :, 64:], kb[:, 1::2], ob[:, :, 16:144], lb.t()
+    assert q.stride() == (h * 256, 256, 1) and k.stride() == (2 * h * 192, 384, 1)
+    assert out.stride() == (h * 160, 160, 1) and lse.stride() == (1, tq)
+    mla.mla_prefill_varlen(q, k, dev_bf16(c.v), dev(c.cu_q), dev(c.cu_k), c.max_q, c.max_k, c.scale,
+                           causal=True, num_splits=splits, sink=dev(c.sink), out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = oracle(c)
+    check_parity(host_f64(out), host_f64(lse), ro, rl, c.name)
+    assert torch.all(ob[:, :, :16] == 9.0) and torch.all(ob[:, :, 144:] == 9.0)
+    with pytest.raises(ValueError):
+        mla.mla_prefill_varlen(q, k, dev_bf16(c.v), dev(c.cu_q), dev(c.cu_k), c.max_q, c.max_k, c.scale,
+                               causal=True, out=ob[:, :, :120])
+
+
 @pytest.mark.parametrize("splits", [2, 3, 8])
 @pytest.mark.parametrize("causal", [False, True])
 def test_dense_forced_splits(splits, causal):
