@@ -84,3 +84,33 @@ def test_chunked_context_empty_context_equals_causal_prefill():
     ro, rl = O.dense_mla_prefill(q, k, v, cu_q, cu_q, float(np.float32(192 ** -0.5)), True)
     check_parity(host_f64(o), host_f64(lse), ro, rl, "chunked empty")
     assert torch.allclose(o.float(), o2.float(), atol=1e-2)
+
+
+def test_chunked_context_strided_views():
+    """New-token Q/K/V, the latent cache, the output and the LSE as strided views into larger
+    buffers: the result matches the oracle and no byte outside the output view changes."""
+    import torch
+    import mla_varlen_prefill_amd as mla
+    ctx, new, heads = [150, 0, 70], [4, 9, 33], 4
+    cu_c, cu_q, lat, w, q, k, v, sink = _inputs(ctx, new, heads, 63)
+    announce("chunked context strided views")
+    t, n = int(cu_q[-1]), lat.shape[0]
+    qb = torch.full((t, heads, 256), 3.0, dtype=torch.bfloat16, device="cuda")
+    qb[:, :, 64:] = dev_bf16(q)
+    kb = torch.full((t, 2 * heads, 192), -2.0, dtype=torch.bfloat16, device="cuda")
+    kb[:, ::2] = dev_bf16(k)
+    vb = torch.full((t, heads, 256), 4.0, dtype=torch.bfloat16, device="cuda")
+    vb[:, :, 128:] = dev_bf16(v)
+    lb = torch.full((n, 640), -1.0, dtype=torch.bfloat16, device="cuda")
+    lb[:, 64:] = dev_bf16(lat)
+    ob = torch.full((t, heads, 144), 9.0, dtype=torch.bfloat16, device="cuda")
+    eb = torch.full((heads, t), 1.5, dtype=torch.float32, device="cuda")
+    out, lse = ob[:, :, 16:], eb.t()
+    mla.mla_prefill_chunked_context(qb[:, :, 64:], kb[:, ::2], vb[:, :, 128:], dev(cu_q), lb[:, 64:], dev(cu_c),
+                                    dev_bf16(w), max(new), max(ctx), 192 ** -0.5, chunk_tokens=64,
+                                    sink=dev(sink), out=out, lse=lse)
+    torch.cuda.synchronize()
+    ro, rl = O.mla_prefill_with_latent_context(q, k, v, cu_q, lat, cu_c, w, float(np.float32(192 ** -0.5)),
+                                               sink=sink, heads=list(range(heads)), round_kv_bf16=True)
+    check_parity(host_f64(out), host_f64(lse), ro, rl, "chunked views")
+    assert torch.all(ob[:, :, :16] == 9.0)
