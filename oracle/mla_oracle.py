@@ -48,6 +48,9 @@ Readings taken where the pages are silent (each also listed with the design note
      (block_table[b][p // block_size], p % block_size). A slot is valid iff R9 holds,
      0 <= p < used_b (used_b = seqused[b] if given, else max_blocks * block_size) and the table
      entry lies in [0, num_blocks). A token outside every sequence has no valid slot.
+     ``seqused_q`` (page "Sgl project Sglang FA4 Interface", Signature: the query tokens of each
+     sequence that are in use): token t of sequence b is in use iff t - cu_q[b] < seqused_q[b];
+     a token not in use has no valid slot (so O = 0 and LSE = -inf, or the sink, by R4).
   R18 Sliding window / band mask (page "Sgl project Sglang FA4 Interface", ``window_size`` =
      (left, right), e.g. (256, 0) = causal with a 256-key window; page "SparseFlashMla",
      ``ori_win_left`` / ``ori_win_right``: the number of past / future tokens a query sees, -1 =
@@ -242,9 +245,11 @@ def sparse_mla_prefill(q: np.ndarray, kv: np.ndarray, indices: np.ndarray, scale
 
 def paged_physical_indices(indices: np.ndarray, block_table: np.ndarray, block_size: int,
                            num_blocks: int, cu_q: Sequence[int],
-                           seqused: Optional[Sequence[int]] = None) -> np.ndarray:
+                           seqused: Optional[Sequence[int]] = None,
+                           seqused_q: Optional[Sequence[int]] = None) -> np.ndarray:
     """Logical index rows -> physical cache rows of [num_blocks * block_size] (reading R17);
-    invalid slots become -1. block_table is [B, max_blocks] int32."""
+    invalid slots, and every slot of a token not in use under seqused_q, become -1. block_table
+    is [B, max_blocks] int32."""
     idx = np.asarray(indices, dtype=np.int64)
     bt = np.asarray(block_table, dtype=np.int64)
     n_tok = idx.shape[0]
@@ -252,7 +257,10 @@ def paged_physical_indices(indices: np.ndarray, block_table: np.ndarray, block_s
     max_blocks = bt.shape[1]
     for b in range(len(cu_q) - 1):
         used = max_blocks * block_size if seqused is None else min(int(seqused[b]), max_blocks * block_size)
-        for t in range(int(cu_q[b]), min(int(cu_q[b + 1]), n_tok)):
+        t_end = min(int(cu_q[b + 1]), n_tok)
+        if seqused_q is not None:
+            t_end = min(t_end, int(cu_q[b]) + max(int(seqused_q[b]), 0))
+        for t in range(int(cu_q[b]), t_end):
             for k, pos in enumerate(idx[t]):
                 if 0 <= pos < used:
                     entry = bt[b, pos // block_size]
@@ -266,12 +274,13 @@ def sparse_mla_prefill_paged(q: np.ndarray, kv_cache: np.ndarray, block_table: n
                              seqused: Optional[Sequence[int]] = None,
                              topk_length: Optional[np.ndarray] = None,
                              sink: Optional[np.ndarray] = None,
-                             tokens: Optional[Iterable[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
+                             tokens: Optional[Iterable[int]] = None,
+                             seqused_q: Optional[Sequence[int]] = None) -> Tuple[np.ndarray, np.ndarray]:
     """Sparse top-k attention over a paged latent cache kv_cache [num_blocks, block_size, D]
     with logical indices (reading R17): the indices are mapped to cache rows, then the sparse
     definition applies unchanged."""
     num_blocks, block_size, d = kv_cache.shape
-    phys = paged_physical_indices(indices, block_table, block_size, num_blocks, cu_q, seqused)
+    phys = paged_physical_indices(indices, block_table, block_size, num_blocks, cu_q, seqused, seqused_q)
     rows = np.asarray(kv_cache).reshape(num_blocks * block_size, d)
     return sparse_mla_prefill(q, rows, phys, scale, dv=dv, topk_length=topk_length, sink=sink, tokens=tokens)
 

@@ -3,13 +3,12 @@
 TEST INFRASTRUCTURE ONLY (imported by ``tests/`` and nowhere in the product path). The GPU
 planner must produce exactly these int32 words.
 
-The pages describe a GPU kernel that plans a batch of varying-length sequences through a
-fixed-size buffer, plus a helper that zeroes its length counters (page "Mojo module mla":
-``mla_prefill_plan``, ``mla_prefill_plan_kernel``, ``set_buffer_lengths_to_zero``), and a
-separate metadata call whose fixed-size int32 output is the task split the attention operator
-consumes (page "SparseFlashMla", Description: call ``SparseFlashMlaMetadata`` first, and
-Constraints: ``metadata`` is int32 of fixed size). The page gives no format, so the format
-below is this library's own.
+Prior art on the pages: a device-side planner for ragged batches, with a helper that clears its
+counters (page "Mojo module mla": ``mla_prefill_plan_kernel``, ``set_buffer_lengths_to_zero``),
+and a metadata call run before the attention operator whose int32 output of fixed size holds the
+operator's task table (page "SparseFlashMla", Description: ``SparseFlashMlaMetadata``;
+Constraints: ``metadata``). Neither page gives a format, so the format below is this library's
+own.
 
 Plan format
 -----------

@@ -41,6 +41,45 @@ def test_hand_examples(case):
     np.testing.assert_allclose(lse[fin, 0], want_lse[fin], rtol=0, atol=1e-12)
 
 
+# ---------------------------------------------------------------- bf16 widening
+def _widening_mismatches(widen) -> int:
+    """Codes (of all 65536 bf16 bit patterns) where `widen` differs from PyTorch's own bf16 ->
+    float64 conversion, NaN codes compared as NaN and zeros by sign."""
+    codes = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(codes.view(np.int16)).view(torch.bfloat16).double().numpy()
+    with np.errstate(invalid="ignore"):   # signalling-NaN codes raise the invalid flag when widened
+        got = np.asarray(widen(codes), dtype=np.float64)
+    if got.shape != want.shape:
+        return codes.size
+    same = ((got == want) & (np.signbit(got) == np.signbit(want))) | (np.isnan(got) & np.isnan(want))
+    return int((~same).sum())
+
+
+def test_widen_bf16_matches_torch_on_every_code():
+    """The oracle's entry point for every bf16 input (page "SparseFlashMla", Parameters table:
+    q and the KV are BFLOAT16) agrees with PyTorch's bf16 -> float64 cast on all 65536 codes:
+    normals, subnormals, both zeros, both infinities and every NaN."""
+    assert _widening_mismatches(O.widen_bf16) == 0
+
+
+def test_widen_bf16_pin_rejects_plausible_mistakes():
+    """Planted on the CPU: each of these wrong widenings must fail the pin above."""
+    def wrong_shift(b):
+        return (np.asarray(b, np.uint16).astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+
+    def low_half(b):
+        return np.asarray(b, np.uint16).astype(np.uint32).view(np.float32).astype(np.float64)
+
+    def as_half(b):
+        return np.asarray(b, np.uint16).view(np.float16).astype(np.float64)
+
+    def truncated_to_int(b):
+        return np.trunc(O.widen_bf16(b))
+
+    for bad in (wrong_shift, low_half, as_half, truncated_to_int):
+        assert _widening_mismatches(bad) > 1000, bad.__name__
+
+
 # ---------------------------------------------------------------- library special case
 def _torch_reference(q, k, v, cu_q, cu_k, scale, causal):
     """PyTorch fp64 CPU SDPA with an explicit boolean mask, and logsumexp of the masked logits."""
@@ -482,6 +521,36 @@ def test_paged_seqused_equals_padding_past_the_used_length():
     o2, l2 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx2, 0.5, dv=4)
     np.testing.assert_array_equal(o1, o2)
     np.testing.assert_array_equal(l1, l2)
+
+
+def test_paged_seqused_q_gives_empty_rows_past_the_used_tokens():
+    """seqused_q[b] = u: the first u tokens of sequence b are unchanged, every later token of the
+    sequence is a row with no key (O = 0 and LSE = -inf, or LSE = sink with a sink), exactly as if
+    all its slots were -1 (page "Sgl project Sglang FA4 Interface", Signature: seqused_q)."""
+    rng = np.random.default_rng(41)
+    lens_kv, n_tok, topk, h, d = [9, 6, 5], [3, 2, 2], 6, 2, 6
+    cache, table, cu_q, idx, _ = _paged_case(rng, 4, lens_kv, n_tok, topk, d=d)
+    q = rng.standard_normal((idx.shape[0], h, d))
+    used_q = [1, 2, 0]
+    sink = np.array([0.25, -0.5])
+    for s in (None, sink):
+        o0, l0 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx, 0.5, dv=4, sink=s)
+        o1, l1 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx, 0.5, dv=4, sink=s, seqused_q=used_q)
+        idx2 = idx.copy()
+        for b in range(3):
+            idx2[cu_q[b] + used_q[b]:cu_q[b + 1]] = -1
+        o2, l2 = O.sparse_mla_prefill_paged(q, cache, table, cu_q, idx2, 0.5, dv=4, sink=s)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+        for b in range(3):
+            keep = slice(cu_q[b], cu_q[b] + used_q[b])
+            drop = slice(cu_q[b] + used_q[b], cu_q[b + 1])
+            np.testing.assert_array_equal(o1[keep], o0[keep])
+            np.testing.assert_array_equal(l1[keep], l0[keep])
+            assert np.all(o1[drop] == 0)
+            want = np.full((cu_q[b + 1] - cu_q[b] - used_q[b], h), -math.inf) if s is None else \
+                np.broadcast_to(s, (cu_q[b + 1] - cu_q[b] - used_q[b], h))
+            np.testing.assert_array_equal(l1[drop], want)
 
 
 def test_paged_bad_table_entry_drops_that_block_only():
