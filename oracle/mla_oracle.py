@@ -180,25 +180,29 @@ def dense_mla_prefill_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q: Se
                            sink: Optional[np.ndarray] = None,
                            window: Tuple[int, int] = (-1, -1)) -> Tuple[np.ndarray, np.ndarray]:
     """The same definition evaluated only at the given (token, head) grid: O [n_tok, n_head, Dv],
-    LSE [n_tok, n_head]. Used to check large problems at sampled rows."""
+    LSE [n_tok, n_head]. Used to check large problems at sampled rows. The requested rows of one
+    sequence are scored in one product against that sequence's keys, exactly as
+    ``dense_mla_prefill`` scores a whole sequence; each head's K/V rows of the sequence are
+    widened once."""
     cu_q = np.asarray(cu_q)
     tokens = np.asarray(tokens, dtype=np.int64)
     dv = v.shape[2]
     out = np.zeros((tokens.size, len(heads), dv))
     lse = np.zeros((tokens.size, len(heads)))
-    for ti, t in enumerate(tokens):
-        b = int(np.searchsorted(cu_q, t, side="right") - 1)
+    seq = np.searchsorted(cu_q, tokens, side="right") - 1
+    for b in np.unique(seq):
+        sel = np.nonzero(seq == b)[0]
         q0, k0, k1 = int(cu_q[b]), int(cu_k[b]), int(cu_k[b + 1])
         sq, sk = int(cu_q[b + 1]) - q0, k1 - k0
-        i = int(t) - q0
-        vis = dense_visible(sq, sk, causal, rows=np.array([i]), window=window)
+        local = tokens[sel] - q0
+        vis = dense_visible(sq, sk, causal, rows=local, window=window)
         for hi, h in enumerate(heads):
-            qrow = _as_f64(q[t, h, :])[None, :]
-            scores = scale * (qrow @ _as_f64(k[k0:k1, h, :]).T)
+            qrows = _as_f64(q[tokens[sel], h, :])
+            scores = scale * (qrows @ _as_f64(k[k0:k1, h, :]).T)
             s = None if sink is None else float(sink[h])
             o, l = _softmax_rows(scores, vis, _as_f64(v[k0:k1, h, :]), s)
-            out[ti, hi] = o[0]
-            lse[ti, hi] = l[0]
+            out[sel, hi] = o
+            lse[sel, hi] = l
     return out, lse
 
 

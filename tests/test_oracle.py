@@ -614,6 +614,22 @@ def test_rows_helper_matches_full():
     np.testing.assert_allclose(rl, lse[np.ix_(toks, heads)], atol=1e-13)
 
 
+@pytest.mark.parametrize("causal,window", [(True, (-1, -1)), (False, (-1, -1)), (False, (4, 2)), (True, (3, -1))])
+def test_rows_helper_any_order_and_duplicates(causal, window):
+    """Rows requested out of order, repeated and from several sequences (one with Sq > Sk, so some
+    rows see no key) give the full evaluation's rows, for every mask rule."""
+    c = make_dense("t", [9, 20, 6], [15, 20, 3], heads=3, causal=causal, seed=25, dqk=16, dv=8,
+                   with_sink=True)
+    o, lse = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, sink=c.sink, window=window)
+    toks, heads = [33, 0, 12, 8, 12, 30, 29, 9], [2, 0]
+    ro, rl = O.dense_mla_prefill_rows(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, causal, toks, heads,
+                                      sink=c.sink, window=window)
+    np.testing.assert_allclose(ro, o[np.ix_(toks, heads)], atol=1e-13)
+    np.testing.assert_array_equal(np.isinf(rl), np.isinf(lse[np.ix_(toks, heads)]))
+    fin = np.isfinite(rl)
+    np.testing.assert_allclose(rl[fin], lse[np.ix_(toks, heads)][fin], atol=1e-13)
+
+
 def test_bf16_rounding_is_round_to_nearest_even():
     x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, -2.5, 3.0e38], dtype=np.float32)
     bits = f32_to_bf16_bits(x)
