@@ -143,9 +143,10 @@ def warm_cold(step, reps: int):
 
 
 def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_splits=0, window=None,
-                      dqk=DQK, dv=DV, fp8_out=False):
+                      dqk=DQK, dv=DV, fp8_out=False, cpu_budget=0.0):
     """One dense workload timed through the C ABI; (dqk, dv) picks the head layout and fp8_out the
-    FP8 output (static scale 2^-8)."""
+    FP8 output (static scale 2^-8). With cpu_budget > 0 the oracle is timed on a sample of the
+    same inputs (cpu_rows_baseline) after the GPU measurements."""
     import torch
     import mla_varlen_prefill_amd as mla
     from workloads import device_dense
@@ -169,7 +170,11 @@ def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_spli
     wc = warm_cold(step, max(3, min(steps, 7)))
     fl = dense_flops(lens_q, lens_k, heads, True, window if window is not None else (-1, -1), dqk, dv)
     by = dense_bytes(lens_q, lens_k, heads, True, dqk, dv, 1 if fp8_out else 2)
-    splits = mla.varlen_num_splits(len(lens_q), max_q, max_k, heads, True, num_splits)
+    splits = mla.varlen_num_splits(len(lens_q), max_q, max_k, heads, True, num_splits, dqk, dv)
+    cpu = None
+    if cpu_budget > 0:
+        cpu = cpu_rows_baseline(q, k, v, cu_q.cpu().numpy(), cu_k.cpu().numpy(), lens_q, lens_k, scale,
+                                cpu_budget)
     del q, k, v, out, lse, ws, out_scale
     torch.cuda.empty_cache()
     res = {"workload": name, "ms_per_call": round(ms, 4), "dense_kernel_ms": round(kms, 4),
@@ -179,6 +184,8 @@ def dense_device_case(name, lens_q, lens_k, heads, seed, steps, warmup, num_spli
            "per_call": wc}
     if CALIB:
         res["frac_measured_mfma"] = round(fl / kms / 1e9 / CALIB["mfma_loop_tflops"], 4)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
@@ -190,7 +197,7 @@ def dense_varlen_variant(name, steps, warmup, **kw):
     return dense_device_case(name, lens, lens, 128, 2, steps, warmup, **kw)
 
 
-def sparse_case(steps, warmup):
+def sparse_case(steps, warmup, cpu_budget=0.0):
     import torch
     import mla_varlen_prefill_amd as mla
     from workloads import device_sparse
@@ -209,6 +216,7 @@ def sparse_case(steps, warmup):
     valid = int(((idx_host >= 0) & (idx_host < n_kv)).sum())
     fl = sparse_flops(valid, h)
     by = sparse_bytes(valid, t, h, topk)
+    cpu = cpu_sparse_baseline(q, kv, idx_host, sink, scale, cpu_budget) if cpu_budget > 0 else None
     del q, kv, idx, out, lse
     torch.cuda.empty_cache()
     res = {"workload": "sparse_t4096_h128_topk2048_pool65536", "ms_per_call": round(ms, 4),
@@ -219,6 +227,8 @@ def sparse_case(steps, warmup):
     res["traffic"] = measured_traffic("sparse_fwd_t4096_h128_topk2048_traffic.json", "sparse_fwd.hip")
     if CALIB:
         res["frac_measured_stream_read"] = round(by / kms / 1e6 / CALIB["stream_read_gbps"], 4)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     return res
 
 
@@ -299,28 +309,98 @@ def sparse_paged_case(steps, warmup, block_size=64):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
-def cpu_baseline(case, budget_s: float):
-    """The fp64 oracle, as it stands, on heads 0, 1, ... of the headline batch until the budget."""
-    from oracle import mla_oracle as O
+def oracle_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
-        threads = os.cpu_count() or 1
-    lens = list(map(int, (case.cu_q[1:] - case.cu_q[:-1])))
+        return os.cpu_count() or 1
+
+
+def cpu_baseline(q, k, v, lens, scale, budget_s: float):
+    """The fp64 oracle, as it stands, on heads 0, 1, ... of the headline batch (all sequences,
+    all rows) until the budget is spent. q/k/v are the device inputs; each head is copied to the
+    host as bf16 bits before it is timed."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    from workloads import bf16_tensor_to_bits, cu_from_lens
+    cu = cu_from_lens(lens)
+    heads = q.shape[1]
     per_head = dense_flops(lens, lens, 1, True)
-    done = 0
-    t0 = time.perf_counter()
-    while done < case.heads:
-        O.dense_mla_prefill(case.q, case.k, case.v, case.cu_q, case.cu_k, case.scale, True, heads=[done])
+    done, el = 0, 0.0
+    while done < heads and el < budget_s:
+        qh, kh, vh = (bf16_tensor_to_bits(x[:, done:done + 1, :]) for x in (q, k, v))
+        t0 = time.perf_counter()
+        O.dense_mla_prefill(qh, kh, vh, cu, cu, scale, True)
+        el += time.perf_counter() - t0
         done += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    el = time.perf_counter() - t0
-    return {"value": round(per_head * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(threads),
+    return {"value": round(per_head * done / el / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(),
             "kind": "oracle",
-            "sample": f"heads 0..{done - 1} of {case.heads} of the headline batch (all 8 sequences, "
-                      f"all rows), {el:.1f} s wall, fp64 numpy"}
+            "sample": f"heads 0..{done - 1} of {heads} of the headline batch (all 8 sequences, all rows), "
+                      f"{el:.1f} s of oracle time, fp64 numpy"}
+
+
+def cpu_rows_baseline(q, k, v, cu_q, cu_k, lens_q, lens_k, scale, budget_s: float, head: int = 0):
+    """The fp64 oracle's row evaluator on one head of a large dense workload: query rows spread
+    evenly over every sequence, timed until the budget is spent. The rate counts the algorithmic
+    work of the rows done (their visible keys x 640 FLOP); the full workload's oracle time is that
+    work extrapolated at the measured rate."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    from workloads import bf16_tensor_to_bits
+    cq, ck = np.asarray(cu_q), np.asarray(cu_k)
+    qh, kh, vh = (bf16_tensor_to_bits(x[:, head:head + 1, :]) for x in (q, k, v))
+    rng = np.random.default_rng(0)
+    order = rng.permutation(int(cq[-1]))
+    fl_done, el, n = 0.0, 0.0, 0
+    for t in order:
+        b = int(np.searchsorted(cq, t, side="right") - 1)
+        sq, sk = int(cq[b + 1] - cq[b]), int(ck[b + 1] - ck[b])
+        i = int(t) - int(cq[b])
+        t0 = time.perf_counter()
+        O.dense_mla_prefill_rows(qh, kh, vh, cq, ck, scale, True, [int(t)], [0])
+        el += time.perf_counter() - t0
+        fl_done += 2.0 * (qh.shape[2] + vh.shape[2]) * max(0, min(sk, i + sk - sq + 1))
+        n += 1
+        if el >= budget_s:
+            break
+    rate = fl_done / el
+    total = dense_flops(lens_q, lens_k, q.shape[1], True)
+    return {"value": round(rate / 1e12, 6), "unit": "TFLOP/s", "cores": oracle_threads(), "kind": "oracle",
+            "extrapolated_full_s": round(total / rate, 1),
+            "sample": f"{n} random query rows of head {head} (of {q.shape[1]}), {el:.1f} s of oracle time, "
+                      f"fp64 numpy; full-workload time extrapolated at that rate"}
+
+
+def cpu_sparse_baseline(q, kv, idx_host, sink, scale, budget_s: float):
+    """The fp64 sparse oracle on random tokens of the sparse workload (all 128 heads each), until
+    the budget is spent; rate in algorithmic TFLOP/s and GB/s of the sample."""
+    import numpy as np
+    from oracle import mla_oracle as O
+    from workloads import bf16_tensor_to_bits
+    kvh = bf16_tensor_to_bits(kv)
+    sink_h = sink.cpu().numpy()
+    n_kv = kvh.shape[0]
+    t_all, heads = q.shape[0], q.shape[1]
+    order = np.random.default_rng(0).permutation(t_all)
+    el, n, valid = 0.0, 0, 0
+    for t in order:
+        qt = bf16_tensor_to_bits(q[int(t):int(t) + 1])
+        it = idx_host[int(t):int(t) + 1]
+        t0 = time.perf_counter()
+        O.sparse_mla_prefill(qt, kvh, it, scale, dv=SP_DV, sink=sink_h)
+        el += time.perf_counter() - t0
+        valid += int(((it >= 0) & (it < n_kv)).sum())
+        n += 1
+        if el >= budget_s:
+            break
+    fl = sparse_flops(valid, heads)
+    by = sparse_bytes(valid, n, heads, idx_host.shape[1])
+    all_valid = int(((idx_host >= 0) & (idx_host < n_kv)).sum())
+    return {"value": round(fl / el / 1e12, 6), "unit": "TFLOP/s", "alg_gbps": round(by / el / 1e9, 3),
+            "cores": oracle_threads(), "kind": "oracle",
+            "extrapolated_full_s": round(sparse_flops(all_valid, heads) / (fl / el), 1),
+            "sample": f"{n} random tokens of {t_all} (all {heads} heads), {el:.1f} s of oracle time, fp64 numpy"}
 
 
 # ----------------------------------------------------------------------------- traffic
@@ -349,7 +429,11 @@ def main():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-calib", action="store_true",
                     help="skip measuring this device's MFMA-loop and streaming-read rates")
-    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work")
+    ap.add_argument("--cpu-budget", type=float, default=10.0,
+                    help="seconds of oracle work on the headline batch")
+    ap.add_argument("--cpu-budget-secondary", type=float, default=4.0,
+                    help="seconds of oracle work on each of the 128-token, long-context, chunked-prefill "
+                         "and sparse workloads")
     ap.add_argument("--only", default=None,
                     help="run one workload and print its line: dense_varlen, dense_long, dense_chunked, "
                          "dense_small, dense_window, dense_dims128, dense_dims256, dense_fp8, chunked_context, "
@@ -364,7 +448,6 @@ def main():
     import numpy as np
     import torch
     import mla_varlen_prefill_amd as mla
-    from workloads import dense_varlen
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -414,28 +497,27 @@ def main():
         print(json.dumps(sec_runs[args.only]()), flush=True)
         return
 
-    # ---------------- headline: dense varlen batch of 8, lengths in [64, 2048], 128 heads
-    case = dense_varlen()
-    lens = list(map(int, (case.cu_q[1:] - case.cu_q[:-1])))
-    heads = case.heads
-
-    def to_dev(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda").view(torch.bfloat16)
-
-    q, k, v = to_dev(case.q), to_dev(case.k), to_dev(case.v)
-    cu_q = torch.from_numpy(case.cu_q).cuda()
-    cu_k = torch.from_numpy(case.cu_k).cuda()
-    max_q, max_k = case.max_q, case.max_k
+    # ---------------- headline: dense varlen batch of 8, lengths in [64, 2048], 128 heads. The
+    # inputs are drawn on the device (no host-side generation just before the timing), and the
+    # step is run back to back for ~100 ms before the warm-up steps, so that the timed steps
+    # start from settled clocks whatever --warmup is.
+    from workloads import device_dense, varlen_lens
+    lens = varlen_lens(2, 8, 64, 2048)
+    heads, batch = 128, len(lens)
+    q, k, v, cu_q, cu_k = device_dense(lens, lens, heads, 2)
+    max_q = max_k = max(lens)
+    scale = float(np.float32(DQK ** -0.5))
     out = torch.empty((q.shape[0], heads, DV), dtype=torch.bfloat16, device="cuda")
     lse = torch.empty((q.shape[0], heads), dtype=torch.float32, device="cuda")
-    ws_bytes = mla.varlen_workspace_bytes(case.batch, q.shape[0], max_q, max_k, heads, True, 0)
+    ws_bytes = mla.varlen_workspace_bytes(batch, q.shape[0], max_q, max_k, heads, True, 0)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
-    splits = mla.varlen_num_splits(case.batch, max_q, max_k, heads, True, 0)
+    splits = mla.varlen_num_splits(batch, max_q, max_k, heads, True, 0)
 
     def step():
-        mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max_q, max_k, case.scale, causal=True,
+        mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max_q, max_k, scale, causal=True,
                                num_splits=0, out=out, lse=lse, workspace=ws)
 
+    settle(step)
     ms, dense_kernel_ms, launches = time_steps(step, args.steps, args.warmup, "dense")
     per_call = warm_cold(step, max(3, min(args.steps, 11)))
     flops = dense_flops(lens, lens, heads, True)
@@ -455,7 +537,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "dense_varlen_b8_h128_causal_lse", "batch": case.batch, "seq_lens": lens,
+        "config": {"workload": "dense_varlen_b8_h128_causal_lse", "batch": batch, "seq_lens": lens,
                    "heads": heads, "head_dim_qk": DQK, "head_dim_v": DV, "causal": True, "lse": True,
                    "num_splits": splits, "algorithmic_flop_per_step": flops,
                    "frac_bf16_peak": round(value / PEAK_BF16_TFLOPS, 4)},
@@ -468,16 +550,19 @@ def main():
     }
     if CALIB:
         result["roofline"]["frac_measured_mfma"] = round(achieved / CALIB["mfma_loop_tflops"], 4)
+    result["cpu_baseline"] = None if args.no_cpu else cpu_baseline(q, k, v, lens, scale, args.cpu_budget)
     del q, k, v, out, lse, ws
     torch.cuda.empty_cache()
 
     if not args.no_secondary:
         sec = []
         ss, sw = max(2, min(args.steps, 5)), 2
-        sec.append(dense_device_case("dense_small_1x128_h16", [128], [128], 16, 1, args.steps, args.warmup))
-        sec.append(dense_device_case("dense_long_1x32768_h128", [32768], [32768], 128, 3, ss, sw))
+        cb = 0.0 if args.no_cpu else args.cpu_budget_secondary
+        sec.append(dense_device_case("dense_small_1x128_h16", [128], [128], 16, 1, args.steps, args.warmup,
+                                     cpu_budget=cb))
+        sec.append(dense_device_case("dense_long_1x32768_h128", [32768], [32768], 128, 3, ss, sw, cpu_budget=cb))
         sec.append(dense_device_case("dense_chunked_b4_q2048", [2048] * 4, [16384, 12345, 8191, 4097],
-                                     128, 4, ss, sw))
+                                     128, 4, ss, sw, cpu_budget=cb))
         sec.append(dense_device_case("dense_window_1x32768_h128_w4096", [32768], [32768], 128, 3, ss, sw,
                                      window=(4096, -1)))
         for name, kw in (("dense_varlen_b8_h128_qk128_v128", dict(dqk=128, dv=128)),
@@ -485,14 +570,10 @@ def main():
                          ("dense_varlen_b8_h128_fp8_out", dict(fp8_out=True))):
             sec.append(dense_varlen_variant(name, max(5, min(args.steps, 50)), 10, **kw))
         sec.append(chunked_context_case(ss, sw))
-        sec.append(sparse_case(ss, sw))
+        sec.append(sparse_case(ss, sw, cpu_budget=cb))
         sec.append(sparse_paged_case(ss, sw))
         result["secondary"] = sec
 
-    if not args.no_cpu:
-        result["cpu_baseline"] = cpu_baseline(case, args.cpu_budget)
-    else:
-        result["cpu_baseline"] = None
     print(json.dumps(result), flush=True)
 
 

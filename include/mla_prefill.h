@@ -17,6 +17,9 @@
  *    gets O = 0 and LSE = -inf (LSE = sink when a sink is given).
  *  - `sink` (nullable) is one float32 logit per head, used as-is (not scaled) as an extra key
  *    whose value vector is zero.
+ *  - `softmax_scale` must be finite and > 0 (the kernels track the running maximum of the raw
+ *    logits, which is the maximum of the scaled ones only for a positive scale); any other value
+ *    returns MLA_ERR_INVALID_ARG.
  *  - Errors are returned as mla_status_t; nothing is launched when a call returns an error.
  *    Per-element contents (cu_seqlens values, index values) are not validated by default:
  *    out-of-range sparse indices are skipped, which is memory-safe; malformed cu_seqlens are the
@@ -61,11 +64,18 @@ void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n);
 /* ------------------------------------------------------------------------------------------
  * Varlen tile plan (GPU kernel, no host synchronisation).
  *
- * Prior art: a GPU kernel that plans a batch of varying-length sequences through a fixed-size
- * buffer, and a helper that zeroes its length counters (page "Mojo module mla",
- * mla_prefill_plan / mla_prefill_plan_kernel / set_buffer_lengths_to_zero); a separate metadata
- * call producing the fixed-size int32 task split of the attention operator (page
- * "SparseFlashMla", Description and Constraints, SparseFlashMlaMetadata / metadata).
+ * Prior art: a device-side planner for ragged batches with a helper that clears its counters
+ * (page "Mojo module mla", mla_prefill_plan_kernel, set_buffer_lengths_to_zero), and a metadata
+ * call run before the attention operator that fills a fixed-size int32 task table (page
+ * "SparseFlashMla", Description and Constraints, SparseFlashMlaMetadata).
+ *
+ * It is the planner mla_prefill_varlen itself runs, exposed so that its bytes can be checked.
+ * It takes the tile sizes and the window instead of max_seqlen_k and num_splits: the items
+ * depend on the tile height, the key block and the mask (a window changes n_blocks and the
+ * order), not on the key-length bound or the split count. The split is not a planned field:
+ * the attention kernel divides an item's n_blocks key blocks into the call's S contiguous
+ * ranges itself (split s takes blocks [s*n/S, (s+1)*n/S)), so one plan serves every split
+ * count.
  *
  * Slots are (b, m) for b < batch and m < Mt = ceil(max_seqlen_q / block_m); slot (b, m) is an
  * item iff m * block_m < Sq_b. Each item is four int32 words (b, m, n_blocks, kv_end): kv_end is
@@ -214,9 +224,13 @@ mla_status_t mla_prefill_varlen_fp8(
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* The number of key splits mla_prefill_varlen uses for these arguments (resolves num_splits=0). */
+/* The number of key splits mla_prefill_varlen (and its window and FP8 variants) uses for these
+ * arguments: num_splits itself when >= 1, else the library heuristic's choice for the kernel
+ * instance of (head_dim_qk, head_dim_v), with the same tile height and residency the call uses.
+ * Returns -1 for num_splits outside [0, 64] or head dims that are not built. */
 int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                      int32_t num_heads, int32_t causal, int32_t num_splits);
+                                      int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                                      int32_t causal, int32_t num_splits);
 
 /* ------------------------------------------------------------------------------------------
  * Sparse top-k MLA prefill over one shared latent KV (absorbed MLA, KV_N = 1).
@@ -273,12 +287,18 @@ mla_status_t mla_prefill_sparse(
  *                 sequence b with cu[b] <= t < cu[b + 1].
  *   seqused_kv  : nullable device int32 [batch]; the number of valid logical positions of each
  *                 sequence (default: max_blocks_per_seq * block_size).
+ *   seqused_q   : nullable device int32 [batch]; the number of query tokens of each sequence
+ *                 that are in use (page "Sgl project Sglang FA4 Interface", Signature:
+ *                 seqused_q). Token t of sequence b is in use iff t - cu[b] < seqused_q[b];
+ *                 a token not in use is written as a row without keys (O = 0, LSE = -inf, or
+ *                 the sink). Default: every token of [cu[b], cu[b + 1]).
  *   indices     : int32 [num_tokens, topk] logical positions, row stride idx_stride_tok.
  * Slot s of token t takes part iff s < topk_length[t] (when given), 0 <= pos < min(seqused[b],
  * max_blocks_per_seq * block_size) and 0 <= block_table[b][pos / block_size] < num_blocks; it
  * then reads cache row block_table[b][pos / block_size] * block_size + pos % block_size. Any
  * other slot (-1, past the used length, a bad table entry) is skipped, which is memory-safe.
- * A token outside every sequence gets O = 0 and LSE = -inf (or the sink). Other arguments,
+ * A token outside every sequence, or not in use under seqused_q, gets O = 0 and LSE = -inf
+ * (or the sink). Other arguments,
  * outputs and ownership as for mla_prefill_sparse.
  * Errors: INVALID_ARG (null block_table or cu_seqlens_q, batch, num_blocks, block_size or
  * max_blocks_per_seq <= 0, bt_stride_seq < max_blocks_per_seq, and the mla_prefill_sparse
@@ -292,6 +312,7 @@ mla_status_t mla_prefill_sparse_paged(
     const void* kv_cache, int64_t kv_stride_row, int32_t num_blocks, int32_t block_size,
     const int32_t* block_table, int64_t bt_stride_seq, int32_t max_blocks_per_seq,
     const int32_t* cu_seqlens_q, int32_t batch, const int32_t* seqused_kv,
+    const int32_t* seqused_q,
     const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
     const int32_t* topk_length,
     int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,

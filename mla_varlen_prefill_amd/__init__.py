@@ -27,7 +27,9 @@ from typing import Optional, Tuple
 import torch
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG_DIR, "libmla_prefill.so")
+# The in-tree build; MLA_PREFILL_LIBRARY may name another build of the same sources (the
+# host-AddressSanitizer build the CPU tests load).
+LIB_PATH = os.environ.get("MLA_PREFILL_LIBRARY") or os.path.join(_PKG_DIR, "libmla_prefill.so")
 
 MLA_OK = 0
 STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
@@ -75,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_prefill_varlen_workspace_size.restype = _c_sz
     lib.mla_prefill_varlen_workspace_size.argtypes = [_c_i32] * 8
     lib.mla_prefill_varlen_num_splits.restype = _c_i32
-    lib.mla_prefill_varlen_num_splits.argtypes = [_c_i32] * 6
+    lib.mla_prefill_varlen_num_splits.argtypes = [_c_i32] * 8
     lib.mla_prefill_varlen.restype = ctypes.c_int
     lib.mla_prefill_varlen.argtypes = [
         _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
@@ -102,7 +104,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         _vp, _c_sz, _vp]
     lib.mla_prefill_sparse_paged.restype = ctypes.c_int
     lib.mla_prefill_sparse_paged.argtypes = [
-        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i32, _c_i32, _vp, _c_i64, _c_i32, _vp, _c_i32, _vp,
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i32, _c_i32, _vp, _c_i64, _c_i32, _vp, _c_i32, _vp, _vp,
         _vp, _c_i64, _c_i32, _vp,
         _c_i32, _c_i32, _c_i32, _c_i32, _c_f32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64,
         _vp, _c_sz, _vp]
@@ -148,6 +150,39 @@ def _require_cuda(*ts) -> None:
             raise ValueError("all tensors must be on the GPU")
 
 
+# Shape and dtype checks, run before anything touches the device: every tensor the kernels read
+# is checked against the sizes passed to the C ABI, so that a short or mistyped tensor is an
+# error here rather than an out-of-bounds read on the GPU.
+def _int32_vec(name: str, t: Optional[torch.Tensor], n: int) -> None:
+    if t is None:
+        return
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous int32 vector")
+    if t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements, got {t.numel()}")
+
+
+def _f32_vec(name: str, t: Optional[torch.Tensor], n: int) -> None:
+    if t is None:
+        return
+    if t.dtype != torch.float32 or t.dim() != 1 or not t.is_contiguous():
+        raise ValueError(f"{name} must be a contiguous float32 vector")
+    if t.numel() != n:
+        raise ValueError(f"{name} must have {n} elements, got {t.numel()}")
+
+
+def _bf16(name: str, t: torch.Tensor, dims: int) -> None:
+    if t.dtype != torch.bfloat16 or t.dim() != dims or t.stride(-1) != 1:
+        raise ValueError(f"{name} must be a bf16 tensor of {dims} dims with a contiguous last dim")
+
+
+def _cu_batch(name: str, t: torch.Tensor) -> int:
+    """Batch size B of a cu_seqlens tensor (int32 [B + 1])."""
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.numel() < 1:
+        raise ValueError(f"{name} must be a contiguous int32 [batch + 1] tensor")
+    return t.numel() - 1
+
+
 def dense_tile_shape() -> Tuple[int, int]:
     lib = load_library()
     bm, bn = _c_i32(), _c_i32()
@@ -161,11 +196,12 @@ def mla_prefill_plan(cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor, max
                      window: Tuple[int, int] = (-1, -1)) -> Tuple[torch.Tensor, torch.Tensor]:
     """Run the GPU planner; returns (plan int32 [capacity, 4], num_items int32 [1])."""
     lib = load_library()
+    batch = _cu_batch("cu_seqlens_q", cu_seqlens_q)
+    _int32_vec("cu_seqlens_k", cu_seqlens_k, batch + 1)
     _require_cuda(cu_seqlens_q, cu_seqlens_k)
     bm0, bn0 = dense_tile_shape()
     bm = bm0 if block_m is None else block_m
     bn = bn0 if block_n is None else block_n
-    batch = cu_seqlens_q.numel() - 1
     mt = -(-max_seqlen_q // bm) if max_seqlen_q > 0 else 0
     cap = batch * mt if capacity is None else capacity
     plan = torch.empty((max(cap, 1), 4), dtype=torch.int32, device=cu_seqlens_q.device)
@@ -183,9 +219,10 @@ def varlen_workspace_bytes(batch: int, total_q: int, max_seqlen_q: int, max_seql
 
 
 def varlen_num_splits(batch: int, max_seqlen_q: int, max_seqlen_k: int, num_heads: int,
-                      causal: bool, num_splits: int = 0) -> int:
+                      causal: bool, num_splits: int = 0, head_dim_qk: int = 192, head_dim_v: int = 128) -> int:
+    """The key-split count mla_prefill_varlen uses for these arguments and head layout."""
     return load_library().mla_prefill_varlen_num_splits(batch, max_seqlen_q, max_seqlen_k, num_heads,
-                                                        int(bool(causal)), num_splits)
+                                                        head_dim_qk, head_dim_v, int(bool(causal)), num_splits)
 
 
 def _check_out_lse(out, lse, rows: int, heads: int, dv: int, elem: int = 2) -> None:
@@ -214,20 +251,21 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     output is FP8 e4m3 of O / out_scale through mla_prefill_varlen_fp8. Returns out [Tq,H,Dv]
     (bf16, or float8_e4m3fn) and, when ``return_lse``, lse float32 [Tq,H]."""
     lib = load_library()
-    _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, sink, out, lse, workspace)
     for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or t.dim() != 3 or t.stride(-1) != 1:
-            raise ValueError(f"{name} must be a bf16 [tokens, heads, dim] tensor with a contiguous last dim")
-    if cu_seqlens_q.dtype != torch.int32 or cu_seqlens_k.dtype != torch.int32:
-        raise ValueError("cu_seqlens must be int32")
+        _bf16(name, t, 3)
     total_q, heads, dqk = q.shape
     dv = v.shape[2]
-    batch = cu_seqlens_q.numel() - 1
+    if tuple(k.shape[1:]) != (heads, dqk):
+        raise ValueError(f"k must be [tokens, {heads}, {dqk}] like q, got {tuple(k.shape)}")
+    if v.shape[0] != k.shape[0] or v.shape[1] != heads:
+        raise ValueError(f"v must be [{k.shape[0]}, {heads}, dv] like k, got {tuple(v.shape)}")
+    batch = _cu_batch("cu_seqlens_q", cu_seqlens_q)
+    _int32_vec("cu_seqlens_k", cu_seqlens_k, batch + 1)
+    _f32_vec("sink", sink, heads)
     fp8 = out_scale is not None
     if fp8:
-        _require_cuda(out_scale)
-        if out_scale.dtype != torch.float32 or out_scale.numel() != 1:
-            raise ValueError("out_scale must be a float32 tensor of one element")
+        _f32_vec("out_scale", out_scale, 1)
+    _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, sink, out, lse, workspace, out_scale)
     if out is None:
         out = torch.empty((total_q, heads, dv), dtype=torch.float8_e4m3fn if fp8 else torch.bfloat16,
                           device=q.device)
@@ -240,8 +278,6 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                                      heads, dv, int(bool(causal)), num_splits)
     if workspace is None:
         workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
-    if sink is not None and (sink.dtype != torch.float32 or not sink.is_contiguous()):
-        raise ValueError("sink must be a contiguous float32 [H] tensor")
     head = (_ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1),
             _ptr(v), v.stride(0), v.stride(1), _ptr(cu_seqlens_q), _ptr(cu_seqlens_k),
             batch, total_q, max_seqlen_q, max_seqlen_k, heads, dqk, dv,
@@ -288,13 +324,17 @@ def mla_prefill_sparse(q: torch.Tensor, kv: torch.Tensor, indices: torch.Tensor,
     """Sparse top-k MLA prefill. q [T,H,576] bf16, kv [N,576] bf16, indices int32 [T, topk]
     (physical rows, -1 = padded). Returns out [T,H,512] bf16 (and lse float32 [T,H])."""
     lib = load_library()
-    _require_cuda(q, kv, indices, topk_length, sink, out, lse)
-    if q.dtype != torch.bfloat16 or kv.dtype != torch.bfloat16 or q.stride(-1) != 1 or kv.stride(-1) != 1:
-        raise ValueError("q and kv must be bf16 with a contiguous last dim")
-    if indices.dtype != torch.int32 or indices.stride(-1) != 1:
-        raise ValueError("indices must be int32 [T, topk] with a contiguous last dim")
+    _bf16("q", q, 3)
+    _bf16("kv", kv, 2)
     t, heads, dqk = q.shape
+    if kv.shape[1] != dqk:
+        raise ValueError(f"kv must be [n_kv, {dqk}] like q's head, got {tuple(kv.shape)}")
+    if indices.dtype != torch.int32 or indices.dim() != 2 or indices.stride(-1) != 1 or indices.shape[0] != t:
+        raise ValueError(f"indices must be int32 [{t}, topk] with a contiguous last dim")
     topk = indices.shape[1]
+    _int32_vec("topk_length", topk_length, t)
+    _f32_vec("sink", sink, heads)
+    _require_cuda(q, kv, indices, topk_length, sink, out, lse)
     if out is None:
         out = torch.empty((t, heads, dv), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
@@ -318,27 +358,32 @@ def mla_prefill_sparse_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_tabl
                              topk_length: Optional[torch.Tensor] = None,
                              sink: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
                              return_lse: bool = True, lse: Optional[torch.Tensor] = None,
-                             dv: int = 512):
+                             dv: int = 512, seqused_q: Optional[torch.Tensor] = None):
     """Sparse top-k MLA prefill over a paged latent cache. kv_cache bf16 [num_blocks, block_size,
     576] (contiguous rows), block_table int32 [B, max_blocks], cu_seqlens_q int32 [B+1], indices
     int32 [T, topk] logical positions of each token's sequence (-1 = padded), seqused_kv int32
-    [B] or None. Returns out [T,H,512] bf16 (and lse float32 [T,H])."""
+    [B] or None (valid KV positions per sequence), seqused_q int32 [B] or None (query tokens in
+    use per sequence). Returns out [T,H,512] bf16 (and lse float32 [T,H])."""
     lib = load_library()
-    _require_cuda(q, kv_cache, block_table, cu_seqlens_q, indices, seqused_kv, topk_length, sink, out, lse)
-    if q.dtype != torch.bfloat16 or kv_cache.dtype != torch.bfloat16 or q.stride(-1) != 1:
-        raise ValueError("q and kv_cache must be bf16 with a contiguous last dim")
-    if kv_cache.dim() != 3 or kv_cache.stride(2) != 1 or kv_cache.stride(0) != kv_cache.shape[1] * kv_cache.stride(1):
-        raise ValueError("kv_cache must be [num_blocks, block_size, 576] with rows of one stride")
-    for name, x in (("indices", indices), ("block_table", block_table), ("cu_seqlens_q", cu_seqlens_q),
-                    ("seqused_kv", seqused_kv)):
-        if x is not None and (x.dtype != torch.int32 or x.stride(-1) != 1):
-            raise ValueError(f"{name} must be int32 with a contiguous last dim")
+    _bf16("q", q, 3)
+    _bf16("kv_cache", kv_cache, 3)
     t, heads, dqk = q.shape
+    if kv_cache.shape[2] != dqk or kv_cache.stride(0) != kv_cache.shape[1] * kv_cache.stride(1):
+        raise ValueError(f"kv_cache must be [num_blocks, block_size, {dqk}] with rows of one stride")
+    if indices.dtype != torch.int32 or indices.dim() != 2 or indices.stride(-1) != 1 or indices.shape[0] != t:
+        raise ValueError(f"indices must be int32 [{t}, topk] with a contiguous last dim")
+    batch = _cu_batch("cu_seqlens_q", cu_seqlens_q)
+    if (block_table.dtype != torch.int32 or block_table.dim() != 2 or block_table.stride(-1) != 1
+            or block_table.shape[0] != batch):
+        raise ValueError(f"block_table must be int32 [{batch}, max_blocks] with a contiguous last dim")
+    _int32_vec("seqused_kv", seqused_kv, batch)
+    _int32_vec("seqused_q", seqused_q, batch)
+    _int32_vec("topk_length", topk_length, t)
+    _f32_vec("sink", sink, heads)
+    _require_cuda(q, kv_cache, block_table, cu_seqlens_q, indices, seqused_kv, seqused_q, topk_length, sink,
+                  out, lse)
     topk = indices.shape[1]
     num_blocks, block_size = kv_cache.shape[0], kv_cache.shape[1]
-    batch = cu_seqlens_q.numel() - 1
-    if block_table.dim() != 2 or block_table.shape[0] != batch:
-        raise ValueError("block_table must be [batch, max_blocks]")
     if out is None:
         out = torch.empty((t, heads, dv), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
@@ -349,7 +394,7 @@ def mla_prefill_sparse_paged(q: torch.Tensor, kv_cache: torch.Tensor, block_tabl
     _check("mla_prefill_sparse_paged", lib.mla_prefill_sparse_paged(
         _ptr(q), q.stride(0), q.stride(1), _ptr(kv_cache), kv_cache.stride(1), num_blocks, block_size,
         _ptr(block_table), block_table.stride(0), block_table.shape[1], _ptr(cu_seqlens_q), batch,
-        _ptr(seqused_kv), _ptr(indices), indices.stride(0), topk, _ptr(topk_length),
+        _ptr(seqused_kv), _ptr(seqused_q), _ptr(indices), indices.stride(0), topk, _ptr(topk_length),
         t, heads, dqk, dv, float(softmax_scale), _ptr(sink),
         _ptr(out), out.stride(0), out.stride(1),
         _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0,
@@ -363,6 +408,14 @@ def chunked_context_workspace_bytes(batch: int, total_q: int, max_seqlen_q: int,
                                                                       chunk_tokens)
 
 
+def _check_latent_weights(latent: torch.Tensor, w_kv: torch.Tensor, heads: int) -> None:
+    """latent rows [N, 576] (512 latent + 64 rope); W_KV [>= H * 256, 512]."""
+    if latent.shape[1] != 576:
+        raise ValueError(f"latent must be [rows, 576], got {tuple(latent.shape)}")
+    if w_kv.shape[1] != 512 or w_kv.shape[0] < heads * 256:
+        raise ValueError(f"w_kv must be [>= {heads * 256}, 512], got {tuple(w_kv.shape)}")
+
+
 def mla_prefill_chunked_context(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, cu_seqlens_q: torch.Tensor,
                                 latent: torch.Tensor, cu_seqlens_ctx: torch.Tensor, w_kv: torch.Tensor,
                                 max_seqlen_q: int, max_seqlen_ctx: int, softmax_scale: float,
@@ -373,12 +426,17 @@ def mla_prefill_chunked_context(q: torch.Tensor, k: torch.Tensor, v: torch.Tenso
     (latent [N,576] bf16 rows, cu_seqlens_ctx int32 [B+1]) up-projected by w_kv [H*256, 512] bf16,
     chunk_tokens context positions per sequence at a time. Returns out [T,H,128] bf16 (and lse)."""
     lib = load_library()
-    _require_cuda(q, k, v, cu_seqlens_q, latent, cu_seqlens_ctx, w_kv, sink, out, lse, workspace)
-    for name, t in (("q", q), ("k", k), ("v", v), ("latent", latent), ("w_kv", w_kv)):
-        if t.dtype != torch.bfloat16 or t.stride(-1) != 1:
-            raise ValueError(f"{name} must be bf16 with a contiguous last dim")
+    for name, t, d in (("q", q, 3), ("k", k, 3), ("v", v, 3), ("latent", latent, 2), ("w_kv", w_kv, 2)):
+        _bf16(name, t, d)
     total_q, heads, _ = q.shape
-    batch = cu_seqlens_q.numel() - 1
+    for name, t, width in (("q", q, 192), ("k", k, 192), ("v", v, 128)):
+        if tuple(t.shape) != (total_q, heads, width):
+            raise ValueError(f"{name} must be [{total_q}, {heads}, {width}], got {tuple(t.shape)}")
+    batch = _cu_batch("cu_seqlens_q", cu_seqlens_q)
+    _int32_vec("cu_seqlens_ctx", cu_seqlens_ctx, batch + 1)
+    _check_latent_weights(latent, w_kv, heads)
+    _f32_vec("sink", sink, heads)
+    _require_cuda(q, k, v, cu_seqlens_q, latent, cu_seqlens_ctx, w_kv, sink, out, lse, workspace)
     if out is None:
         out = torch.empty((total_q, heads, 128), dtype=torch.bfloat16, device=q.device)
     if return_lse and lse is None:
@@ -401,8 +459,11 @@ def mla_latent_upproject(latent: torch.Tensor, cu_seqlens_ctx: torch.Tensor, w_k
                          ctx_start: int, chunk_tokens: int):
     """One chunk of cached latent rows -> (k [B*chunk, H, 192], v [B*chunk, H, 128], cu_chunk [B+1])."""
     lib = load_library()
+    _bf16("latent", latent, 2)
+    _bf16("w_kv", w_kv, 2)
+    batch = _cu_batch("cu_seqlens_ctx", cu_seqlens_ctx)
+    _check_latent_weights(latent, w_kv, num_heads)
     _require_cuda(latent, cu_seqlens_ctx, w_kv)
-    batch = cu_seqlens_ctx.numel() - 1
     rows = max(batch * chunk_tokens, 1)
     k = torch.empty((rows, num_heads, 192), dtype=torch.bfloat16, device=latent.device)
     v = torch.empty((rows, num_heads, 128), dtype=torch.bfloat16, device=latent.device)
@@ -419,10 +480,16 @@ def mla_combine(o_part: torch.Tensor, lse_part: torch.Tensor, num_heads: int,
     """Merge partials o_part float32 [S, T*H, Dv] / lse_part float32 [S, T*H] into out bf16
     [T, H, Dv] (and lse float32 [T, H])."""
     lib = load_library()
-    _require_cuda(o_part, lse_part, sink, out, lse)
-    if not (o_part.is_contiguous() and lse_part.is_contiguous()):
-        raise ValueError("o_part and lse_part must be contiguous")
+    if (o_part.dtype != torch.float32 or lse_part.dtype != torch.float32 or o_part.dim() != 3
+            or not (o_part.is_contiguous() and lse_part.is_contiguous())):
+        raise ValueError("o_part and lse_part must be contiguous float32 tensors")
     s, rows, dv = o_part.shape
+    if tuple(lse_part.shape) != (s, rows):
+        raise ValueError(f"lse_part must be [{s}, {rows}], got {tuple(lse_part.shape)}")
+    if num_heads <= 0 or rows % num_heads != 0:
+        raise ValueError(f"the {rows} partial rows are not a whole number of tokens of {num_heads} heads")
+    _f32_vec("sink", sink, num_heads)
+    _require_cuda(o_part, lse_part, sink, out, lse)
     t = rows // num_heads
     if out is None:
         out = torch.empty((t, num_heads, dv), dtype=torch.bfloat16, device=o_part.device)

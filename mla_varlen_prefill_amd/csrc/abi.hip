@@ -18,7 +18,7 @@
 
 namespace {
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kDenseBN = 64;
 constexpr int kDenseDqk = 192;
 constexpr int kDenseDv = 128;
@@ -271,11 +271,13 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
 }
 
 int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
-                                      int32_t num_heads, int32_t causal, int32_t num_splits) {
+                                      int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+                                      int32_t causal, int32_t num_splits) {
   (void)causal;
-  if (num_splits < 0 || num_splits > kMaxSplits) return -1;
+  if (num_splits < 0 || num_splits > kMaxSplits || !dense_dims_ok(head_dim_qk, head_dim_v)) return -1;
+  // the instance the bf16-output call runs (FP8 output selects the same tile height and residency)
   return resolve_splits(batch, max_seqlen_q, max_seqlen_k, num_heads, num_splits,
-                        dense_shape(kDenseDqk, kDenseDv, false));
+                        dense_shape(head_dim_qk, head_dim_v, false));
 }
 
 size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
@@ -321,7 +323,7 @@ static mla_status_t varlen_call(
       cu_seqlens_k == nullptr || out == nullptr)
     return MLA_ERR_INVALID_ARG;
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads <= 0 ||
-      num_splits < 0 || num_splits > kMaxSplits || !std::isfinite(softmax_scale) ||
+      num_splits < 0 || num_splits > kMaxSplits || !std::isfinite(softmax_scale) || !(softmax_scale > 0.f) ||
       window_left < -1 || window_right < -1)
     return MLA_ERR_INVALID_ARG;
   const int32_t right = causal ? 0 : window_right;  // causal is the right window 0
@@ -580,7 +582,8 @@ mla_status_t mla_prefill_chunked_context(
   if (latent == nullptr || cu_seqlens_ctx == nullptr || w_kv == nullptr || q == nullptr || out == nullptr)
     return MLA_ERR_INVALID_ARG;
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_ctx < 0 || num_heads <= 0 ||
-      chunk_tokens <= 0 || latent_stride_row < kSparseDqk || w_stride_row < 512 || !std::isfinite(softmax_scale))
+      chunk_tokens <= 0 || latent_stride_row < kSparseDqk || w_stride_row < 512 || !std::isfinite(softmax_scale) ||
+      !(softmax_scale > 0.f))
     return MLA_ERR_INVALID_ARG;
   if (batch > 65535 || num_heads > 32767 || chunk_tokens > (1 << 24) ||
       (int64_t)batch * chunk_tokens > INT32_MAX || (int64_t)num_heads * kDenseDqk >= (1 << 23))
@@ -661,7 +664,8 @@ mla_status_t sparse_call(mla::SparseParams& sp, const void* q, int64_t q_stride_
                          void* hip_stream) {
   if (q == nullptr || kv == nullptr || indices == nullptr || out == nullptr)
     return MLA_ERR_INVALID_ARG;
-  if (num_tokens < 0 || num_heads <= 0 || n_kv < 0 || topk <= 0 || !std::isfinite(softmax_scale))
+  if (num_tokens < 0 || num_heads <= 0 || n_kv < 0 || topk <= 0 || !std::isfinite(softmax_scale) ||
+      !(softmax_scale > 0.f))
     return MLA_ERR_INVALID_ARG;
   if (head_dim_qk != kSparseDqk || head_dim_v != kSparseDv || num_heads > 128 || topk > 8192 ||
       n_kv > INT32_MAX)
@@ -729,6 +733,7 @@ mla_status_t mla_prefill_sparse_paged(
     const void* kv_cache, int64_t kv_stride_row, int32_t num_blocks, int32_t block_size,
     const int32_t* block_table, int64_t bt_stride_seq, int32_t max_blocks_per_seq,
     const int32_t* cu_seqlens_q, int32_t batch, const int32_t* seqused_kv,
+    const int32_t* seqused_q,
     const int32_t* indices, int64_t idx_stride_tok, int32_t topk,
     const int32_t* topk_length,
     int32_t num_tokens, int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
@@ -747,7 +752,8 @@ mla_status_t mla_prefill_sparse_paged(
     return MLA_ERR_UNSUPPORTED;
   if ((reinterpret_cast<uintptr_t>(block_table) & 3u) != 0 ||
       (reinterpret_cast<uintptr_t>(cu_seqlens_q) & 3u) != 0 ||
-      (seqused_kv != nullptr && (reinterpret_cast<uintptr_t>(seqused_kv) & 3u) != 0))
+      (seqused_kv != nullptr && (reinterpret_cast<uintptr_t>(seqused_kv) & 3u) != 0) ||
+      (seqused_q != nullptr && (reinterpret_cast<uintptr_t>(seqused_q) & 3u) != 0))
     return MLA_ERR_ALIGNMENT;
   if (validate_inputs() && num_tokens > 0) {
     const mla_status_t vs = check_cu(cu_seqlens_q, batch, num_tokens, false, INT32_MAX, (hipStream_t)hip_stream);
@@ -756,7 +762,7 @@ mla_status_t mla_prefill_sparse_paged(
   mla::SparseParams sp{};
   sp.block_table = block_table; sp.bt_st = bt_stride_seq;
   sp.max_blocks = max_blocks_per_seq; sp.block_size = block_size; sp.num_blocks = num_blocks;
-  sp.cu_q = cu_seqlens_q; sp.batch = batch; sp.seqused = seqused_kv;
+  sp.cu_q = cu_seqlens_q; sp.batch = batch; sp.seqused = seqused_kv; sp.seqused_q = seqused_q;
   return sparse_call(sp, q, q_stride_tok, q_stride_head, kv_cache, kv_stride_row,
                      (int64_t)num_blocks * block_size, indices, idx_stride_tok, topk, topk_length,
                      num_tokens, num_heads, head_dim_qk, head_dim_v, softmax_scale, sink, out,

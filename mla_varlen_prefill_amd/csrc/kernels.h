@@ -76,6 +76,7 @@ struct SparseParams {
   int32_t max_blocks, block_size, num_blocks;
   const int32_t* cu_q; int32_t batch;
   const int32_t* seqused;
+  const int32_t* seqused_q;  // nullable [batch]: tokens of sequence b at or past cu_q[b] + seqused_q[b] see no key
 };
 
 struct CombineParams {

@@ -1,10 +1,9 @@
 // Varlen tile planner: one work-group turns cu_seqlens into the ordered list of query-tile work
 // items the dense kernel consumes, on the device (no host synchronisation, capturable).
 //
-// Prior art: a GPU kernel that plans varying-length sequences through a fixed-size buffer and a
-// helper that zeroes its counters (page "Mojo module mla", mla_prefill_plan_kernel,
-// set_buffer_lengths_to_zero); a metadata call producing a fixed-size int32 task split before
-// the attention call (page "SparseFlashMla", Description). The format is this library's own:
+// Prior art: a device-side planner for ragged batches with a counter-clearing helper (page "Mojo
+// module mla", mla_prefill_plan_kernel, set_buffer_lengths_to_zero); a metadata call that fills
+// an int32 task table before the attention operator (page "SparseFlashMla", Description). The format is this library's own:
 // items (b, m, n_blocks, kv_end), sequence by sequence (sequences with more key blocks first,
 // ties by b) and within a sequence from its last query tile to its first (with a left window:
 // n_blocks descending, then slot ascending), unused entries -1.

@@ -271,13 +271,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
       const int mid = (lo + hi + 1) >> 1;
       if (p.cu_q[mid] <= t) lo = mid; else hi = mid - 1;
     }
-    if (p.cu_q[lo] <= t && t < p.cu_q[lo + 1]) {
+    const bool in_use = p.seqused_q == nullptr || t - p.cu_q[lo] < p.seqused_q[lo];
+    if (p.cu_q[lo] <= t && t < p.cu_q[lo + 1] && in_use) {
       c.bt_row = p.block_table + (int64_t)lo * p.bt_st;
       int64_t used = (int64_t)p.max_blocks * p.block_size;
       if (p.seqused != nullptr) used = min(used, (int64_t)max(p.seqused[lo], 0));
       c.used = (int)used;
     } else {
-      c.len = 0;  // a token outside every sequence has no valid slot
+      c.len = 0;  // a token outside every sequence, or not in use, has no valid slot
     }
   }
   const int nblk = (c.len + BNS - 1) / BNS;

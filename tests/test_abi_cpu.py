@@ -33,7 +33,7 @@ def test_status_strings_and_version():
     lib = mla.load_library()
     for code, name in mla.STATUS_NAMES.items():
         assert lib.mla_status_string(code).decode() == name
-    assert lib.mla_abi_version() == 1
+    assert lib.mla_abi_version() == 2
     bm, bn = mla.dense_tile_shape()
     assert bm in (128, 256) and bn == 64
 
@@ -71,6 +71,7 @@ def test_varlen_window_argument_errors():
     """Windows below -1 are rejected; the other checks are those of mla_prefill_varlen."""
     lib = mla.load_library()
     assert _varlen_window(lib, -2, 0) == 1
+    assert _varlen_window(lib, 256, 0, scale=0.0) == 1
     assert _varlen_window(lib, 5, -3) == 1
     assert _varlen_window(lib, 256, 0, dqk=256) == 2
     assert _varlen_window(lib, 256, 0, q=P + 2) == 3
@@ -85,6 +86,8 @@ def test_varlen_argument_errors():
     assert _varlen(lib, splits=-1) == 1
     assert _varlen(lib, splits=65) == 1
     assert _varlen(lib, scale=float("nan")) == 1
+    assert _varlen(lib, scale=0.0) == 1                    # the scale must be positive
+    assert _varlen(lib, scale=-0.07) == 1
     assert _varlen(lib, qsh=100) == 1                      # head stride smaller than the row
     assert _varlen(lib, dqk=256) == 2                      # (256, 128) is not an MLA layout
     assert _varlen(lib, dv=256) == 2                       # nor (192, 256)
@@ -124,6 +127,7 @@ def test_varlen_fp8_argument_errors():
     is validated as for bf16 output."""
     lib = mla.load_library()
     assert _varlen_fp8(lib, scale_ptr=None) == 1
+    assert _varlen_fp8(lib, scale=-1.0) == 1
     assert _varlen_fp8(lib, ost=128 * 128 + 8) == 3
     assert _varlen_fp8(lib, osh=136, ost=128 * 136) == 3
     assert _varlen_fp8(lib, scale_ptr=P + 2) == 3
@@ -161,6 +165,9 @@ def test_sparse_argument_errors():
     assert lib.mla_prefill_sparse_workspace_size(4096, 128, 2048, 512) == 0
     assert _sparse(lib, kv=None) == 1
     assert _sparse(lib, topk=0) == 1
+    assert _sparse(lib, scale=0.0) == 1
+    assert _sparse(lib, scale=-0.04) == 1
+    assert _sparse(lib, scale=float("inf")) == 1
     assert _sparse(lib, idxst=32) == 1
     assert _sparse(lib, heads=129) == 2
     assert _sparse(lib, topk=8193, idxst=8193) == 2
@@ -172,13 +179,13 @@ def test_sparse_argument_errors():
 
 def _sparse_paged(lib, **kw):
     a = dict(q=P, qst=128 * 576, qsh=576, kv=P, kvst=576, nb=100, bs=64, bt=P, btst=16, maxb=16,
-             cu=P, batch=2, used=None, idx=P, idxst=64, topk=64, tl=None, t=4, heads=128, dqk=576,
+             cu=P, batch=2, used=None, usedq=None, idx=P, idxst=64, topk=64, tl=None, t=4, heads=128, dqk=576,
              dv=512, scale=0.04, sink=None, out=P, ost=128 * 512, osh=512, lse=None, lst=128, lsh=1,
              ws=None, wsb=0, stream=None)
     a.update(kw)
     return lib.mla_prefill_sparse_paged(
         a["q"], a["qst"], a["qsh"], a["kv"], a["kvst"], a["nb"], a["bs"], a["bt"], a["btst"],
-        a["maxb"], a["cu"], a["batch"], a["used"], a["idx"], a["idxst"], a["topk"], a["tl"], a["t"],
+        a["maxb"], a["cu"], a["batch"], a["used"], a["usedq"], a["idx"], a["idxst"], a["topk"], a["tl"], a["t"],
         a["heads"], a["dqk"], a["dv"], a["scale"], a["sink"], a["out"], a["ost"], a["osh"], a["lse"],
         a["lst"], a["lsh"], a["ws"], a["wsb"], a["stream"])
 
@@ -197,9 +204,63 @@ def test_sparse_paged_argument_errors():
     assert _sparse_paged(lib, nb=1 << 22, bs=1024) == 2          # rows above 2^31 - 1
     assert _sparse_paged(lib, bt=P + 2) == 3
     assert _sparse_paged(lib, used=P + 1) == 3
+    assert _sparse_paged(lib, usedq=P + 2) == 3
+    assert _sparse_paged(lib, scale=0.0) == 1
     assert _sparse_paged(lib, heads=129) == 2                    # shared sparse checks
     assert _sparse_paged(lib, kv=P + 4) == 3
     assert _sparse_paged(lib, t=0) == 0
+
+
+def _chunked(lib, **kw):
+    a = dict(q=P, qst=128 * 192, qsh=192, k=P, kst=128 * 192, ksh=192, v=P, vst=128 * 128, vsh=128, cuq=P,
+             lat=P, latst=576, cuc=P, w=P, wst=512, batch=2, total_q=16, max_q=8, max_c=100, heads=128,
+             chunk=64, scale=0.07, sink=None, out=P, ost=128 * 128, osh=128, lse=None, lst=128, lsh=1,
+             ws=P, wsb=64, stream=None)
+    a.update(kw)
+    return lib.mla_prefill_chunked_context(
+        a["q"], a["qst"], a["qsh"], a["k"], a["kst"], a["ksh"], a["v"], a["vst"], a["vsh"], a["cuq"],
+        a["lat"], a["latst"], a["cuc"], a["w"], a["wst"], a["batch"], a["total_q"], a["max_q"], a["max_c"],
+        a["heads"], a["chunk"], a["scale"], a["sink"], a["out"], a["ost"], a["osh"], a["lse"], a["lst"],
+        a["lsh"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_chunked_context_argument_errors():
+    lib = mla.load_library()
+    assert _chunked(lib, lat=None) == 1
+    assert _chunked(lib, chunk=0) == 1
+    assert _chunked(lib, scale=0.0) == 1
+    assert _chunked(lib, scale=-0.07) == 1
+    assert _chunked(lib, latst=512) == 1
+    assert _chunked(lib, lat=P + 8) == 3
+    assert _chunked(lib) == 4                                     # 64 bytes of workspace
+    assert _chunked(lib, batch=0) == 0
+
+
+@pytest.mark.parametrize("dqk,dv", [(192, 128), (128, 128), (256, 256)])
+@pytest.mark.parametrize("batch,max_len,heads", [(1, 4096, 2), (2, 300, 8), (1, 32768, 1), (8, 2048, 128),
+                                                 (3, 100, 1)])
+def test_num_splits_helper_is_the_split_count_the_call_uses(dqk, dv, batch, max_len, heads):
+    """mla_prefill_varlen_num_splits resolves num_splits = 0 with the tile height and residency of
+    the (dqk, dv) instance the call runs: a workspace sized for exactly that split count passes
+    the call's workspace check (which happens before any device access, so the call then stops at
+    MLA_ERR_HIP on a machine without a GPU), and one byte less fails it. The workspace grows by
+    total_q * H * dv * 4 bytes per split, so no other split count fits the same size."""
+    lib = mla.load_library()
+    total_q = batch * max_len
+    s = lib.mla_prefill_varlen_num_splits(batch, max_len, max_len, heads, dqk, dv, 1, 0)
+    assert 1 <= s <= 64
+    ws = lib.mla_prefill_varlen_workspace_size(batch, total_q, max_len, max_len, heads, dv, 1, s)
+    if s > 1:
+        ws_less = lib.mla_prefill_varlen_workspace_size(batch, total_q, max_len, max_len, heads, dv, 1, s - 1)
+        assert ws - ws_less >= total_q * heads * dv * 4
+    kw = dict(qst=heads * dqk, qsh=dqk, kst=heads * dqk, ksh=dqk, vst=heads * dv, vsh=dv, ost=heads * dv,
+              osh=dv, batch=batch, total_q=total_q, max_q=max_len, max_k=max_len, heads=heads, dqk=dqk, dv=dv,
+              splits=0)
+    assert _varlen(lib, ws_bytes=ws, **kw) == 5
+    assert _varlen(lib, ws_bytes=ws - 1, **kw) == 4
+    assert lib.mla_prefill_varlen_num_splits(batch, max_len, max_len, heads, dqk, dv, 1, 3) == 3
+    assert lib.mla_prefill_varlen_num_splits(batch, max_len, max_len, heads, 192, 256, 1, 0) == -1
+    assert lib.mla_prefill_varlen_num_splits(batch, max_len, max_len, heads, dqk, dv, 1, 65) == -1
 
 
 def test_combine_and_plan_argument_errors():

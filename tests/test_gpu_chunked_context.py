@@ -69,8 +69,9 @@ def test_chunked_context_matches_oracle(chunk, heads):
 
 
 def test_chunked_context_empty_context_equals_causal_prefill():
-    """Without context the result is the plain causal prefill of the new tokens (bit-identical:
-    same kernel, fp32 partial then the same rounding)."""
+    """Without context the result is the plain causal prefill of the new tokens: bit-identical to
+    the unsplit varlen call (the same planner and kernel launches), and within rounding of a
+    2-split call."""
     import torch
     import mla_varlen_prefill_amd as mla
     ctx, new = [0, 0], [200, 77]
@@ -78,11 +79,15 @@ def test_chunked_context_empty_context_equals_causal_prefill():
     announce("chunked context empty")
     o, lse = mla.mla_prefill_chunked_context(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(cu_q), dev_bf16(lat),
                                              dev(cu_c), dev_bf16(w), max(new), 0, 192 ** -0.5, chunk_tokens=64)
+    o1, lse1 = mla.mla_prefill_varlen(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(cu_q), dev(cu_q), max(new), max(new),
+                                      192 ** -0.5, causal=True, num_splits=1)
     o2, lse2 = mla.mla_prefill_varlen(dev_bf16(q), dev_bf16(k), dev_bf16(v), dev(cu_q), dev(cu_q), max(new), max(new),
                                       192 ** -0.5, causal=True, num_splits=2)
     torch.cuda.synchronize()
     ro, rl = O.dense_mla_prefill(q, k, v, cu_q, cu_q, float(np.float32(192 ** -0.5)), True)
     check_parity(host_f64(o), host_f64(lse), ro, rl, "chunked empty")
+    assert torch.equal(o.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(lse.view(torch.int32), lse1.view(torch.int32))
     assert torch.allclose(o.float(), o2.float(), atol=1e-2)
 
 

@@ -5,8 +5,7 @@ import numpy as np
 import pytest
 
 from oracle import mla_oracle as O
-from workloads import (make_dense, dense_small, dense_varlen, device_dense, bf16_tensor_to_bits,
-                       cu_from_lens, CHUNKED_SK)
+from workloads import make_dense, dense_small, dense_varlen
 from tests.gpu_util import announce, dev_bf16, dev, host_f64, check_parity
 
 pytestmark = pytest.mark.gpu
@@ -47,7 +46,10 @@ def test_dense_small_config():
     check_parity(o, lse, ro, rl, c.name)
 
 
-PROBES = [(1, 128), (129, 512), (1, 4096), (129, 4096), (129, 8192), (257, 300), (64, 64)]
+# The warm-up shape probes of page "FlashAttention backend for MLA prefill" (get_warmup_keys:
+# (max_seqlen_q, max_seqlen_k) in (1, 128), (129, 512), (1, 4096), (129, 4096), (1, 8192),
+# (129, 8192)), plus two ragged tile tails.
+PROBES = [(1, 128), (129, 512), (1, 4096), (129, 4096), (1, 8192), (129, 8192), (257, 300), (64, 64)]
 
 
 @pytest.mark.parametrize("causal", [False, True])
@@ -169,46 +171,6 @@ def test_dense_deterministic_and_batch_invariant():
     assert np.array_equal(o3, o1[a:b]) and np.array_equal(l3, l1[a:b])
 
 
-def _full_size_sampled(lens_q, lens_k, heads, seed, tokens, sample_heads, num_splits):
-    """Run a full-size case on the device and check sampled (token, head) rows against the oracle."""
-    import torch
-    import mla_varlen_prefill_amd as mla
-    q, k, v, cu_q, cu_k = device_dense(lens_q, lens_k, heads, seed)
-    scale = 192 ** -0.5
-    out, lse = mla.mla_prefill_varlen(q, k, v, cu_q, cu_k, max(lens_q), max(lens_k), scale,
-                                      causal=True, num_splits=num_splits)
-    torch.cuda.synchronize()
-    hs = list(sample_heads)
-    qb = bf16_tensor_to_bits(q[tokens][:, hs])
-    kb = bf16_tensor_to_bits(k[:, hs])
-    vb = bf16_tensor_to_bits(v[:, hs])
-    # oracle over the sampled tokens (their own sequences' keys), re-indexed to the sampled heads
-    cq = cu_from_lens(lens_q)
-    qfull = np.zeros((int(cq[-1]), len(hs), 192), dtype=np.uint16)
-    qfull[tokens] = qb
-    ro, rl = O.dense_mla_prefill_rows(qfull, kb, vb, cq, cu_from_lens(lens_k), float(np.float32(scale)),
-                                      True, tokens, list(range(len(hs))))
-    og = host_f64(out[tokens][:, hs])
-    lg = host_f64(lse[tokens][:, hs])
-    check_parity(og, lg, ro, rl, f"full-size {lens_q[:2]}.. splits={num_splits}")
-    del q, k, v, out, lse
-    torch.cuda.empty_cache()
-
-
-@pytest.mark.parametrize("num_splits", [0, 2, 4])
-def test_dense_long_context_sampled(num_splits):
-    announce(f"dense long 1x32768 h128 splits={num_splits}")
-    tokens = [0, 1, 127, 128, 4095, 16000, 32766, 32767]
-    _full_size_sampled([32768], [32768], 128, 3, tokens, [0, 5, 77, 127], num_splits)
-
-
-def test_dense_chunked_prefill_sampled():
-    announce("dense chunked b4 q2048")
-    cq = cu_from_lens([2048] * 4)
-    tokens = [0, 2047, 2048, 3000, 4096, 6143, 6144, 8191]
-    _full_size_sampled([2048] * 4, list(CHUNKED_SK), 128, 4, tokens, [1, 64, 126], 0)
-
-
 # The dense kernel keeps a fixed grid of work-groups that each run many work items in turn, handing
 # over from one item to the next inside the last key blocks. A tiny grid makes every work-group run
 # a long chain of items: items with zero, one, two and many key blocks, tail tiles, ties in the
@@ -239,3 +201,20 @@ def test_dense_persistent_item_chains_repeat_identical(monkeypatch):
     for _ in range(3):
         again = run_case(c)
         assert np.array_equal(first[0], again[0]) and np.array_equal(first[1], again[1], equal_nan=True)
+
+
+@pytest.mark.parametrize("heads", [16, 32])
+@pytest.mark.parametrize("wgs_per_xcd", [1, 3])
+@pytest.mark.parametrize("num_splits", [1, 3])
+def test_dense_contiguous_xcd_units_item_chains(heads, wgs_per_xcd, num_splits, monkeypatch):
+    """Head counts whose (head, split) units divide over the 8 XCDs take the contiguous per-XCD
+    lists (the path every 128-head call takes: several units per XCD, the shortest eighth of the
+    items last, stealing from other XCDs' lists once a list is used up). A tiny grid makes every
+    work-group run long chains of ragged items; every head is checked in full."""
+    monkeypatch.setenv("MLA_DENSE_WGS_PER_XCD", str(wgs_per_xcd))
+    c = make_dense(f"xcd_units_h{heads}_w{wgs_per_xcd}_s{num_splits}", MANY_LENS_Q, MANY_LENS_K,
+                   heads=heads, causal=True, seed=43, with_sink=True)
+    announce(f"dense {c.name}")
+    o, lse = run_case(c, num_splits=num_splits)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)

@@ -3,7 +3,7 @@ import numpy as np
 import pytest
 
 from oracle import mla_oracle as O
-from workloads import make_sparse, device_sparse, bf16_tensor_to_bits, f32_to_bf16_bits
+from workloads import make_sparse, f32_to_bf16_bits
 from tests.gpu_util import announce, dev_bf16, dev, host_f64, check_parity
 
 pytestmark = pytest.mark.gpu
@@ -97,20 +97,28 @@ def test_sparse_deterministic_no_lse():
     check_parity(o1, l1, ro, rl, c.name)
 
 
-def test_sparse_full_size_sampled_tokens():
+@pytest.mark.parametrize("topk", [200, 2500])
+def test_sparse_slot_permutation_invariance(topk):
+    """Each index slot counts independently (page "SparseFlashMla", formula over the participating
+    KV; -1 = padded slot), so permuting the slots of every token's row, pads included, leaves the
+    result unchanged up to summation order: the permuted call agrees with the oracle of the
+    original rows and with the unpermuted call within the tolerances. topk 2500 crosses the
+    kernel's staged index windows, so slots move between windows."""
     import torch
-    import mla_varlen_prefill_amd as mla
-    announce("sparse full size t4096 h128 topk2048 pool65536")
-    q, kv, idx, sink, idx_host = device_sparse(4096, 128, 65536, 2048, seed=5)
-    scale = 576 ** -0.5
-    out, lse = mla.mla_prefill_sparse(q, kv, idx, scale, sink=sink)
-    torch.cuda.synchronize()
-    toks = [0, 1, 2047, 4094, 4095]
-    qb = bf16_tensor_to_bits(q[toks])
-    kvb = bf16_tensor_to_bits(kv)
-    ro, rl = O.sparse_mla_prefill(qb, kvb, idx_host[toks], float(np.float32(scale)), dv=512,
-                                  sink=sink.cpu().numpy())
-    check_parity(host_f64(out[toks]), host_f64(lse[toks]), ro, rl, "sparse full size")
+    c = make_sparse(f"sparse_perm_k{topk}", num_tokens=6, heads=128, n_kv=4000, topk=topk, seed=48,
+                    pad_p=0.1, with_sink=True)
+    announce(f"sparse {c.name}")
+    o1, l1 = run_sparse(c)
+    ro, rl = oracle(c)
+    rng = np.random.default_rng(49)
+    perm = c.indices.copy()
+    for t in range(perm.shape[0]):
+        perm[t] = perm[t][rng.permutation(topk)]
+    assert not np.array_equal(perm, c.indices)
+    c.indices = perm
+    o2, l2 = run_sparse(c)
+    check_parity(o2, l2, ro, rl, f"{c.name} permuted vs oracle of the original rows")
+    check_parity(o2, l2, o1, l1, f"{c.name} permuted vs unpermuted")
 
 
 def test_sparse_strided_views():

@@ -10,7 +10,7 @@ from tests.gpu_util import announce, dev_bf16, dev, host_f64, check_parity
 pytestmark = pytest.mark.gpu
 
 
-def run_paged(c):
+def run_paged(c, seqused_q=None):
     import torch
     import mla_varlen_prefill_amd as mla
     q, cache = dev_bf16(c.q), dev_bf16(c.kv_cache)
@@ -18,14 +18,16 @@ def run_paged(c):
         q, cache, dev(c.block_table), dev(c.cu_q), dev(c.indices), c.scale,
         seqused_kv=dev(c.seqused) if c.seqused is not None else None,
         topk_length=dev(c.topk_length) if c.topk_length is not None else None,
-        sink=dev(c.sink) if c.sink is not None else None)
+        sink=dev(c.sink) if c.sink is not None else None,
+        seqused_q=dev(np.asarray(seqused_q, dtype=np.int32)) if seqused_q is not None else None)
     torch.cuda.synchronize()
     return host_f64(res[0]), host_f64(res[1])
 
 
-def oracle(c):
+def oracle(c, seqused_q=None):
     return O.sparse_mla_prefill_paged(c.q, c.kv_cache, c.block_table, c.cu_q, c.indices, c.scale,
-                                      dv=512, seqused=c.seqused, topk_length=c.topk_length, sink=c.sink)
+                                      dv=512, seqused=c.seqused, topk_length=c.topk_length, sink=c.sink,
+                                      seqused_q=seqused_q)
 
 
 @pytest.mark.parametrize("block_size", [1, 16, 64, 100])
@@ -39,6 +41,22 @@ def test_paged_ragged_sequences(block_size):
     o, lse = run_paged(c)
     ro, rl = oracle(c)
     check_parity(o, lse, ro, rl, c.name)
+
+
+@pytest.mark.parametrize("with_sink", [False, True])
+def test_paged_seqused_q(with_sink):
+    """seqused_q: only the first seqused_q[b] tokens of each sequence are in use; the others are
+    written as rows without keys (O = 0, LSE = -inf or the sink). Counts of 0, partial and full."""
+    c = make_sparse_paged("paged_seqused_q", [700, 40, 300], [5, 3, 4], 128, 300, 16, seed=80,
+                          with_sink=with_sink)
+    used_q = [2, 0, 4]
+    announce(f"sparse paged seqused_q sink={with_sink}")
+    o, lse = run_paged(c, used_q)
+    ro, rl = oracle(c, used_q)
+    check_parity(o, lse, ro, rl, "paged seqused_q")
+    for b in range(3):
+        drop = slice(int(c.cu_q[b]) + used_q[b], int(c.cu_q[b + 1]))
+        assert np.all(o[drop] == 0)
 
 
 def test_paged_edges_bad_table_entries_empty_sequence_and_stray_token():
@@ -70,9 +88,12 @@ def test_paged_full_size_matches_physical_rows_and_oracle():
     t, h, n_kv, topk, bs = 4096, 128, 65536, 2048, 64
     q, kv, cache, table, cu_q, idx, sink, idx_host = device_sparse_paged(t, h, n_kv, topk, bs, seed=5)
     scale = 576 ** -0.5
-    o_p, l_p = mla.mla_prefill_sparse_paged(q, cache, table, cu_q, idx, scale, sink=sink)
+    o_p = torch.full((t, h, 512), float("nan"), dtype=torch.bfloat16, device="cuda")
+    l_p = torch.full((t, h), float("nan"), dtype=torch.float32, device="cuda")
+    mla.mla_prefill_sparse_paged(q, cache, table, cu_q, idx, scale, sink=sink, out=o_p, lse=l_p)
     o_r, l_r = mla.mla_prefill_sparse(q, kv, idx, scale, sink=sink)
     torch.cuda.synchronize()
+    assert not bool(torch.isnan(o_p).any()) and not bool(torch.isnan(l_p).any()), "rows never written"
     assert torch.equal(o_p.view(torch.int16), o_r.view(torch.int16))
     assert torch.equal(l_p, l_r)
     toks = [0, 1, 2047, 4095]
