@@ -167,6 +167,42 @@ mla_status_t mla_prefill_varlen(
     void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /* ------------------------------------------------------------------------------------------
+ * Allocation-free variant of mla_prefill_varlen.
+ *
+ * For callers that cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation. Same operation, arguments (without the workspace),
+ * kernels and results as mla_prefill_varlen; the plan, the work-ticket counters and the split
+ * partials live in a static device array of MLA_NOALLOC_SCRATCH_BYTES bytes inside the library
+ * (one per GPU, held from library load until the process ends). The call allocates nothing and
+ * clears what must start at zero itself (the planner kernel zeroes the counters), so it may be
+ * captured into a HIP graph.
+ *   - Every call on one GPU uses that GPU's single array: calls that may overlap in time on the
+ *     same GPU (different streams, or concurrent host threads) RACE and must be serialised by
+ *     the caller. Sequential calls on one stream are safe.
+ *   - MLA_VALIDATE is ignored here (its host copy allocates and synchronises).
+ * Size limit: the call runs iff mla_prefill_varlen_workspace_size(...) for the same arguments is
+ * at most MLA_NOALLOC_SCRATCH_BYTES (64 MiB). Unsplit, that is about 1.3 KB plus 32 bytes per
+ * query-tile slot (batch * ceil(max_seqlen_q / 128)), so every call below two million slots
+ * fits; each split adds total_q * H * (head_dim_v + 1) * 4 bytes of partials, so a split call
+ * (forced, or chosen by the heuristic for small grids) fits only while those partials do.
+ * Errors: those of mla_prefill_varlen, where WORKSPACE means the size limit above is exceeded
+ * (checked on the host before anything is launched); HIP if the array's device address cannot
+ * be resolved.
+ * ------------------------------------------------------------------------------------------ */
+#define MLA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+mla_status_t mla_prefill_varlen_noalloc(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head, void* hip_stream);
+
+/* ------------------------------------------------------------------------------------------
  * Dense varlen MLA prefill with a sliding-window (band) mask.
  *
  * mla_prefill_varlen with a window (page "Sgl project Sglang FA4 Interface", window_size =

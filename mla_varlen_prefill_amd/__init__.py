@@ -9,6 +9,7 @@ gfx950 GPU, every call raises.
 Entry points (same names as the C ABI):
   mla_prefill_varlen  dense varlen prefill, q/k 192 = 128 nope + 64 rope, v 128, causal or not
                       (also the other MLA layouts: q/k 128 with v 128, q/k 256 with v 256)
+  mla_prefill_varlen_noalloc  the same without a workspace or any allocation (static scratch)
   mla_prefill_varlen_window  the same with a (left, right) sliding-window band mask
   mla_prefill_varlen_fp8  the same with FP8 e4m3 output under a static per-tensor scale
   mla_prefill_sparse  sparse top-k prefill over one shared 576-wide latent KV (v = first 512)
@@ -37,7 +38,8 @@ STATUS_NAMES = {0: "MLA_OK", 1: "MLA_ERR_INVALID_ARG", 2: "MLA_ERR_UNSUPPORTED",
 
 EXPORTED_SYMBOLS = (
     "mla_status_string", "mla_abi_version", "mla_dense_tile_shape", "mla_prefill_plan",
-    "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_window",
+    "mla_prefill_varlen_workspace_size", "mla_prefill_varlen", "mla_prefill_varlen_noalloc",
+    "mla_prefill_varlen_window",
     "mla_prefill_varlen_fp8", "mla_prefill_varlen_num_splits",
     "mla_prefill_sparse_workspace_size", "mla_prefill_sparse", "mla_prefill_sparse_paged",
     "mla_prefill_chunked_context_workspace_size", "mla_prefill_chunked_context", "mla_latent_upproject",
@@ -83,6 +85,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
         _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
         _c_f32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_sz, _vp]
+    lib.mla_prefill_varlen_noalloc.restype = ctypes.c_int
+    lib.mla_prefill_varlen_noalloc.argtypes = [
+        _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
+        _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32, _c_i32,
+        _c_f32, _c_i32, _c_i32, _vp, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp]
     lib.mla_prefill_varlen_window.restype = ctypes.c_int
     lib.mla_prefill_varlen_window.argtypes = [
         _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _c_i64, _c_i64, _vp, _vp,
@@ -296,6 +303,40 @@ def mla_prefill_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
         _check("mla_prefill_varlen_window",
                lib.mla_prefill_varlen_window(*head, int(window[0]), int(window[1]), *tail))
     return (out, lse) if return_lse else out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MLA_NOALLOC_SCRATCH_BYTES of include/mla_prefill.h
+
+
+def mla_prefill_varlen_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                               cu_seqlens_q: torch.Tensor, cu_seqlens_k: torch.Tensor,
+                               max_seqlen_q: int, max_seqlen_k: int, softmax_scale: float,
+                               out: torch.Tensor, lse: Optional[torch.Tensor] = None,
+                               causal: bool = True, num_splits: int = 0,
+                               sink: Optional[torch.Tensor] = None) -> None:
+    """The allocation-free dense entry point (mla_prefill_varlen_noalloc): the caller passes the
+    output (bf16 [Tq, H, Dv]) and, optionally, the LSE (float32 [Tq, H]); nothing is allocated
+    here or in the library (the plan and partials use the library's static device scratch, so
+    calls that overlap in time on one GPU race). Results are those of mla_prefill_varlen."""
+    lib = load_library()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _bf16(name, t, 3)
+    total_q, heads, dqk = q.shape
+    dv = v.shape[2]
+    if tuple(k.shape[1:]) != (heads, dqk):
+        raise ValueError(f"k must be [tokens, {heads}, {dqk}] like q, got {tuple(k.shape)}")
+    if v.shape[0] != k.shape[0] or v.shape[1] != heads:
+        raise ValueError(f"v must be [{k.shape[0]}, {heads}, dv] like k, got {tuple(v.shape)}")
+    batch = _cu_batch("cu_seqlens_q", cu_seqlens_q)
+    _int32_vec("cu_seqlens_k", cu_seqlens_k, batch + 1)
+    _f32_vec("sink", sink, heads)
+    _check_out_lse(out, lse, total_q, heads, dv)
+    _require_cuda(q, k, v, cu_seqlens_q, cu_seqlens_k, sink, out, lse)
+    _check("mla_prefill_varlen_noalloc", lib.mla_prefill_varlen_noalloc(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), k.stride(1), _ptr(v), v.stride(0), v.stride(1),
+        _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), batch, total_q, max_seqlen_q, max_seqlen_k, heads, dqk, dv,
+        float(softmax_scale), int(bool(causal)), num_splits, _ptr(sink), _ptr(out), out.stride(0), out.stride(1),
+        _ptr(lse), lse.stride(0) if lse is not None else 0, lse.stride(1) if lse is not None else 0, _stream()))
 
 
 def mla_prefill_varlen_window(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

@@ -49,6 +49,29 @@ const DeviceInfo* device_info() {
   return g_dev[dev].ok ? &g_dev[dev] : nullptr;
 }
 
+// ---- scratch of the allocation-free dense entry point ---------------------------------------
+// The plan, the ticket counters and the split partials of one mla_prefill_varlen_noalloc call
+// live in this array instead of a caller workspace. Every GPU the library runs on holds its own
+// copy from module load until the process ends; host code never uses the array's name as an
+// address (it is a host-side stand-in), only the device address resolved below.
+constexpr size_t kNoAllocScratchBytes = MLA_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+void* g_scratch_ptr[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`, resolved once per device with that
+// device current; null if the device cannot be queried or the lookup failed.
+void* scratch_device_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::call_once(g_scratch_once[dev], [dev]() {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[dev] = p;
+  });
+  return g_scratch_ptr[dev];
+}
+
 // ---- launch timing (measurement aid) ------------------------------------------------------
 constexpr int kNumKernels = 5;
 constexpr size_t kMaxPending = 65536;
@@ -311,13 +334,15 @@ static mla_status_t varlen_call(
     void* out, int64_t o_stride_tok, int64_t o_stride_head,
     float* lse, int64_t lse_stride_tok, int64_t lse_stride_head,
     void* workspace, size_t workspace_bytes, void* hip_stream,
-    float* part_o = nullptr, float* part_lse = nullptr, int accumulate = 0, bool check = true) {
+    float* part_o = nullptr, float* part_lse = nullptr, int accumulate = 0, bool check = true,
+    bool noalloc = false) {
   // out_scale: null for bf16 output, else fp8 e4m3 output of O / *out_scale.
   // part_o / part_lse (internal use): write the normalised fp32 result [total_q, H, Dv] and its
   // LSE [total_q, H] there instead of `out` / `lse`, unsplit and without the sink; with
   // accumulate = 1, merge it into the running result already held there; with 2, merge it with
   // that result and write the final `out` / `lse` (sink folded in) instead. check = false skips
-  // the MLA_VALIDATE checks (cu_seqlens built by the library itself).
+  // the MLA_VALIDATE checks (cu_seqlens built by the library itself). noalloc: the workspace is
+  // this device's copy of `scratch` (the caller passes none).
   if (part_o != nullptr) num_splits = 1;
   if (q == nullptr || k == nullptr || v == nullptr || cu_seqlens_q == nullptr ||
       cu_seqlens_k == nullptr || out == nullptr)
@@ -353,6 +378,12 @@ static mla_status_t varlen_call(
   const VarlenLayout L = varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits, ds);
   const int dv_tiles = head_dim_v / 128;  // work items per (row tile, head, split): 128 columns each
   if ((int64_t)L.n_slots * num_heads * L.splits * dv_tiles > INT32_MAX - 8) return MLA_ERR_UNSUPPORTED;
+  if (noalloc) {
+    if (L.total > kNoAllocScratchBytes) return MLA_ERR_WORKSPACE;
+    workspace = scratch_device_ptr();
+    workspace_bytes = kNoAllocScratchBytes;
+    if (workspace == nullptr) return MLA_ERR_HIP;
+  }
   if (workspace == nullptr || workspace_bytes < L.total) return MLA_ERR_WORKSPACE;
   if (!aligned16(workspace)) return MLA_ERR_ALIGNMENT;
   const DeviceInfo* di = device_info();
@@ -460,6 +491,25 @@ mla_status_t mla_prefill_varlen(
                      max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal, -1, -1,
                      num_splits, sink, nullptr, out, o_stride_tok, o_stride_head, lse, lse_stride_tok,
                      lse_stride_head, workspace, workspace_bytes, hip_stream);
+}
+
+mla_status_t mla_prefill_varlen_noalloc(
+    const void* q, int64_t q_stride_tok, int64_t q_stride_head,
+    const void* k, int64_t k_stride_tok, int64_t k_stride_head,
+    const void* v, int64_t v_stride_tok, int64_t v_stride_head,
+    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+    int32_t batch, int32_t total_q, int32_t max_seqlen_q, int32_t max_seqlen_k,
+    int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
+    float softmax_scale, int32_t causal, int32_t num_splits, const float* sink,
+    void* out, int64_t o_stride_tok, int64_t o_stride_head,
+    float* lse, int64_t lse_stride_tok, int64_t lse_stride_head, void* hip_stream) {
+  // Same launches as mla_prefill_varlen; MLA_VALIDATE is not honoured here (its host copy
+  // allocates and synchronises).
+  return varlen_call(q, q_stride_tok, q_stride_head, k, k_stride_tok, k_stride_head, v, v_stride_tok,
+                     v_stride_head, cu_seqlens_q, cu_seqlens_k, batch, total_q, max_seqlen_q,
+                     max_seqlen_k, num_heads, head_dim_qk, head_dim_v, softmax_scale, causal, -1, -1,
+                     num_splits, sink, nullptr, out, o_stride_tok, o_stride_head, lse, lse_stride_tok,
+                     lse_stride_head, nullptr, 0, hip_stream, nullptr, nullptr, 0, false, true);
 }
 
 mla_status_t mla_prefill_varlen_window(

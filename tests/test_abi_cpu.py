@@ -109,6 +109,41 @@ def test_varlen_argument_errors():
                    vst=128 * 256, vsh=256, ost=128 * 128, osh=128) == 1   # output rows overlap
 
 
+def _varlen_noalloc(lib, **kw):
+    a = dict(q=P, qst=128 * 192, qsh=192, k=P, kst=128 * 192, ksh=192, v=P, vst=128 * 128, vsh=128,
+             cuq=P, cuk=P, batch=1, total_q=16, max_q=16, max_k=16, heads=128, dqk=192, dv=128,
+             scale=0.07, causal=1, splits=1, sink=None, out=P, ost=128 * 128, osh=128, lse=None,
+             lst=128, lsh=1, stream=None)
+    a.update(kw)
+    return lib.mla_prefill_varlen_noalloc(
+        a["q"], a["qst"], a["qsh"], a["k"], a["kst"], a["ksh"], a["v"], a["vst"], a["vsh"], a["cuq"],
+        a["cuk"], a["batch"], a["total_q"], a["max_q"], a["max_k"], a["heads"], a["dqk"], a["dv"], a["scale"],
+        a["causal"], a["splits"], a["sink"], a["out"], a["ost"], a["osh"], a["lse"], a["lst"], a["lsh"],
+        a["stream"])
+
+
+def test_varlen_noalloc_argument_errors_and_size_limit():
+    """The allocation-free entry point validates like mla_prefill_varlen, then checks on the host
+    that the call's workspace fits the library's static scratch (64 MiB): a call that does not
+    fit returns WORKSPACE before anything is resolved or launched; one that fits gets as far as
+    the device (HIP on a machine without a GPU)."""
+    lib = mla.load_library()
+    assert _varlen_noalloc(lib, q=None) == 1
+    assert _varlen_noalloc(lib, scale=0.0) == 1
+    assert _varlen_noalloc(lib, dqk=256) == 2
+    assert _varlen_noalloc(lib, q=P + 8) == 3
+    assert _varlen_noalloc(lib, batch=0) == 0
+    limit = mla.NOALLOC_SCRATCH_BYTES
+    # 64 forced splits of 1000 rows x 8 heads: 64 * 8000 * 129 * 4 bytes of partials
+    big = dict(qst=8 * 192, kst=8 * 192, vst=8 * 128, ost=8 * 128, heads=8, total_q=1000, max_q=1000, max_k=1000,
+               splits=64)
+    assert lib.mla_prefill_varlen_workspace_size(1, 1000, 1000, 1000, 8, 128, 1, 64) > limit
+    assert _varlen_noalloc(lib, **big) == 4
+    fits = dict(big, splits=2)
+    assert lib.mla_prefill_varlen_workspace_size(1, 1000, 1000, 1000, 8, 128, 1, 2) <= limit
+    assert _varlen_noalloc(lib, **fits) == 5
+
+
 def _varlen_fp8(lib, scale_ptr=P, **kw):
     a = dict(q=P, qst=128 * 192, qsh=192, k=P, kst=128 * 192, ksh=192, v=P, vst=128 * 128, vsh=128,
              cuq=P, cuk=P, batch=1, total_q=16, max_q=16, max_k=16, heads=128, dqk=192, dv=128,
