@@ -77,6 +77,13 @@ __device__ __forceinline__ void g2lds16(const void* gptr, void* lds_base) {
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Work-group barrier for hand-offs through LDS: waits for this wave's own LDS operations, then
+// joins the barrier, in one asm statement that the compiler cannot move memory accesses across.
+// Unlike __syncthreads(), whose work-group release fence also waits for every global -> LDS copy
+// still in flight (vmcnt(0)), it leaves those copies running; the caller waits for the copies it
+// needs with an explicit vmcnt before calling it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ bf16x8 lds_read_b128(const void* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }

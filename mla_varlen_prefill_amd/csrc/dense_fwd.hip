@@ -43,7 +43,10 @@ namespace {
 
 constexpr int BN = 64;
 
-constexpr float kRescaleLog2 = 8.f;  // rescale O only when a row max grows by more than 2^8
+// A row's probabilities are taken against a reference logit (see compute_block); a block whose
+// row sum would pass 2^64 is redone against its exact maximum (P stays far inside bf16 / fp32
+// range, and O = sum P V inside fp32 range for any bf16 V).
+constexpr float kOverflowSum = 18446744073709551616.f;  // 2^64
 // Bytes of a wave's K copy region used by the epilogue's output turn-around (32 rows x 128 B).
 constexpr int kEpilogueBytes = 32 * 128;
 
@@ -224,43 +227,58 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
         }
     }
   }
-  // ---- online softmax (per lane = per query; halves l and l^32 share a query), lazy rescale
+  // ---- softmax against a per-row reference logit (per lane = per query; lanes l and l^32 share
+  // a query). A row's reference m_run is the largest logit of the first block in which it sees a
+  // key, so the row maximum is only computed while some row of the wave has no reference yet. P =
+  // 2^((s - m_run) * scale * log2 e) is summed in fp32 (before its rounding to bf16 for P.V, so
+  // the LSE keeps fp32 accuracy on rows with few keys). A block whose running sum would pass 2^64
+  // (a logit some 44 nats above the reference) is redone exactly: its maximum becomes the
+  // reference and the accumulated O and l are rescaled.
   bf16x8 pf[NQ][2][2];
-  const float tau_raw = kRescaleLog2 / scale_log2;
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
-    float mx = s[nq][0][0];
+    auto block_max = [&]() {
+      float mx = s[nq][0][0];
 #pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
+      for (int mt = 0; mt < NMT; ++mt)
 #pragma unroll
-      for (int i = (mt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[nq][mt][i]);
-    mx = xhalf_max(mx);
-    const float m_new = fmaxf(m_run[nq], mx);
-    if (__ballot(m_new > m_run[nq] + tau_raw) != 0ull) {
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run[nq] - m_use) * scale_log2);
+        for (int i = (mt == 0 ? 1 : 0); i < 16; ++i) mx = fmaxf(mx, s[nq][mt][i]);
+      return xhalf_max(mx);
+    };
+    auto exps = [&](float ref, float l0) {
+      const float mc = ((ref == -INFINITY) ? 0.f : ref) * scale_log2;
+      float rs = l0;
+#pragma unroll
+      for (int mt = 0; mt < NMT; ++mt)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          u32x4 packed;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float p0 = fast_exp2(fmaf(s[nq][mt][cc * 8 + 2 * e], scale_log2, -mc));
+            const float p1 = fast_exp2(fmaf(s[nq][mt][cc * 8 + 2 * e + 1], scale_log2, -mc));
+            packed[e] = pack_bf16x2(p0, p1);
+            rs += p0 + p1;
+          }
+          pf[nq][mt][cc] = __builtin_bit_cast(bf16x8, packed);
+        }
+      return rs;
+    };
+    if (__ballot(m_run[nq] == -INFINITY) != 0ull) {
+      const float mx = block_max();
+      if (m_run[nq] == -INFINITY) m_run[nq] = mx;
+    }
+    float l_new = exps(m_run[nq], l_run[nq]);
+    if (__ballot(!(l_new <= kOverflowSum)) != 0ull) {
+      const float m_new = fmaxf(m_run[nq], block_max());
+      const float alpha = (m_new == m_run[nq]) ? 1.f : fast_exp2((m_run[nq] - m_new) * scale_log2);
       l_run[nq] *= alpha;
 #pragma unroll
       for (int dt = 0; dt < DV / 32; ++dt) o[nq][dt] *= alpha;
       m_run[nq] = m_new;
+      l_new = exps(m_run[nq], l_run[nq]);
     }
-    const float mc = ((m_run[nq] == -INFINITY) ? 0.f : m_run[nq]) * scale_log2;
-    float rs = l_run[nq];
-#pragma unroll
-    for (int mt = 0; mt < NMT; ++mt)
-#pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
-        u32x4 packed;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float p0 = fast_exp2(fmaf(s[nq][mt][cc * 8 + 2 * e], scale_log2, -mc));
-          const float p1 = fast_exp2(fmaf(s[nq][mt][cc * 8 + 2 * e + 1], scale_log2, -mc));
-          packed[e] = pack_bf16x2(p0, p1);
-          rs += p0 + p1;
-        }
-        pf[nq][mt][cc] = __builtin_bit_cast(bf16x8, packed);
-      }
-    l_run[nq] = rs;
+    l_run[nq] = l_new;
   }
   // ---- O^T += V_blk^T * P^T: the four dv tiles are independent chains; the transposed V reads
   // run PF steps ahead of their MFMA.

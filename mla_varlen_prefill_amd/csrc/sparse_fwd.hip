@@ -132,16 +132,24 @@ __device__ __forceinline__ void issue_gather(const SparseParams& p, const Sparse
   // keeps the compiler from hoisting it out of the block loop into registers it would spill.
   int lane = c.lane;
   asm volatile("" : "+v"(lane));
+  // All index reads first, then all copies: the copies write LDS, so the compiler would otherwise
+  // keep each index read behind the previous copy and wait for it on its own (one LDS round trip
+  // per copy instead of one per block).
+  int rid[COPIES_PER_WAVE], chunk[COPIES_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < COPIES_PER_WAVE; ++i) {
     const int q = min(c.wave + NWAVES * i, COPIES - 1);
     const int slot = q * 64 + lane;
     const int row = min(slot / ROW_CHUNKS, BNS - 1);
-    int chunk = slot - (slot / ROW_CHUNKS) * ROW_CHUNKS;
-    chunk = (slot / ROW_CHUNKS >= BNS || chunk >= CHUNKS) ? 0 : chunk;
-    int rid = c.idx[base + row_key(row)];
-    rid = (rid >= 0 && (int64_t)rid < p.n_kv) ? rid : 0;
-    g2lds16(p.kv + (int64_t)rid * p.kv_st + chunk * 8, stage + q * 1024);
+    const int ch = slot - (slot / ROW_CHUNKS) * ROW_CHUNKS;
+    chunk[i] = (slot / ROW_CHUNKS >= BNS || ch >= CHUNKS) ? 0 : ch;
+    rid[i] = c.idx[base + row_key(row)];
+  }
+#pragma unroll
+  for (int i = 0; i < COPIES_PER_WAVE; ++i) {
+    const int q = min(c.wave + NWAVES * i, COPIES - 1);
+    const int r = (rid[i] >= 0 && (int64_t)rid[i] < p.n_kv) ? rid[i] : 0;
+    g2lds16(p.kv + (int64_t)r * p.kv_st + chunk[i] * 8, stage + q * 1024);
   }
   if (c.wave == 0) {
     const int rid = c.idx[base + (c.lane & 31)];
@@ -189,11 +197,16 @@ __device__ __forceinline__ void compute_block(const SparseCtx& c, const char* st
   }
   // ---- invalid slots: this lane holds keys 16*mt + 4*g + i
   if (valid != 0xFFFFFFFFu) {
+    // the lane's bits, shifted once per block; the tests below then take constant bit positions
+    // (per-lane bit masks hoisted out of the loop would cost registers the loop does not have, and
+    // a reload from scratch here would wait for every gather in flight)
+    uint32_t vl = valid >> (4 * c.g);
+    asm volatile("" : "+v"(vl));
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        if (((valid >> (16 * mt + 4 * c.g + i)) & 1u) == 0u) s[mt][i] = -INFINITY;
+        if (((vl >> (16 * mt + i)) & 1u) == 0u) s[mt][i] = -INFINITY;
   }
   // ---- online softmax against the reference max (fixed once the head holds any mass)
   float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
@@ -317,7 +330,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
     for (int b = 0; b < 3; ++b)
       if (b < nblk) issue_gather(p, c, b, stages[b], &valid_mask[b]);
     wait_gather(min(nblk, 3) - 1);
-    __syncthreads();
+    lds_barrier();
 
     // Steady state, unrolled by four so that each ring slot is a distinct LDS object.
 #define MLA_SPARSE_STEP(K, CUR, NEXT)                                                            \
@@ -337,7 +350,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
         compute_block(c, CUR, valid_mask[(K)], qf, m_ref, l_run, o, p.scale_log2, flush_raw,      \
                       m_true, overflow);                                                          \
       wait_gather(min(nblk - 1, jj + 3) - (jj + 1));                                              \
-      __syncthreads();                                                                            \
+      lds_barrier(); /* the later blocks' copies stay in flight */                                \
     }
     for (int j = 0; j < nblk; j += 4) {
       MLA_SPARSE_STEP(0, stage0, stage3)
