@@ -24,14 +24,16 @@ def _inputs(ctx, new, heads, seed):
     return cu_c, cu_q, lat, w, q, k, v, sink
 
 
+@pytest.mark.parametrize("heads", [4, 5, 128])
 @pytest.mark.parametrize("ctx_start,chunk", [(0, 128), (100, 64), (0, 1000)])
-def test_upproject_chunk_matches_oracle(ctx_start, chunk):
+def test_upproject_chunk_matches_oracle(ctx_start, chunk, heads):
+    """Rows of several sequences (one empty, one of a single row, tails of 128-row tiles), an odd
+    head count (a half-filled head pair) and 128 heads (every XCD's head pairs)."""
     import torch
     import mla_varlen_prefill_amd as mla
     ctx = [300, 0, 129, 1]
-    heads = 4
     cu_c, _, lat, w, *_ = _inputs(ctx, [1] * 4, heads, 61)
-    announce(f"upproject start={ctx_start} chunk={chunk}")
+    announce(f"upproject start={ctx_start} chunk={chunk} heads={heads}")
     k, v, cu = mla.mla_latent_upproject(dev_bf16(lat), dev(cu_c), dev_bf16(w), heads, ctx_start, chunk)
     torch.cuda.synchronize()
     lens = [min(max(n - ctx_start, 0), chunk) for n in ctx]
