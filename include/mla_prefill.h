@@ -78,12 +78,16 @@ void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n);
  * count.
  *
  * Slots are (b, m) for b < batch and m < Mt = ceil(max_seqlen_q / block_m); slot (b, m) is an
- * item iff m * block_m < Sq_b. Each item is four int32 words (b, m, n_blocks, kv_end): kv_end is
- * the count of leading keys any row of the tile may see (Sk_b without a right limit, else the
- * bottom-right bound clamp(i_last + Sk_b - Sq_b + r + 1, 0, Sk_b) with i_last the tile's last
- * row and r the right window, 0 when causal). With a left window l >= 0 the first key any row
- * may see is kv_start = clamp(m * block_m + Sk_b - Sq_b - l, 0, Sk_b), else 0; n_blocks counts
- * the blocks from kv_start / block_n to ceil(kv_end / block_n) (0 when kv_end <= kv_start).
+ * item iff m < T_b = ceil(Sq_b / block_m). Query tiles are aligned to the end of the sequence:
+ * tile m holds the existing rows of [m * block_m - pad_b, (m + 1) * block_m - pad_b), pad_b =
+ * T_b * block_m - Sq_b (the Sq_b mod block_m leftover rows form tile 0, where causal rows see the
+ * fewest keys). Each item is four int32 words (b, m, n_blocks, kv_end): kv_end is the count of
+ * leading keys any row of the tile may see (Sk_b without a right limit, else the bottom-right
+ * bound clamp(i_last + Sk_b - Sq_b + r + 1, 0, Sk_b) with i_last the tile's last row and r the
+ * right window, 0 when causal). With a left window l >= 0 the first key any row may see is
+ * kv_start = clamp(i_first + Sk_b - Sq_b - l, 0, Sk_b) with i_first the tile's first row, else 0;
+ * n_blocks counts the blocks from kv_start / block_n to ceil(kv_end / block_n) (0 when
+ * kv_end <= kv_start).
  * Items are ordered sequence by sequence, sequences with more key blocks first
  * (min(ceil(Sk_b / block_n), 0x3FFFE) descending, ties by b ascending), and within a sequence
  * from its last query tile to its first (m descending); with a left window (window_left >= 0)
@@ -138,11 +142,10 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
  *         after.
  *         It holds the plan and the work-ticket counters of the call: calls that may overlap in
  *         time (other streams) must not share a workspace.
- * Tuning (environment, read by the library): MLA_DENSE_NQ=2 selects 256-row query tiles (one
- * work-group per CU; (192, 128) with bf16 output only, other instances keep 128 rows); MLA_DENSE_GROUP=n schedules n (head, split) units per XCD at a time
- * (default 1); MLA_DENSE_WGS_PER_XCD=n caps the persistent grid at 8*n work-groups (default: all
- * resident slots). The last two leave results bitwise unchanged (each work item is computed the
- * same way whichever work-group runs it); the tile height may change them within rounding.
+ * Tuning (environment, read by the library): MLA_DENSE_GROUP=n schedules n (head, split) units
+ * per XCD at a time (default 1); MLA_DENSE_WGS_PER_XCD=n caps the persistent grid at 8*n
+ * work-groups (default: all resident slots). Both leave results bitwise unchanged (each work item
+ * is computed the same way whichever work-group runs it).
  * With num_splits == 1 a sequence's result does not depend on the other sequences in the batch,
  * and repeated calls are bitwise identical.
  * Errors: INVALID_ARG (null q/k/v/cu/out, sizes <= 0 where a count is required, strides smaller

@@ -117,15 +117,8 @@ hipError_t timed_launch(int kind, hipStream_t stream, F&& fn) {
   return hipSuccess;
 }
 
-// Query rows per dense work-group: 128 (NQ = 1, two work-groups per CU) or 256 (NQ = 2).
-int dense_nq() {
-  static int nq = []() {
-    const char* e = std::getenv("MLA_DENSE_NQ");
-    return (e != nullptr && std::atoi(e) == 2) ? 2 : 1;
-  }();
-  return nq;
-}
-int dense_bm() { return 128 * dense_nq(); }
+// Query rows per dense work-group (one 32-row query tile per wave).
+int dense_bm() { return 128; }
 
 // Head dimensions the dense kernels are built for: (q/k head, v head) = (192, 128), the default
 // MLA layout 128 nope + 64 rope with v 128, and the other layouts (64 + 64, v 128) = (128, 128),
@@ -140,7 +133,7 @@ struct DenseShape {
   bool fp8;
 };
 DenseShape dense_shape(int dqk, int dv, bool fp8) {
-  DenseShape d{dqk, dv, (dqk == 192 && dv == 128 && !fp8) ? dense_nq() : 1, 1, 128, fp8};
+  DenseShape d{dqk, dv, 1, 1, 128, fp8};
   d.occ = mla::dense_occupancy_of(d.nq, dqk, dv);
   d.bm = mla::dense_rows_per_tile(d.nq, dqk, dv);
   return d;

@@ -65,6 +65,10 @@ struct Shape {
   static constexpr int NW = DQK == 256 ? 8 : 4;
   // operand reads run PF MFMA steps ahead (fewer where registers are short)
   static constexpr int PF = DQK == 256 ? 3 : 6;
+  // The next block's copies are issued one after each of the first S products (256-wide layout;
+  // measured 8 % faster there) or all before them (the others: spreading them measured 6 % slower
+  // on long sequences, where they hold scalar registers through the product loop).
+  static constexpr bool SPREAD_COPIES = DQK == 256;
   static constexpr int K_STAGE_BYTES = BN * DQK * 2;
   static constexpr int V_STAGE_BYTES = BN * DVT * 2;
   static constexpr int KCH = BN * (DQK / 8) / (64 * NW);    // wave-wide 1 KiB copies per K block
@@ -101,12 +105,20 @@ struct DenseCtx {
   int va[S::DVT / 32];               // V rows: + (mt*32 + cc*16 [+8]) * DVT*2 per step
 };
 
-// One work item (wave-uniform): query tile `row0` of sequence b, head h, key blocks [blo, bhi).
+// One work item (wave-uniform): the query tile of sequence b whose local row r is sequence row
+// row0 + r (rows [rlo, rows) of the tile exist), head h, key blocks [blo, bhi).
+// The item's head, key split and output column tile (columns [dvh * DVT, (dvh + 1) * DVT)) share
+// one word: the item stream keeps two items live in scalar registers, where every extra word
+// spills.
 struct Item {
   const char* kbase;  // K of this sequence/head at key 0 (bytes)
   const char* vbase;
-  int cq0, sq, sk, row0, rows, blo, bhi, h, split;
-  int dvh;            // output column tile: columns [dvh * DVT, (dvh + 1) * DVT)
+  int cq0, sq, sk, row0, rows, blo, bhi;
+  int hsd;  // head (bits 0-15), split (16-22), dvh (23)
+  __device__ int h() const { return hsd & 0xFFFF; }
+  __device__ int split() const { return (hsd >> 16) & 0x7F; }
+  __device__ int dvh() const { return (hsd >> 23) & 1; }
+  __device__ int rlo() const { return max(0, -row0); }  // first local row of the sequence
 };
 
 // 32-bit value the optimiser must treat as opaque (keeps precomputed offsets 32-bit at their use
@@ -114,6 +126,29 @@ struct Item {
 __device__ __forceinline__ uint32_t opaque(uint32_t x) {
   asm volatile("" : "+v"(x));
   return x;
+}
+
+// Copy i (of KCH + VCH wave-wide 1 KiB copies: K first, then V) of key block j of an item into
+// a stage. Rows past the end of the sequence re-read its last key (finite values, masked later).
+template <int NQ, class S>
+__device__ __forceinline__ void issue_copy(const DenseCtx<NQ, S>& c, const Item& it, int j, char* kst, char* vst,
+                                           int i) {
+  const int key0 = j * BN;
+  const bool is_k = i < S::KCH;
+  const int ci = is_k ? i : i - S::KCH;
+  const int st_b = is_k ? c.k_st_b : c.v_st_b;
+  const char* base = (is_k ? it.kbase : it.vbase) + (int64_t)key0 * st_b;
+  const uint32_t off = is_k ? c.koff[ci] : c.voff[ci];
+  char* dst = is_k ? kst + c.kdst + ci * 1024 : vst + c.vdst + ci * 1024;
+  if (key0 + BN <= it.sk) {
+    g2lds16(base + opaque(off), dst);
+  } else {
+    const int lane = (int)opaque((uint32_t)c.lane);
+    const int nch = is_k ? S::DQK / 8 : S::DVT / 8;  // 16-byte chunks per row
+    const int r = (int)((uint32_t)((c.wave * (is_k ? S::KCH : S::VCH) + ci) * 64 + lane) / (uint32_t)nch);
+    const int shift = (min(r, it.sk - 1 - key0) - r) * st_b;
+    g2lds16(base + (uint32_t)((int)off + shift), dst);
+  }
 }
 
 template <int NQ, class S>
@@ -128,7 +163,6 @@ __device__ __forceinline__ void issue_block_load(const DenseCtx<NQ, S>& c, const
 #pragma unroll
     for (int i = 0; i < S::VCH; ++i) g2lds16(vb + opaque(c.voff[i]), vst + c.vdst + i * 1024);
   } else {
-    // tail block: rows past the sequence re-read its last key (finite values, masked later)
     const int last = it.sk - 1 - key0;
     const int lane = (int)opaque((uint32_t)c.lane);
 #pragma unroll
@@ -148,7 +182,8 @@ __device__ __forceinline__ void issue_block_load(const DenseCtx<NQ, S>& c, const
 
 // NMT: how many of the block's two 32-key tiles this wave computes (2, or 1 when the second tile
 // is entirely masked for every row of the wave; a wave with both tiles masked skips the block).
-// q_done(kk) runs right after the last product that reads the Q^T fragments qf[.][kk].
+// q_done(kk) runs right after the last product that reads the Q^T fragments qf[.][kk]; copy(st)
+// right after S product st.
 // The kernel's arguments, re-read from the kernel-argument segment at each use: values needed
 // only once per work item are loaded there instead of being held in scalar registers for the
 // whole kernel (the optimiser cannot see through the empty asm, so it cannot hoist the loads).
@@ -158,12 +193,12 @@ __device__ __forceinline__ const DenseParams& kargs() {
   return *(const DenseParams*)kp;
 }
 
-template <int NQ, int NMT, bool MASK, class S, class QDone>
+template <int NQ, int NMT, bool MASK, class S, class QDone, class Copy>
 __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const Item& it, int j,
                                               const char* ks, const char* vs,
                                               bf16x8 (&qf)[NQ][S::DQK / 16], float (&m_run)[NQ],
                                               float (&l_run)[NQ], f32x16 (&o)[NQ][S::DVT / 32],
-                                              float scale_log2, bool causal, QDone&& q_done) {
+                                              float scale_log2, bool causal, QDone&& q_done, Copy&& copy) {
   constexpr int DQK = S::DQK, DV = S::DVT, KA_N = S::KA_N, KA_GROUP = S::KA_GROUP;
   // ---- S^T = K_blk * Q^T: the 32-key tiles are independent accumulator chains, issued
   // alternately, with the K fragments read from LDS PF steps ahead of their MFMA.
@@ -188,6 +223,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
       const int kk = st / NMT, mt = st % NMT;
 #pragma unroll
       for (int nq = 0; nq < NQ; ++nq) s[nq][mt] = mfma32(a[st], qf[nq][kk], s[nq][mt]);
+      copy(st);
       if (mt == NMT - 1) {
         __builtin_amdgcn_sched_barrier(0);  // the old fragments are read before q_done replaces them
         q_done(kk);
@@ -205,7 +241,7 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
   // to local row i iff j < Sk, j <= i + diag (when right-limited: causal or a right window, whose
   // width is folded into diag) and j >= i + dleft (with a left window).
   const int key0 = j * BN;
-  const int qmin = it.row0 + c.wave * 32 * NQ;  // smallest local query row of this wave
+  const int qmin = it.row0 + c.wave * 32 * NQ;  // smallest query row of this wave
   const int wl = kargs().win_left;
   const int diag = it.sk - it.sq + kargs().win_right;  // bottom-right alignment offset (+ right window)
   const int dleft = it.sk - it.sq - wl;
@@ -312,10 +348,11 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
   }
 }
 
-// One key block: optionally issue the copy of block ld_j of item ld into the other stage, then
-// compute block j of item it from the current stage. The stage pointers are restrict-qualified:
-// the two stages never overlap, and saying so lets the compiler order the operand reads of the
-// current stage freely against the copy in flight into the other one.
+// One key block: compute block j of item it from the current stage and, optionally, copy block
+// ld_j of item ld into the other stage (the copies issued before the S products, or spread over
+// them). The stage pointers are restrict-qualified: the two stages never overlap, and saying so
+// lets the compiler order the operand reads of the current stage freely against the copy in
+// flight into the other one.
 template <int NQ, int NMT, bool MASK, class S, class QDone>
 __device__ __forceinline__ void block_step(const DenseCtx<NQ, S>& c, const Item& it, int j, const Item& ld,
                                            int ld_j, bool do_load, char* __restrict__ kn,
@@ -324,8 +361,11 @@ __device__ __forceinline__ void block_step(const DenseCtx<NQ, S>& c, const Item&
                                            float (&m_run)[NQ], float (&l_run)[NQ],
                                            f32x16 (&o)[NQ][S::DVT / 32], float scale_log2, bool causal,
                                            QDone&& q_done) {
-  if (do_load) issue_block_load(c, ld, ld_j, kn, vn);
-  compute_block<NQ, NMT, MASK>(c, it, j, kc, vc, qf, m_run, l_run, o, scale_log2, causal, q_done);
+  static_assert(!S::SPREAD_COPIES || S::KCH + S::VCH <= NMT * (S::DQK / 16), "one copy per S product");
+  if (!S::SPREAD_COPIES && do_load) issue_block_load(c, ld, ld_j, kn, vn);
+  compute_block<NQ, NMT, MASK>(c, it, j, kc, vc, qf, m_run, l_run, o, scale_log2, causal, q_done, [&](int st) {
+    if (S::SPREAD_COPIES && st < S::KCH + S::VCH && do_load) issue_copy(c, ld, ld_j, kn, vn, st);
+  });
 }
 
 // Read-only metadata (plan, cu_seqlens, sink, item count) is read through the constant address
@@ -412,30 +452,34 @@ __device__ __forceinline__ Item make_item(int item, int h, int split, int dvh) {
   it.sq = f[1];
   const int ck0 = f[2];
   it.sk = f[3];
-  it.row0 = m * 32 * S::NW * NQ;
-  it.rows = min(32 * S::NW * NQ, it.sq - it.row0);
+  // Query tiles are aligned to the end of the sequence: tile m holds rows [m*BM - pad, (m+1)*BM -
+  // pad) with pad = ceil(Sq/BM)*BM - Sq, so the leftover Sq mod BM rows form the first tile, whose
+  // rows see the fewest keys under a causal mask.
+  constexpr int bm = 32 * S::NW * NQ;
+  it.row0 = m * bm - ((it.sq + bm - 1) / bm * bm - it.sq);
+  it.rows = min(bm, it.sq - it.row0);
   // with a left window the item's blocks start at the block of the first key its first row sees
-  const int blk0 = p.win_left >= 0 ? min(max(it.row0 + it.sk - it.sq - p.win_left, 0), it.sk) / BN : 0;
+  const int blk0 =
+      p.win_left >= 0 ? min(max(it.row0 + it.rlo() + it.sk - it.sq - p.win_left, 0), it.sk) / BN : 0;
   it.blo = blk0 + (int)(((int64_t)split * nb) / p.num_splits);
   it.bhi = blk0 + (int)(((int64_t)(split + 1) * nb) / p.num_splits);
-  it.h = h;
-  it.split = split;
-  it.dvh = dvh;
+  it.hsd = h | (split << 16) | (dvh << 23);
   it.kbase = reinterpret_cast<const char*>(p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh);
   it.vbase = reinterpret_cast<const char*>(p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh + dvh * S::DVT);
   return it;
 }
 
-// Q^T fragments of this wave's query columns. Rows past the tile re-read its last row: their
-// scores stay finite and their outputs are never stored, so no zeroing (and no wait) is needed.
+// Q^T fragments of this wave's query columns. Rows outside the sequence re-read its nearest row
+// of the tile: their scores stay finite and their outputs are never stored, so no zeroing (and no
+// wait) is needed.
 template <int NQ, class S>
 __device__ __forceinline__ void q_rows(const DenseCtx<NQ, S>& c, const Item& it, const __bf16* (&qp)[NQ]) {
   const DenseParams& p = kargs();
 #pragma unroll
   for (int nq = 0; nq < NQ; ++nq) {
     const int lane = (int)opaque((uint32_t)c.lane);
-    const int r = min(c.wave * 32 * NQ + nq * 32 + (lane & 31), it.rows - 1);
-    qp[nq] = p.q + (int64_t)(it.cq0 + it.row0 + r) * p.q_st + (int64_t)it.h * p.q_sh + (lane >> 5) * 8;
+    const int r = min(max(c.wave * 32 * NQ + nq * 32 + (lane & 31), it.rlo()), it.rows - 1);
+    qp[nq] = p.q + (int64_t)(it.cq0 + it.row0 + r) * p.q_st + (int64_t)it.h() * p.q_sh + (lane >> 5) * 8;
   }
 }
 
@@ -466,7 +510,7 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
   constexpr int ESZ = S::FP8 ? 1 : 2;  // output element bytes
   // The arguments are read once, before any store (a store could otherwise be taken to change them).
   const DenseParams& p = kargs();
-  const int h = it.h;
+  const int h = it.h();
   const float scale = p.scale;
   float* const o_part = p.o_part;
   float* const lse_part = p.lse_part;
@@ -475,12 +519,12 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
   const bool accumulate = p.accumulate != 0;
   const bool final_merge = p.accumulate == 2;
   const bool to_part = o_part != nullptr && !final_merge;
-  const int64_t part_row = (int64_t)it.split * p.total_q;  // split-mode row base
+  const int64_t part_row = (int64_t)it.split() * p.total_q;  // split-mode row base
   const int num_heads = p.num_heads;
-  char* const out_h = static_cast<char*>(p.out) + ((int64_t)h * p.o_sh + it.dvh * DV) * ESZ;
+  char* const out_h = static_cast<char*>(p.out) + ((int64_t)h * p.o_sh + it.dvh() * DV) * ESZ;
   // every column tile of a row computes the same LSE; the first one stores it (the running
   // merge of accumulate mode is used with a single tile only)
-  const bool store_lse = it.dvh == 0;
+  const bool store_lse = it.dvh() == 0;
   const int64_t o_st_b = p.o_st * ESZ;
   float* const lse = p.lse;
   const int64_t l_st = p.l_st, l_sh = p.l_sh;
@@ -509,12 +553,12 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
         lse_v = mx + __logf(z);
       }
     }
-    if (r < it.rows) {
+    if (r >= it.rlo() && r < it.rows) {
       const int tok = it.cq0 + it.row0 + r;
       if (final_merge) {
         // the running result merged with this one, normalised, then the sink folded in; the
         // merged values replace the accumulators for the output path below
-        const float* op = o_part + ((int64_t)tok * num_heads + h) * S::DV + it.dvh * DV;
+        const float* op = o_part + ((int64_t)tok * num_heads + h) * S::DV + it.dvh() * DV;
         const float l_old = lse_part[(int64_t)tok * num_heads + h];
         f32x4 old[DV / 32][4];
 #pragma unroll
@@ -549,7 +593,7 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
         inv = 1.f;
       }
       if (to_part) {
-        float* op = o_part + ((part_row + tok) * num_heads + h) * S::DV + it.dvh * DV;
+        float* op = o_part + ((part_row + tok) * num_heads + h) * S::DV + it.dvh() * DV;
         float* lp = lse_part + (part_row + tok) * num_heads + h;
         float w_new = inv, w_old = 0.f;
         f32x4 old[DV / 32][4];
@@ -629,7 +673,7 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int rr = i * 8 + (lane >> 3);
-          if (r0 + rr < it.rows)
+          if (r0 + rr >= it.rlo() && r0 + rr < it.rows)
             *reinterpret_cast<u32x4*>(out_h + (int64_t)(it.cq0 + it.row0 + r0 + rr) * o_st_b + seg * 128 + cc * 16) = v[i];
         }
       }
@@ -765,7 +809,8 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
   f32x16 o[NQ][DV / 32];
   int st = 0;  // stage holding the next block to compute
 
-  Item cur = make_item<NQ, S>(wi, wh, wsplit, wdvh);
+  auto new_item = [&]() { return make_item<NQ, S>(wi, wh, wsplit, wdvh); };
+  Item cur = new_item();
   load_q(c, cur, qf);
   if (cur.blo < cur.bhi) issue_block_load(c, cur, cur.blo, stage_k(st), stage_v(st));
   wait_vmem();
@@ -781,6 +826,11 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
       for (int dt = 0; dt < DV / 32; ++dt) o[nq][dt] = f32x16{};
     }
     const bool had_blocks = cur.blo < cur.bhi;
+    // This wave's query rows [qlo, qlo + 32*NQ); a wave holding no row of the sequence (in the first
+    // tile of a sequence whose length is not a multiple of the tile height) only copies.
+    const int first = cur.row0 + cur.rlo();  // first sequence row of the tile
+    const int qlo = cur.row0 + c.wave * 32 * NQ;
+    const bool active = qlo + 32 * NQ > first && qlo < cur.row0 + cur.rows;
     // Hand-over to the next item: its ticket is fetched at the start of block fetch_j, shared at
     // the start of block share_j (where its descriptor is built), and the last block copies its
     // first key block and loads its Q^T fragments. Sharing waits for the ticket, so it comes at
@@ -796,27 +846,27 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
       const int diag = cur.sk - cur.sq + p.win_right;
       int jd = cur.sk / BN;
       if (causal) {
-        const int x = cur.row0 + diag - (BN - 1);
+        const int x = first + diag - (BN - 1);
         jd = min(jd, x < 0 ? 0 : x / BN + 1);
       }
       const int jm = max(cur.blo, min(jd, cur.bhi - 2));
       // Per wave, only the leading 32-key tiles holding a key visible to some row of the wave
       // are computed (0, 1 or 2; wave-uniform).
-      const int qmax = cur.row0 + c.wave * 32 * NQ + 32 * NQ - 1;  // largest local query row
-      const int vis_end = min(cur.sk, causal ? qmax + diag + 1 : cur.sk);
+      const int qmax = qlo + 32 * NQ - 1;  // largest query row of this wave
+      const int vis_end = !active ? 0 : min(cur.sk, causal ? qmax + diag + 1 : cur.sk);
 
       auto no_q = [](int) {};
       auto prepare = [&](int jj) {  // at the start of block jj, before its copy
         if (jj == fetch_j) fetch();
         if (jj == share_j) {
           has_next = take(st ^ 1);
-          if (has_next) nxt = make_item<NQ, S>(wi, wh, wsplit, wdvh);
+          if (has_next) nxt = new_item();
         }
       };
       int j = cur.blo;
       // With a left window, the blocks holding a key below the window of the tile's last row need
       // the mask; they come first (at most up to the last block, which runs below).
-      if (p.win_left >= 0) {
+      if (p.win_left >= 0 && active) {
         const int x = cur.row0 + cur.rows - 1 + cur.sk - cur.sq - p.win_left;  // last row's first key
         const int jl = min(x <= 0 ? 0 : (x + BN - 1) / BN, cur.bhi - 1);
         for (; j < jl; ++j, st ^= 1) {
@@ -827,17 +877,19 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
           __syncthreads();
         }
       }
-      for (; j < jm; ++j, st ^= 1) {
+      // (an inactive wave runs every block but the last in the loop below, where it only copies:
+      // the waves' barriers stay in step, as no ticket is shared before block jm)
+      for (const int jm_w = active ? jm : j; j < jm_w; ++j, st ^= 1) {
         if (j == fetch_j) fetch();
-        block_step<NQ, 2, false>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st), stage_v(st),
-                                 qf, m_run, l_run, o, p.scale_log2, causal, no_q);
+        block_step<NQ, 2, false>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st),
+                                 stage_v(st), qf, m_run, l_run, o, p.scale_log2, causal, no_q);
         wait_vmem();
         __syncthreads();
       }
       // The one-tile body exists only for one query tile per wave (with two, a second copy of the
       // body does not fit the register file). A wave with no visible key in the block only copies.
       for (; j < cur.bhi - 1; ++j, st ^= 1) {
-        prepare(j);
+        prepare(j);  // before jm, at most the fetch, as in the loop above
         const int rem = vis_end - j * BN;
         if (rem > 32 || (NQ > 1 && rem > 0))
           block_step<NQ, 2, true>(c, cur, j, cur, j + 1, true, stage_k(st ^ 1), stage_v(st ^ 1), stage_k(st), stage_v(st),
@@ -877,7 +929,7 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
     // in the other), or, for an item without blocks, the one the next item will be copied into.
     store_item(c, cur, m_run, l_run, o, had_blocks ? stage_k(st ^ 1) : stage_k(st));
     if (!has_next) break;
-    cur = had_blocks ? nxt : make_item<NQ, S>(wi, wh, wsplit, wdvh);
+    cur = had_blocks ? nxt : new_item();
     if (!had_blocks) {  // nothing was handed over: start the next item from scratch
       load_q(c, cur, qf);
       if (cur.blo < cur.bhi) issue_block_load(c, cur, cur.blo, stage_k(st), stage_v(st));
@@ -895,7 +947,6 @@ using Shape256 = Shape<256, 256, false>;
 using Shape256F8 = Shape<256, 256, true>;
 
 template __global__ void dense_fwd_kernel<1, Shape192>(DenseParams);
-template __global__ void dense_fwd_kernel<2, Shape192>(DenseParams);
 template __global__ void dense_fwd_kernel<1, Shape192F8>(DenseParams);
 template __global__ void dense_fwd_kernel<1, Shape128>(DenseParams);
 template __global__ void dense_fwd_kernel<1, Shape128F8>(DenseParams);
@@ -908,14 +959,12 @@ static void launch_one(const DenseParams& p, int grid, hipStream_t stream) {
 }
 
 int dense_occupancy_of(int nq, int dqk, int dv) {
-  if (nq == 2) return dense_occupancy<2, Shape192>();
   if (dqk == 256 && dv == 256) return dense_occupancy<1, Shape256>();
   if (dqk == 128 && dv == 128) return dense_occupancy<1, Shape128>();
   return dense_occupancy<1, Shape192>();
 }
 
 int dense_rows_per_tile(int nq, int dqk, int dv) {
-  if (nq == 2) return 32 * Shape192::NW * 2;
   if (dqk == 256 && dv == 256) return 32 * Shape256::NW;
   if (dqk == 128 && dv == 128) return 32 * Shape128::NW;
   return 32 * Shape192::NW;
@@ -926,7 +975,6 @@ hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool 
   if (grid <= 0) return hipSuccess;
   if (dqk == 192 && dv == 128) {
     if (fp8_out) launch_one<1, Shape192F8>(p, grid, stream);
-    else if (nq == 2) launch_one<2, Shape192>(p, grid, stream);
     else launch_one<1, Shape192>(p, grid, stream);
   } else if (dqk == 128 && dv == 128) {
     if (fp8_out) launch_one<1, Shape128F8>(p, grid, stream);

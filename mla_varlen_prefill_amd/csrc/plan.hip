@@ -3,10 +3,13 @@
 //
 // Prior art: a device-side planner for ragged batches with a counter-clearing helper (page "Mojo
 // module mla", mla_prefill_plan_kernel, set_buffer_lengths_to_zero); a metadata call that fills
-// an int32 task table before the attention operator (page "SparseFlashMla", Description). The format is this library's own:
-// items (b, m, n_blocks, kv_end), sequence by sequence (sequences with more key blocks first,
-// ties by b) and within a sequence from its last query tile to its first (with a left window:
-// n_blocks descending, then slot ascending), unused entries -1.
+// an int32 task table before the attention operator (page "SparseFlashMla", Description). The
+// format is this library's own: items (b, m, n_blocks, kv_end) for query tiles aligned to the end
+// of each sequence (tile m holds rows [m*BM - pad, (m+1)*BM - pad), pad = ceil(Sq/BM)*BM - Sq, so
+// the Sq mod BM leftover rows form tile 0, where causal rows see the fewest keys), sequence by
+// sequence (sequences with more key blocks first, ties by b) and within a sequence from its last
+// query tile to its first (with a left window: n_blocks descending, then slot ascending), unused
+// entries -1.
 // With a left window n_blocks counts from the block of the first key the tile's first row sees
 // (the dense kernel recomputes that block). Long work goes first, and the tiles in flight at
 // any time come from few sequences, whose keys and values then stay in L2.
@@ -33,13 +36,16 @@ __device__ __forceinline__ Item slot_item(const PlanParams& p, int s) {
   const int sk = p.cu_k[it.b + 1] - it.ck0;
   it.sq = sq;
   it.sk = sk;
-  it.valid = it.m * p.bm < sq;
+  // tile m holds rows [row0, row0 + bm) of the sequence that exist: tiles end at the sequence end
+  const int n_tiles = (sq + p.bm - 1) / p.bm;
+  const int row0 = it.m * p.bm - (n_tiles * p.bm - sq);
+  it.valid = it.m < n_tiles;
   int kv_end = sk;
   if (p.causal) {
-    const int i_last = min((it.m + 1) * p.bm, sq) - 1;
+    const int i_last = row0 + p.bm - 1;
     kv_end = min(max(i_last + sk - sq + p.win_right + 1, 0), sk);
   }
-  const int kv_start = p.win_left >= 0 ? min(max(it.m * p.bm + sk - sq - p.win_left, 0), sk) : 0;
+  const int kv_start = p.win_left >= 0 ? min(max(max(row0, 0) + sk - sq - p.win_left, 0), sk) : 0;
   it.kv_end = kv_end;
   it.nb = kv_end <= kv_start ? 0 : (kv_end + p.bn - 1) / p.bn - kv_start / p.bn;
   return it;

@@ -13,13 +13,17 @@ own.
 Plan format
 -----------
 Slots: ``slot = b * Mt + m`` for sequence ``b`` in [0, B) and query tile ``m`` in [0, Mt) with
-``Mt = ceil(max_seqlen_q / BM)``. A slot is a work item iff ``m * BM < Sq_b``.
+``Mt = ceil(max_seqlen_q / BM)``. A slot is a work item iff ``m < T_b = ceil(Sq_b / BM)``.
+Query tiles are aligned to the end of their sequence: tile ``m`` holds the rows
+``[m*BM - pad_b, (m+1)*BM - pad_b)`` that exist, with ``pad_b = T_b*BM - Sq_b`` (the leftover
+``Sq_b mod BM`` rows form tile 0, where causal rows see the fewest keys); see ``tile_rows``.
 
 For an item: ``kv_end`` is the number of leading keys any row of the tile can see:
 ``Sk_b`` without a right limit; with the bottom-right causal mask (right window 0) or a right
-window ``r >= 0`` it is ``clamp(i_last + Sk_b - Sq_b + r + 1, 0, Sk_b)`` where
-``i_last = min((m+1)*BM, Sq_b) - 1``. With a left window ``l >= 0`` the first key any row can see
-is ``kv_start = clamp(m*BM + Sk_b - Sq_b - l, 0, Sk_b)`` (else 0). ``n_blocks`` counts the key
+window ``r >= 0`` it is ``clamp(i_last + Sk_b - Sq_b + r + 1, 0, Sk_b)`` where ``i_last`` is the
+tile's last row. With a left window ``l >= 0`` the first key any row can see is
+``kv_start = clamp(i_first + Sk_b - Sq_b - l, 0, Sk_b)`` with ``i_first`` the tile's first row
+(else 0). ``n_blocks`` counts the key
 blocks from ``kv_start // BN`` up to ``ceil(kv_end / BN)``, and is 0 when ``kv_end <= kv_start``;
 without a left window it is ``ceil(kv_end / BN)``. The dense kernel recomputes ``kv_start // BN``
 from ``(m, Sq_b, Sk_b, l)``.
@@ -42,6 +46,13 @@ SORT_CAPACITY = 16384
 MAX_BLOCKS = 0x3FFFE
 
 
+def tile_rows(sq: int, m: int, bm: int) -> Tuple[int, int]:
+    """Rows [first, last] of sequence rows held by query tile m (tiles aligned to the sequence end)."""
+    n_tiles = -(-sq // bm)
+    row0 = m * bm - (n_tiles * bm - sq)
+    return max(row0, 0), row0 + bm - 1
+
+
 def plan_items(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: int, bn: int,
                causal: bool, window: Tuple[int, int] = (-1, -1)) -> list:
     """The work items as (b, m, n_blocks, kv_end) tuples, in plan order; window = (left, right),
@@ -55,15 +66,13 @@ def plan_items(cu_q: Sequence[int], cu_k: Sequence[int], max_seqlen_q: int, bm: 
     for b in range(b_count):
         sq = int(cu_q[b + 1]) - int(cu_q[b])
         sk = int(cu_k[b + 1]) - int(cu_k[b])
-        for m in range(mt):
-            if m * bm >= sq:
-                continue
+        for m in range(-(-sq // bm)):
+            i_first, i_last = tile_rows(sq, m, bm)
             if right >= 0:
-                i_last = min((m + 1) * bm, sq) - 1
                 kv_end = min(max(i_last + sk - sq + right + 1, 0), sk)
             else:
                 kv_end = sk
-            kv_start = min(max(m * bm + sk - sq - left, 0), sk) if left >= 0 else 0
+            kv_start = min(max(i_first + sk - sq - left, 0), sk) if left >= 0 else 0
             n_blocks = 0 if kv_end <= kv_start else -(-kv_end // bn) - kv_start // bn
             if left < 0:
                 order = (-min(-(-sk // bn), MAX_BLOCKS), b, -m)

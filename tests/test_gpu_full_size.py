@@ -27,17 +27,21 @@ SLAB = 32  # query rows per wave
 
 def item_rows(lens_q, bm, seed):
     """Global query rows: per sequence and query tile, one row in each 32-row wave slab of the tile
-    (the tile's last row for the last slab), restricted to the sequence."""
+    that holds rows of the sequence (the tile's last row for the last slab). Tiles are aligned to
+    the sequence end: local row r of tile m is sequence row m*bm - pad + r, pad = ceil(sq/bm)*bm - sq."""
     rng = np.random.default_rng(seed)
     cu = cu_from_lens(lens_q)
     rows = []
     for b, sq in enumerate(lens_q):
+        pad = -(-sq // bm) * bm - sq
         for m in range(-(-sq // bm)):
-            top = min(bm, sq - m * bm)
-            for w in range(-(-top // SLAB)):
-                lo, hi = w * SLAB, min((w + 1) * SLAB, top)
-                r = hi - 1 if hi == top else int(rng.integers(lo, hi))
-                rows.append(int(cu[b]) + m * bm + r)
+            row0 = m * bm - pad
+            for w in range(bm // SLAB):
+                lo, hi = max(w * SLAB, -row0), (w + 1) * SLAB
+                if lo >= hi:
+                    continue
+                r = hi - 1 if hi == bm else int(rng.integers(lo, hi))
+                rows.append(int(cu[b]) + row0 + r)
     return np.asarray(sorted(set(rows)), dtype=np.int64)
 
 

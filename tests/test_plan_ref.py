@@ -11,8 +11,28 @@ from oracle.mla_oracle import dense_visible
 from workloads import cu_from_lens
 
 
+def _tile(sq, m, bm):
+    """Rows of query tile m: tiles are aligned to the sequence end, so row r belongs to tile
+    (r + pad) // bm with pad = ceil(sq / bm) * bm - sq."""
+    pad = -(-sq // bm) * bm - sq
+    r = np.arange(sq)
+    return r[(r + pad) // bm == m]
+
+
+def test_tile_rows_partition_the_sequence():
+    for sq, bm in [(1, 128), (127, 128), (128, 128), (129, 128), (1726, 128), (300, 64), (5, 16)]:
+        t = -(-sq // bm)
+        tiles = [_tile(sq, m, bm) for m in range(t)]
+        assert np.array_equal(np.concatenate(tiles), np.arange(sq))
+        assert all(len(x) == bm for x in tiles[1:]) and 1 <= len(tiles[0]) <= bm
+        assert tiles[-1][-1] == sq - 1
+        for m in range(t):
+            first, last = plan_ref.tile_rows(sq, m, bm)
+            assert (first, last) == (int(tiles[m][0]), int(tiles[m][-1]))
+
+
 def _brute_kv_end(sq, sk, m, bm, causal):
-    rows = np.arange(m * bm, min((m + 1) * bm, sq))
+    rows = _tile(sq, m, bm)
     vis = dense_visible(sq, sk, causal, rows=rows)
     cols = np.nonzero(vis.any(axis=0))[0]
     return 0 if cols.size == 0 else int(cols.max()) + 1
@@ -60,7 +80,7 @@ def test_plan_items_window_extent_brute_force(lens_q, lens_k, causal, window, bm
     assert len(items) == sum(-(-sq // bm) for sq in lens_q)
     for (b, m, nb, kv_end) in items:
         sq, sk = lens_q[b], lens_k[b]
-        rows = np.arange(m * bm, min((m + 1) * bm, sq))
+        rows = _tile(sq, m, bm)
         cols = np.nonzero(dense_visible(sq, sk, causal, rows=rows, window=window).any(axis=0))[0]
         if cols.size == 0:
             assert nb == 0
@@ -69,7 +89,7 @@ def test_plan_items_window_extent_brute_force(lens_q, lens_k, causal, window, bm
         assert kv_end == int(cols.max()) + 1
         assert nb == hi_blk - lo_blk
         left = window[0]
-        kv_start = min(max(m * bm + sk - sq - left, 0), sk) if left >= 0 else 0
+        kv_start = min(max(int(rows[0]) + sk - sq - left, 0), sk) if left >= 0 else 0
         assert kv_start // bn == lo_blk
     mt = -(-max(lens_q) // bm)
     if window[0] >= 0:   # longest first, ties by slot
@@ -86,6 +106,9 @@ def test_plan_buffer_fill_and_capacity():
     assert np.all(buf[n:] == -1)
     assert buf[0].tolist() == [1, 3, 4, 200]   # the sequence with more keys first, from its last tile
     assert buf[1:4, 1].tolist() == [2, 1, 0] and buf[4].tolist()[:2] == [0, 0]
+    # tiles end at the sequence end: tile 0 of the 200-row sequence holds rows 0..7 (pad 56), so
+    # under the causal mask it sees 8 keys in one block; tile 1 holds rows 8..71
+    assert buf[3].tolist() == [1, 0, 1, 8] and buf[2].tolist() == [1, 1, 2, 72]
     with pytest.raises(ValueError):
         plan_ref.plan_buffer(cu, cu, 200, 64, 64, True, capacity=4)
 
