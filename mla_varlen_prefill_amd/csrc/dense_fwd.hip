@@ -414,6 +414,10 @@ __device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& ite
       const int k = r / xu;
       item = n_long + k;
       u = xcd * xu + (r - k * xu);
+    } else if (gu == 1) {  // one unit per group: no division by the group size
+      const int grp = i / n_long;
+      item = i - grp * n_long;
+      u = xcd * xu + grp;
     } else {
       const int per_group = n_long * gu;
       const int grp = i / per_group;
@@ -434,7 +438,7 @@ __device__ __forceinline__ bool decode_pos(int n_items, int xcd, int i, int& ite
   }
   const int hs = S::DVH == 1 ? u : u / S::DVH;
   dvh = u - hs * S::DVH;
-  h = hs / p.num_splits;
+  h = p.num_splits == 1 ? hs : hs / p.num_splits;
   split = hs - h * p.num_splits;
   return true;
 }
@@ -461,8 +465,13 @@ __device__ __forceinline__ Item make_item(int item, int h, int split, int dvh) {
   // with a left window the item's blocks start at the block of the first key its first row sees
   const int blk0 =
       p.win_left >= 0 ? min(max(it.row0 + it.rlo() + it.sk - it.sq - p.win_left, 0), it.sk) / BN : 0;
-  it.blo = blk0 + (int)(((int64_t)split * nb) / p.num_splits);
-  it.bhi = blk0 + (int)(((int64_t)(split + 1) * nb) / p.num_splits);
+  if (p.num_splits == 1) {  // (the common case: no 64-bit division)
+    it.blo = blk0;
+    it.bhi = blk0 + nb;
+  } else {
+    it.blo = blk0 + (int)(((int64_t)split * nb) / p.num_splits);
+    it.bhi = blk0 + (int)(((int64_t)(split + 1) * nb) / p.num_splits);
+  }
   it.hsd = h | (split << 16) | (dvh << 23);
   it.kbase = reinterpret_cast<const char*>(p.k + (int64_t)ck0 * p.k_st + (int64_t)h * p.k_sh);
   it.vbase = reinterpret_cast<const char*>(p.v + (int64_t)ck0 * p.v_st + (int64_t)h * p.v_sh + dvh * S::DVT);
