@@ -66,8 +66,8 @@ struct Shape {
   // operand reads run PF MFMA steps ahead (fewer where registers are short)
   static constexpr int PF = DQK == 256 ? 3 : 6;
   // The next block's copies are issued one after each of the first S products (256-wide layout;
-  // measured 8 % faster there) or all before them (the others: spreading them measured 6 % slower
-  // on long sequences, where they hold scalar registers through the product loop).
+  // measured 8 % faster there) or all after the first one (the others: spreading them measured 6 %
+  // slower on long sequences, where they hold scalar registers through the product loop).
   static constexpr bool SPREAD_COPIES = DQK == 256;
   static constexpr int K_STAGE_BYTES = BN * DQK * 2;
   static constexpr int V_STAGE_BYTES = BN * DVT * 2;
@@ -349,8 +349,9 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
 }
 
 // One key block: compute block j of item it from the current stage and, optionally, copy block
-// ld_j of item ld into the other stage (the copies issued before the S products, or spread over
-// them). The stage pointers are restrict-qualified: the two stages never overlap, and saying so
+// ld_j of item ld into the other stage (the copies issued together right after the first S
+// product, which then runs while the copies queue: 1 % faster than before it; or spread over
+// the S products). The stage pointers are restrict-qualified: the two stages never overlap, and saying so
 // lets the compiler order the operand reads of the current stage freely against the copy in
 // flight into the other one.
 template <int NQ, int NMT, bool MASK, class S, class QDone>
@@ -362,9 +363,9 @@ __device__ __forceinline__ void block_step(const DenseCtx<NQ, S>& c, const Item&
                                            f32x16 (&o)[NQ][S::DVT / 32], float scale_log2, bool causal,
                                            QDone&& q_done) {
   static_assert(!S::SPREAD_COPIES || S::KCH + S::VCH <= NMT * (S::DQK / 16), "one copy per S product");
-  if (!S::SPREAD_COPIES && do_load) issue_block_load(c, ld, ld_j, kn, vn);
   compute_block<NQ, NMT, MASK>(c, it, j, kc, vc, qf, m_run, l_run, o, scale_log2, causal, q_done, [&](int st) {
     if (S::SPREAD_COPIES && st < S::KCH + S::VCH && do_load) issue_copy(c, ld, ld_j, kn, vn, st);
+    if (!S::SPREAD_COPIES && st == 0 && do_load) issue_block_load(c, ld, ld_j, kn, vn);
   });
 }
 
