@@ -109,7 +109,7 @@ hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int
                            hipStream_t stream);
 hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream);
 // Dense kernel instances: (dqk, dv) in {(192, 128), (128, 128), (256, 256)}, bf16 or fp8 output;
-// nq = 2 (256-row query tiles) only for (192, 128) with bf16 output.
+// nq (query tiles per wave) is 1.
 hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool fp8_out, hipStream_t stream);
 // Resident work-groups per CU of the instance.
 int dense_occupancy_of(int nq, int dqk, int dv);
