@@ -20,11 +20,11 @@
 //     MFMA (two 16-key tiles, 18 steps each); online softmax per head across the four lanes that
 //     hold a head column; O^T (512 x 16) += V~^T (A, transposed LDS reads of the same rows) * P^T
 //     (B, the S^T registers converted to bf16 in place).
-//   * The reference max of a head is fixed by the first block with a visible key, so the
-//     accumulator is never rescaled (P may reach 2^32, well inside fp32/bf16 range). The exact
-//     running max is tracked too; if any head's max exceeds its reference by more than 2^32, the
-//     work-group runs the slots a second time with the exact max (rare; never for rows whose
-//     logits span less than about 22 nats).
+//   * A head's reference logit is the largest logit of the first block in which it sees a key, so
+//     the block maximum is only computed while some head of the wave has no reference yet, and
+//     the accumulator is not rescaled in the steady state. A block whose running sum would pass
+//     2^64 (a logit some 44 nats above the reference) is redone against its exact maximum, with
+//     the accumulated O and l rescaled.
 // LDS layout of a gathered block: rows padded to 73 chunks of 16 bytes (1168 B), so row r
 // starts on 16-byte bank group 9r mod 16 of the 256-byte (64-bank) window. The LDS serves a
 // 16-byte read in four cycles of 16 lanes, each cycle taking the 4-lane quads of one half-wave
@@ -58,7 +58,10 @@ constexpr int COPIES_PER_WAVE = (COPIES + NWAVES - 1) / NWAVES;  // 5 (extra slo
 constexpr int KSTEPS = D / 32;                          // 18 MFMA steps of depth 32
 constexpr int DTILES = DVS / 16;                        // 32 output tiles of 16 columns
 constexpr int IDX_WIN = 2048;                           // index slots staged in LDS at a time
-constexpr float kFlushLog2 = 32.f;                      // P may grow to 2^32 (see the second pass)
+// A head's probabilities are taken against a reference logit (see compute_block); a block whose
+// running sum would pass 2^64 is redone against its exact maximum (P stays far inside bf16 / fp32
+// range, and O = sum P V inside fp32 range for any bf16 V).
+constexpr float kOverflowSum = 18446744073709551616.f;  // 2^64
 
 // LDS row of key k within a block, and its inverse.
 __device__ __forceinline__ int key_row(int k) {
@@ -81,7 +84,20 @@ struct SparseCtx {
   const int32_t* bt_row;   // paged cache: block-table row of the token's sequence (else null)
   int used;                // paged cache: logical positions [0, used) may be valid
   int bs, nblocks;         // paged cache: block size, number of blocks
+  // Gather map of this lane's copies (two per word, 12 bits each: row_key of the slot's row in
+  // bits 0-4, its 16-byte chunk in bits 5-11): the same for every block, so computed once.
+  uint32_t gmap[(COPIES_PER_WAVE + 1) / 2];
 };
+
+// Row-key index and chunk of copy i of this lane (see SparseCtx::gmap).
+__device__ __forceinline__ uint32_t gather_map_entry(int wave, int lane, int i) {
+  const int q = min(wave + NWAVES * i, COPIES - 1);
+  const int slot = q * 64 + lane;
+  const int row = min(slot / ROW_CHUNKS, BNS - 1);
+  const int ch = slot - (slot / ROW_CHUNKS) * ROW_CHUNKS;
+  const int chunk = (slot / ROW_CHUNKS >= BNS || ch >= CHUNKS) ? 0 : ch;
+  return (uint32_t)row_key(row) | ((uint32_t)chunk << 5);
+}
 
 // Stage index slots [win0, win0 + IDX_WIN) of this token in LDS (entries past `len` read as -1).
 // All loads are issued before any is used (slots past the row's end read its slot 0, which
@@ -125,31 +141,33 @@ __device__ __forceinline__ void stage_indices(const SparseCtx& c, int tid) {
 // last copy repeat it; identical bytes), so the vector-memory counter advances uniformly per
 // block. Pad chunks and the stage tail receive harmless copies of chunk 0 of a valid row.
 // Wave 0 also publishes the block's validity mask (bit k = key k).
+// SMALL: the latent pool spans less than 4 GiB, so a copy's source is a scalar base plus a 32-bit
+// lane offset (no 64-bit address arithmetic per copy).
+template <bool SMALL>
 __device__ __forceinline__ void issue_gather(const SparseParams& p, const SparseCtx& c, int j,
                                              char* stage, uint32_t* mask_slot) {
   const int base = j * BNS - c.win0;
-  // The per-copy row/chunk arithmetic is a handful of integer ops; an opaque copy of the lane id
-  // keeps the compiler from hoisting it out of the block loop into registers it would spill.
-  int lane = c.lane;
-  asm volatile("" : "+v"(lane));
   // All index reads first, then all copies: the copies write LDS, so the compiler would otherwise
   // keep each index read behind the previous copy and wait for it on its own (one LDS round trip
   // per copy instead of one per block).
   int rid[COPIES_PER_WAVE], chunk[COPIES_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < COPIES_PER_WAVE; ++i) {
-    const int q = min(c.wave + NWAVES * i, COPIES - 1);
-    const int slot = q * 64 + lane;
-    const int row = min(slot / ROW_CHUNKS, BNS - 1);
-    const int ch = slot - (slot / ROW_CHUNKS) * ROW_CHUNKS;
-    chunk[i] = (slot / ROW_CHUNKS >= BNS || ch >= CHUNKS) ? 0 : ch;
-    rid[i] = c.idx[base + row_key(row)];
+    const uint32_t e = c.gmap[i >> 1] >> (12 * (i & 1));
+    chunk[i] = (int)((e >> 5) & 127u);
+    rid[i] = c.idx[base + (int)(e & 31u)];
   }
 #pragma unroll
   for (int i = 0; i < COPIES_PER_WAVE; ++i) {
     const int q = min(c.wave + NWAVES * i, COPIES - 1);
-    const int r = (rid[i] >= 0 && (int64_t)rid[i] < p.n_kv) ? rid[i] : 0;
-    g2lds16(p.kv + (int64_t)r * p.kv_st + chunk[i] * 8, stage + q * 1024);
+    if (SMALL) {
+      const int r = (uint32_t)rid[i] < (uint32_t)p.n_kv ? rid[i] : 0;
+      const uint32_t off = (uint32_t)r * (uint32_t)(p.kv_st * 2) + (uint32_t)chunk[i] * 16u;
+      g2lds16(reinterpret_cast<const char*>(p.kv) + off, stage + q * 1024);
+    } else {
+      const int r = (rid[i] >= 0 && (int64_t)rid[i] < p.n_kv) ? rid[i] : 0;
+      g2lds16(p.kv + (int64_t)r * p.kv_st + chunk[i] * 8, stage + q * 1024);
+    }
   }
   if (c.wave == 0) {
     const int rid = c.idx[base + (c.lane & 31)];
@@ -173,8 +191,7 @@ __device__ __forceinline__ void wait_gather(int newer) {
 
 __device__ __forceinline__ void compute_block(const SparseCtx& c, const char* stage, uint32_t valid,
                                               const bf16x8 (&qf)[KSTEPS], float& m_ref,
-                                              float& l_run, f32x4 (&o)[DTILES], float scale_log2,
-                                              float flush_raw, float& m_true, bool& overflow) {
+                                              float& l_run, f32x4 (&o)[DTILES], float scale_log2) {
   // ---- S^T = K~ * Q^T: two 16-key tiles (independent chains), K~ fragments read from LDS a
   // few steps ahead of their MFMA.
   constexpr int NST = 2 * KSTEPS;  // (kk, mt)
@@ -208,22 +225,38 @@ __device__ __forceinline__ void compute_block(const SparseCtx& c, const char* st
       for (int i = 0; i < 4; ++i)
         if (((vl >> (16 * mt + i)) & 1u) == 0u) s[mt][i] = -INFINITY;
   }
-  // ---- online softmax against the reference max (fixed once the head holds any mass)
-  float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
-                   fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
-  mx = xquad_max(mx);
-  m_true = fmaxf(m_true, mx);
-  if (m_ref == -INFINITY) m_ref = mx;  // first visible key of this head (same in all 4 lanes)
-  overflow = overflow || (mx > m_ref + flush_raw);
-  const float mc = ((m_ref == -INFINITY) ? 0.f : m_ref) * scale_log2;
+  // ---- online softmax against the head's reference logit (per head = per 4-lane column)
+  auto block_max = [&]() {
+    const float mx = fmaxf(fmaxf(fmaxf(s[0][0], s[0][1]), fmaxf(s[0][2], s[0][3])),
+                           fmaxf(fmaxf(s[1][0], s[1][1]), fmaxf(s[1][2], s[1][3])));
+    return xquad_max(mx);  // the same in the 4 lanes of a head
+  };
   u32x4 packed;
-  float rs = 0.f;
+  auto exps = [&](float ref) {
+    const float mc = ((ref == -INFINITY) ? 0.f : ref) * scale_log2;
+    float rs = 0.f;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float p0 = fast_exp2(fmaf(s[e >> 1][2 * (e & 1)], scale_log2, -mc));
-    const float p1 = fast_exp2(fmaf(s[e >> 1][2 * (e & 1) + 1], scale_log2, -mc));
-    packed[e] = pack_bf16x2(p0, p1);
-    rs += p0 + p1;
+    for (int e = 0; e < 4; ++e) {
+      const float p0 = fast_exp2(fmaf(s[e >> 1][2 * (e & 1)], scale_log2, -mc));
+      const float p1 = fast_exp2(fmaf(s[e >> 1][2 * (e & 1) + 1], scale_log2, -mc));
+      packed[e] = pack_bf16x2(p0, p1);
+      rs += p0 + p1;
+    }
+    return rs;
+  };
+  if (__ballot(m_ref == -INFINITY) != 0ull) {  // some head of the wave has no reference yet
+    const float mx = block_max();
+    if (m_ref == -INFINITY) m_ref = mx;
+  }
+  float rs = exps(m_ref);
+  if (__ballot(!(l_run + rs <= kOverflowSum)) != 0ull) {  // rare: redo against the exact maximum
+    const float m_new = fmaxf(m_ref, block_max());
+    const float alpha = (m_new == m_ref) ? 1.f : fast_exp2((m_ref - m_new) * scale_log2);
+    l_run *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) o[dt] *= alpha;
+    m_ref = m_new;
+    rs = exps(m_ref);
   }
   l_run += rs;
   // P^T operand: k-slot 8*g + j holds key 4g + j (j < 4) or 16 + 4g + (j - 4) (j >= 4).
@@ -251,6 +284,7 @@ __device__ __forceinline__ void compute_block(const SparseCtx& c, const char* st
 
 }  // namespace
 
+template <bool SMALL>
 __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p) {
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
@@ -258,7 +292,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
   __shared__ __attribute__((aligned(1024))) char stage3[STAGE_BYTES];
   __shared__ int idx_lds[IDX_WIN];
   __shared__ uint32_t valid_mask[4];
-  __shared__ int redo_flag;
 
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -277,6 +310,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
   c.used = 0;
   c.bs = p.block_size;
   c.nblocks = p.num_blocks;
+#pragma unroll
+  for (int i = 0; i < (COPIES_PER_WAVE + 1) / 2; ++i) {
+    c.gmap[i] = gather_map_entry(c.wave, c.lane, 2 * i);
+    if (2 * i + 1 < COPIES_PER_WAVE) c.gmap[i] |= gather_map_entry(c.wave, c.lane, 2 * i + 1) << 12;
+  }
   if (p.block_table != nullptr) {
     // sequence of token t: the last b with cu_q[b] <= t (empty sequences are skipped over)
     int lo = 0, hi = p.batch - 1;
@@ -311,24 +349,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
   }
 
   f32x4 o[DTILES];
-  float m_ref = -INFINITY, l_run = 0.f, m_true = -INFINITY;
-  const float flush_raw = kFlushLog2 / p.scale_log2;
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt) o[dt] = f32x4{};
+  float m_ref = -INFINITY, l_run = 0.f;
   char* stages[4] = {stage0, stage1, stage2, stage3};
 
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int dt = 0; dt < DTILES; ++dt) o[dt] = f32x4{};
-    l_run = 0.f;
-    if (pass == 1) m_ref = m_true;  // exact max: P <= 1 everywhere
-    bool overflow = false;
-
+  {
     // prologue: index window 0, then the first three blocks in flight
     c.win0 = 0;
     stage_indices(c, tid);
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < 3; ++b)
-      if (b < nblk) issue_gather(p, c, b, stages[b], &valid_mask[b]);
+      if (b < nblk) issue_gather<SMALL>(p, c, b, stages[b], &valid_mask[b]);
     wait_gather(min(nblk, 3) - 1);
     lds_barrier();
 
@@ -344,11 +377,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
           stage_indices(c, tid);                                                                  \
           __syncthreads();                                                                        \
         }                                                                                         \
-        issue_gather(p, c, jj + 3, NEXT, &valid_mask[((K) + 3) & 3]);                            \
+        issue_gather<SMALL>(p, c, jj + 3, NEXT, &valid_mask[((K) + 3) & 3]);                     \
       }                                                                                           \
       if (wave_active)                                                                            \
-        compute_block(c, CUR, valid_mask[(K)], qf, m_ref, l_run, o, p.scale_log2, flush_raw,      \
-                      m_true, overflow);                                                          \
+        compute_block(c, CUR, valid_mask[(K)], qf, m_ref, l_run, o, p.scale_log2);                \
       wait_gather(min(nblk - 1, jj + 3) - (jj + 1));                                              \
       lds_barrier(); /* the later blocks' copies stay in flight */                                \
     }
@@ -359,13 +391,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
       MLA_SPARSE_STEP(3, stage3, stage2)
     }
 #undef MLA_SPARSE_STEP
-
-    if (pass == 1) break;
-    if (tid == 0) redo_flag = 0;
-    __syncthreads();
-    if (__ballot(overflow) != 0ull && c.lane == 0) redo_flag = 1;
-    __syncthreads();
-    if (redo_flag == 0) break;
   }
 
   // ---- epilogue: normalise, fold in the sink logit, write O and LSE
@@ -401,7 +426,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
 
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
-  hipLaunchKernelGGL(sparse_fwd_kernel, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);
+  // the byte extent of the pool (rows of kv_st elements, the last row's 576 columns)
+  const int64_t extent = p.n_kv <= 0 ? 0 : (p.n_kv - 1) * p.kv_st * 2 + D * 2;
+  if (extent <= (int64_t)UINT32_MAX)
+    hipLaunchKernelGGL(sparse_fwd_kernel<true>, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL(sparse_fwd_kernel<false>, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 

@@ -65,9 +65,11 @@ def test_sparse_all_padded_with_sink():
     check_parity(o, lse, ro, rl, c.name)
 
 
-def test_sparse_wide_logit_range_takes_second_pass():
-    """Logits spanning far more than 2^32 in probability: the first block sets a low reference
-    max and a later key exceeds it by ~40 nats, which the kernel must handle exactly."""
+def test_sparse_wide_logit_range_redoes_the_block():
+    """Logits spanning far more than 2^64 in probability: the first block sets a low reference
+    logit and a later key exceeds it by 80 nats, so that block's sum would overflow the bound and
+    is redone against its exact maximum (the accumulated O and l rescaled): the result must still
+    be the definition's."""
     c = make_sparse("sparse_wide", num_tokens=2, heads=128, n_kv=300, topk=128, seed=44, pad_p=0.0,
                     with_sink=True)
     kv = np.zeros((300, 576), dtype=np.float32)
