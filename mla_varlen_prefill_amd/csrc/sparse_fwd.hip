@@ -268,7 +268,7 @@ __device__ __forceinline__ void compute_block(const SparseCtx& c, const char* st
     const int k0 = 4 * c.g + (c.l16 >> 2);
     const char* r0 = stage + key_row(k0) * ROW_BYTES + 8 * (c.l16 & 3);
     const char* r1 = r0 + 16 * ROW_BYTES;  // key k0 + 16 sits 16 rows further
-    constexpr int PFV = 3;
+    constexpr int PFV = 4;  // (5 spills)
     bf16x8 va[DTILES];
     auto vr = [&](int dt) { va[dt] = join(lds_read_tr16(r0 + dt * 32), lds_read_tr16(r1 + dt * 32)); };
 #pragma unroll
