@@ -57,8 +57,10 @@ const char* mla_status_string(int status);
 /* Library ABI version (increments on any signature change). */
 int32_t mla_abi_version(void);
 
-/* Query-tile rows (BM) and key-block size (BN) the dense kernel is built with; the plan uses
- * the same values. */
+/* Query-tile rows (BM) and key-block size (BN) of the dense kernel's default instances; the
+ * plan uses the same values by default. The (192, 128) layout runs tiles of 2 * BM rows instead
+ * when max_seqlen_q >= 256 and max_seqlen_k >= 2048 (8192 with the causal mask); see
+ * mla_prefill_varlen. */
 void mla_dense_tile_shape(int32_t* block_m, int32_t* block_n);
 
 /* ------------------------------------------------------------------------------------------
@@ -137,15 +139,21 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
  *   out  : bf16 [total_q, H, 128], strides (o_stride_tok, o_stride_head), written.
  *   lse  : nullable float32 [total_q, H], strides (lse_stride_tok, lse_stride_head), written.
  *   workspace : device memory of at least mla_prefill_varlen_workspace_size(...) bytes with the
- *         same batch/total_q/max_seqlen/H/head_dim_v/num_splits (it returns 0 for arguments it
+ *         same batch/total_q/max_seqlen/H/head_dim_v/causal/num_splits (it returns 0 for arguments it
  *         rejects, a head_dim_v other than 128 or 256 included); scratch only, contents undefined
  *         after.
  *         It holds the plan and the work-ticket counters of the call: calls that may overlap in
  *         time (other streams) must not share a workspace.
+ * Work items are query tiles of 128 rows (four-wave work-groups, two per CU). For (192, 128),
+ * when max_seqlen_q >= 256 and max_seqlen_k >= 2048 (8192 with causal != 0), they are tiles of
+ * 256 rows (eight-wave work-groups, one per CU), which halve the key/value copies per query row
+ * where the rows see many keys; the bounds pick the instance, so a call with looser bounds may
+ * run the other one (results agree within rounding).
  * Tuning (environment, read by the library): MLA_DENSE_GROUP=n schedules n (head, split) units
  * per XCD at a time (default 1); MLA_DENSE_WGS_PER_XCD=n caps the persistent grid at 8*n
  * work-groups (default: all resident slots). Both leave results bitwise unchanged (each work item
- * is computed the same way whichever work-group runs it).
+ * is computed the same way whichever work-group runs it). MLA_DENSE_WAVES=4 or 8 forces the
+ * (192, 128) tile height (read once per process; the workspace size and split helpers follow it).
  * With num_splits == 1 a sequence's result does not depend on the other sequences in the batch,
  * and repeated calls are bitwise identical.
  * Errors: INVALID_ARG (null q/k/v/cu/out, sizes <= 0 where a count is required, strides smaller

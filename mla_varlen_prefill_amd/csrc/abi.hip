@@ -117,7 +117,7 @@ hipError_t timed_launch(int kind, hipStream_t stream, F&& fn) {
   return hipSuccess;
 }
 
-// Query rows per dense work-group (one 32-row query tile per wave).
+// Query rows per dense work-group of the default (four-wave) instances.
 int dense_bm() { return 128; }
 
 // Head dimensions the dense kernels are built for: (q/k head, v head) = (192, 128), the default
@@ -127,16 +127,34 @@ bool dense_dims_ok(int dqk, int dv) {
   return (dqk == 192 && dv == 128) || (dqk == 128 && dv == 128) || (dqk == 256 && dv == 256);
 }
 
-// Instance of a dense call: query tiles per wave, resident work-groups per CU and tile height.
+// Instance of a dense call: waves per work-group, resident work-groups per CU and tile height.
+// The (192, 128) layout takes eight waves (256-row tiles) when a tile's rows see many keys: with
+// at least 256 query rows in some sequence and at least 2048 keys (8192 under the causal mask,
+// where a taller tile also computes a larger triangle of masked scores). Measured against four
+// waves: 2-3% faster without the mask at 2048-4096 keys, 1.6% faster at 16384 causal, even at
+// 4096-8192 causal, 1.5% slower on causal batches of 2048-token sequences. MLA_DENSE_WAVES (4 or
+// 8) overrides the choice.
 struct DenseShape {
-  int dqk, dv, nq, occ, bm;
+  int dqk, dv, nw, occ, bm;
   bool fp8;
 };
-DenseShape dense_shape(int dqk, int dv, bool fp8) {
-  DenseShape d{dqk, dv, 1, 1, 128, fp8};
-  d.occ = mla::dense_occupancy_of(d.nq, dqk, dv);
-  d.bm = mla::dense_rows_per_tile(d.nq, dqk, dv);
+DenseShape with_waves(DenseShape d, int nw) {
+  d.nw = nw;
+  d.occ = mla::dense_occupancy_of(nw, d.dqk, d.dv);
+  d.bm = mla::dense_rows_per_tile(nw, d.dqk, d.dv);
   return d;
+}
+DenseShape dense_shape(int dqk, int dv, bool fp8, int32_t max_q, int32_t max_k, bool causal) {
+  DenseShape d{dqk, dv, mla::dense_default_waves(dqk, dv), 1, 128, fp8};
+  if (dqk == 192 && dv == 128) {
+    static const int forced = []() {
+      const char* e = std::getenv("MLA_DENSE_WAVES");
+      return e != nullptr ? std::atoi(e) : 0;
+    }();
+    const bool tall = max_q >= 256 && max_k >= (causal ? 8192 : 2048);
+    d.nw = (forced == 4 || forced == 8) ? forced : (tall ? 8 : 4);
+  }
+  return with_waves(d, d.nw);
 }
 
 // Dense scheduling groups: each XCD works through `n` (head, split) units at a time (longest
@@ -289,17 +307,15 @@ mla_status_t mla_prefill_plan(const int32_t* cu_seqlens_q, const int32_t* cu_seq
 int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32_t max_seqlen_k,
                                       int32_t num_heads, int32_t head_dim_qk, int32_t head_dim_v,
                                       int32_t causal, int32_t num_splits) {
-  (void)causal;
   if (num_splits < 0 || num_splits > kMaxSplits || !dense_dims_ok(head_dim_qk, head_dim_v)) return -1;
   // the instance the bf16-output call runs (FP8 output selects the same tile height and residency)
   return resolve_splits(batch, max_seqlen_q, max_seqlen_k, num_heads, num_splits,
-                        dense_shape(head_dim_qk, head_dim_v, false));
+                        dense_shape(head_dim_qk, head_dim_v, false, max_seqlen_q, max_seqlen_k, causal != 0));
 }
 
 size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
                                          int32_t max_seqlen_k, int32_t num_heads,
                                          int32_t head_dim_v, int32_t causal, int32_t num_splits) {
-  (void)causal;
   if (batch < 0 || total_q < 0 || max_seqlen_q < 0 || max_seqlen_k < 0 || num_heads <= 0 ||
       num_splits < 0 || num_splits > kMaxSplits || (head_dim_v != 128 && head_dim_v != 256))
     return 0;
@@ -310,7 +326,8 @@ size_t mla_prefill_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t
     if (!dense_dims_ok(dqk, head_dim_v)) continue;
     for (bool fp8 : {false, true})
       need = std::max(need, varlen_layout(batch, total_q, max_seqlen_q, max_seqlen_k, num_heads, num_splits,
-                                          dense_shape(dqk, head_dim_v, fp8)).total);
+                                          dense_shape(dqk, head_dim_v, fp8, max_seqlen_q, max_seqlen_k,
+                                                      causal != 0)).total);
   }
   return need;
 }
@@ -349,7 +366,7 @@ static mla_status_t varlen_call(
       max_seqlen_k > (1 << 24) || k_stride_tok >= (1 << 23) || v_stride_tok >= (1 << 23))
     return MLA_ERR_UNSUPPORTED;  // key-block byte offsets are kept in 31 bits
   const bool fp8 = out_scale != nullptr && (part_o == nullptr || accumulate == 2);
-  const DenseShape ds = dense_shape(head_dim_qk, head_dim_v, fp8);
+  const DenseShape ds = dense_shape(head_dim_qk, head_dim_v, fp8, max_seqlen_q, max_seqlen_k, causal != 0);
   // fp8 rows are written in 16-byte pieces: strides in whole 16-element units
   const bool ostride_ok = fp8 ? ((o_stride_tok & 15) == 0 && (o_stride_head & 15) == 0)
                               : (stride_ok(o_stride_tok) && stride_ok(o_stride_head));
@@ -446,7 +463,7 @@ static mla_status_t varlen_call(
     }
     dp.counters = tickets;
   }
-  if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, ds.nq, ds.dqk, ds.dv, ds.fp8, stream); }) !=
+  if (timed_launch(MLA_KERNEL_DENSE, stream, [&] { return mla::launch_dense_fwd(dp, ds.nw, ds.dqk, ds.dv, ds.fp8, stream); }) !=
       hipSuccess)
     return MLA_ERR_HIP;
 
@@ -554,8 +571,14 @@ struct ChunkedLayout {
 
 ChunkedLayout chunked_layout(int32_t batch, int32_t total_q, int32_t max_q, int32_t heads, int32_t chunk) {
   ChunkedLayout C{};
-  C.dense = align256(varlen_layout(batch, total_q, max_q, std::max(max_q, chunk), heads, 1,
-                                   dense_shape(kDenseDqk, kDenseDv, false)).total);
+  // enough for the dense calls of a chunked call with either tile height
+  const int32_t max_k = std::max(max_q, chunk);
+  size_t dense = 0;
+  for (int nw : {4, 8})
+    dense = std::max(dense, varlen_layout(batch, total_q, max_q, max_k, heads, 1,
+                                          with_waves(dense_shape(kDenseDqk, kDenseDv, false, max_q, max_k, false),
+                                                     nw)).total);
+  C.dense = align256(dense);
   const size_t rows = (size_t)batch * chunk;
   const size_t th = (size_t)total_q * heads;
   C.off_cu = C.dense;

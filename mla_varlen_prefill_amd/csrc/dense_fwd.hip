@@ -47,22 +47,22 @@ constexpr int BN = 64;
 // row sum would pass 2^64 is redone against its exact maximum (P stays far inside bf16 / fp32
 // range, and O = sum P V inside fp32 range for any bf16 V).
 constexpr float kOverflowSum = 18446744073709551616.f;  // 2^64
-// Bytes of a wave's K copy region used by the epilogue's output turn-around (32 rows x 128 B).
-constexpr int kEpilogueBytes = 32 * 128;
 
 // Head dimensions (q/k head DQK, v head DV) and output type of a kernel instance. A work item
 // computes DVT = 128 of the DV output columns (DVH = DV / DVT items per row tile and head, all
 // computing the same scores): a wave's 32 x 256 fp32 output tile would not fit the registers
 // beside its Q fragments.
-template <int DQK_, int DV_, bool FP8_>
+template <int DQK_, int DV_, bool FP8_, int NW_ = (DQK_ == 256 ? 8 : 4)>
 struct Shape {
   static constexpr int DQK = DQK_, DV = DV_;
   static constexpr int DVT = 128, DVH = DV / DVT;
   static constexpr bool FP8 = FP8_;                         // fp8 e4m3 output with a static scale
   // Waves per work-group (32 query rows each). The 256-wide layout needs all of a wave's
   // registers at two waves per SIMD and 96 KB of LDS per work-group, so its work-groups have
-  // eight waves (one per CU); the others run two four-wave work-groups per CU.
-  static constexpr int NW = DQK == 256 ? 8 : 4;
+  // eight waves (one per CU). The others run two four-wave work-groups per CU, or one of eight
+  // waves, whose 256-row tiles halve the key and value copies per query row: faster when items
+  // see many keys, slower when they see few (a longer prologue and epilogue per key block).
+  static constexpr int NW = NW_;
   // operand reads run PF MFMA steps ahead (fewer where registers are short)
   static constexpr int PF = DQK == 256 ? 3 : 6;
   // The next block's copies are issued one after each of the first S products (256-wide layout;
@@ -77,9 +77,14 @@ struct Shape {
   // KA_N per-lane offsets cover one group's MFMA steps.
   static constexpr int KA_GROUP = DQK == 192 ? 128 : 256;
   static constexpr int KA_N = KA_GROUP / 32;
+  // The epilogue turns each wave's 32 x DV output tile around in the wave's K copy region, one
+  // row segment of EPI_SEG bytes at a time: 128-byte segments when the 4 KiB fit the region, else
+  // 64-byte ones.
+  static constexpr int EPI_SEG = KCH * 1024 >= 32 * 128 ? 128 : 64;
+  static constexpr int EPI_BYTES = 32 * EPI_SEG;
   // The work ticket handed between waves sits past the epilogue area of the wave's K copy region
   // when it fits there, else at the start of the wave's V copy region (which the epilogue never uses).
-  static constexpr bool TICKET_IN_K = kEpilogueBytes + 4 <= KCH * 1024;
+  static constexpr bool TICKET_IN_K = EPI_BYTES + 4 <= KCH * 1024;
   static_assert((BN * DQK / 8) % (64 * NW) == 0 && (BN * DVT / 8) % (64 * NW) == 0 && DV % DVT == 0, "shape");
 };
 
@@ -643,15 +648,17 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
     }
     if (!to_part) {
       // Output through LDS: the lane layout holds pieces of 4 consecutive columns of a row, so the
-      // tile is turned around in this wave's own copy region of a free stage, one 128-byte row
-      // segment at a time (64 bf16 or 128 fp8 columns; 16-byte chunks XOR-swizzled by row), and
-      // written as whole 128-byte row segments.
+      // tile is turned around in this wave's own copy region of a free stage, one row segment of
+      // SEG bytes at a time (16-byte chunks XOR-swizzled by row), and written as whole segments.
+      constexpr int SEG = S::EPI_SEG;
+      constexpr int CPR = SEG / 16;      // 16-byte chunks per segment row
+      constexpr int RPI = 64 / CPR;      // rows one wave-wide 16-byte access covers
       char* buf = stage + c.kdst;
       const int r0 = c.wave * 32 * NQ + nq * 32;  // first tile row of this 32-row slab
       // lane-derived addresses are computed here, not hoisted into long-lived registers
       const int lane = (int)opaque((uint32_t)c.lane), l32 = lane & 31, hl = lane >> 5;
-      const int cc = lane & 7;
-      constexpr int SEG_DT = 128 / (32 * ESZ);  // 32-column MFMA tiles per 128-byte segment
+      const int cc = lane & (CPR - 1);
+      constexpr int SEG_DT = SEG / (32 * ESZ);  // 32-column MFMA tiles per segment
       const float w = inv * q_mul;
 #pragma unroll
       for (int seg = 0; seg < DV / (32 * SEG_DT); ++seg) {
@@ -665,26 +672,26 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
               const uint32_t v = pack_fp8x4(o[nq][dt][g4 * 4 + 0] * w, o[nq][dt][g4 * 4 + 1] * w,
                                             o[nq][dt][g4 * 4 + 2] * w, o[nq][dt][g4 * 4 + 3] * w);
               const int chunk = dd * 2 + (g4 >> 1);
-              *reinterpret_cast<uint32_t*>(buf + l32 * 128 + ((chunk ^ (l32 & 7)) * 16) + (g4 & 1) * 8 + hl * 4) = v;
+              *reinterpret_cast<uint32_t*>(buf + l32 * SEG + ((chunk ^ (l32 & (CPR - 1))) * 16) + (g4 & 1) * 8 + hl * 4) = v;
             } else {
               const int chunk = dd * 4 + g4;
               u32x2 v = {pack_bf16x2(o[nq][dt][g4 * 4 + 0] * w, o[nq][dt][g4 * 4 + 1] * w),
                          pack_bf16x2(o[nq][dt][g4 * 4 + 2] * w, o[nq][dt][g4 * 4 + 3] * w)};
-              *reinterpret_cast<u32x2*>(buf + l32 * 128 + ((chunk ^ (l32 & 7)) * 16) + hl * 8) = v;
+              *reinterpret_cast<u32x2*>(buf + l32 * SEG + ((chunk ^ (l32 & (CPR - 1))) * 16) + hl * 8) = v;
             }
           }
         }
-        u32x4 v[4];
+        u32x4 v[32 / RPI];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = i * 8 + (lane >> 3);
-          v[i] = *reinterpret_cast<const u32x4*>(buf + rr * 128 + ((cc ^ (rr & 7)) * 16));
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int rr = i * RPI + lane / CPR;
+          v[i] = *reinterpret_cast<const u32x4*>(buf + rr * SEG + ((cc ^ (rr & (CPR - 1))) * 16));
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int rr = i * 8 + (lane >> 3);
+        for (int i = 0; i < 32 / RPI; ++i) {
+          const int rr = i * RPI + lane / CPR;
           if (r0 + rr >= it.rlo() && r0 + rr < it.rows)
-            *reinterpret_cast<u32x4*>(out_h + (int64_t)(it.cq0 + it.row0 + r0 + rr) * o_st_b + seg * 128 + cc * 16) = v[i];
+            *reinterpret_cast<u32x4*>(out_h + (int64_t)(it.cq0 + it.row0 + r0 + rr) * o_st_b + seg * SEG + cc * 16) = v[i];
         }
       }
     }
@@ -693,10 +700,10 @@ __device__ __forceinline__ void store_item(const DenseCtx<NQ, S>& c, const Item&
 
 }  // namespace
 
-// Two work-groups per CU when their registers and LDS fit, else one.
+// Two four-wave work-groups per CU when their registers and LDS fit, else one work-group.
 template <int NQ, class S>
 constexpr int dense_occupancy() {
-  return (NQ == 1 && 2 * (S::K_STAGE_BYTES + S::V_STAGE_BYTES) <= 80 * 1024) ? 2 : 1;
+  return (NQ == 1 && S::NW == 4 && 2 * (S::K_STAGE_BYTES + S::V_STAGE_BYTES) <= 80 * 1024) ? 2 : 1;
 }
 
 template <int NQ, class S>
@@ -721,12 +728,12 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
   auto stage_v = [&](int s) { return s ? lds_v1 : lds_v0; };
   // Thread 0 hands a ticket to every wave through a stage that is free at that moment: one copy
   // in each wave's own copy region, which only that wave's next block copy overwrites (after the
-  // wave has read it). In the K region the copy sits past the first kEpilogueBytes, which the
+  // wave has read it). In the K region the copy sits past the first EPI_BYTES, which the
   // epilogue of the previous item may still be using in that stage (a wave can still be turning
   // its output around there while thread 0 shares the ticket of the next item); the V region is
   // never used by the epilogue.
   auto ticket_slot = [&](int s, int w) -> char* {
-    return S::TICKET_IN_K ? stage_k(s) + w * KCH * 1024 + kEpilogueBytes : stage_v(s) + w * VCH * 1024;
+    return S::TICKET_IN_K ? stage_k(s) + w * KCH * 1024 + S::EPI_BYTES : stage_v(s) + w * VCH * 1024;
   };
   auto share_ticket = [&](int sfree, int tk) -> int {
     if (threadIdx.x == 0) {
@@ -951,6 +958,8 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
 
 using Shape192 = Shape<192, 128, false>;
 using Shape192F8 = Shape<192, 128, true>;
+using Shape192W8 = Shape<192, 128, false, 8>;
+using Shape192F8W8 = Shape<192, 128, true, 8>;
 using Shape128 = Shape<128, 128, false>;
 using Shape128F8 = Shape<128, 128, true>;
 using Shape256 = Shape<256, 256, false>;
@@ -958,6 +967,8 @@ using Shape256F8 = Shape<256, 256, true>;
 
 template __global__ void dense_fwd_kernel<1, Shape192>(DenseParams);
 template __global__ void dense_fwd_kernel<1, Shape192F8>(DenseParams);
+template __global__ void dense_fwd_kernel<1, Shape192W8>(DenseParams);
+template __global__ void dense_fwd_kernel<1, Shape192F8W8>(DenseParams);
 template __global__ void dense_fwd_kernel<1, Shape128>(DenseParams);
 template __global__ void dense_fwd_kernel<1, Shape128F8>(DenseParams);
 template __global__ void dense_fwd_kernel<1, Shape256>(DenseParams);
@@ -968,32 +979,45 @@ static void launch_one(const DenseParams& p, int grid, hipStream_t stream) {
   hipLaunchKernelGGL((dense_fwd_kernel<NQ, S>), dim3(grid), dim3(64 * S::NW), 0, stream, p);
 }
 
-int dense_occupancy_of(int nq, int dqk, int dv) {
+bool dense_waves_ok(int nw, int dqk, int dv) {
+  if (dqk == 192 && dv == 128) return nw == 4 || nw == 8;
+  if (dqk == 128 && dv == 128) return nw == Shape128::NW;
+  if (dqk == 256 && dv == 256) return nw == Shape256::NW;
+  return false;
+}
+
+int dense_default_waves(int dqk, int dv) {
+  if (dqk == 256 && dv == 256) return Shape256::NW;
+  if (dqk == 128 && dv == 128) return Shape128::NW;
+  return Shape192::NW;
+}
+
+int dense_occupancy_of(int nw, int dqk, int dv) {
   if (dqk == 256 && dv == 256) return dense_occupancy<1, Shape256>();
   if (dqk == 128 && dv == 128) return dense_occupancy<1, Shape128>();
-  return dense_occupancy<1, Shape192>();
+  return nw == 8 ? dense_occupancy<1, Shape192W8>() : dense_occupancy<1, Shape192>();
 }
 
-int dense_rows_per_tile(int nq, int dqk, int dv) {
-  if (dqk == 256 && dv == 256) return 32 * Shape256::NW;
-  if (dqk == 128 && dv == 128) return 32 * Shape128::NW;
-  return 32 * Shape192::NW;
-}
+int dense_rows_per_tile(int nw, int dqk, int dv) { return dense_waves_ok(nw, dqk, dv) ? 32 * nw : 0; }
 
-hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool fp8_out, hipStream_t stream) {
+hipError_t launch_dense_fwd(const DenseParams& p, int nw, int dqk, int dv, bool fp8_out, hipStream_t stream) {
   const int grid = 8 * p.wgs_per_xcd;
+  if (!dense_waves_ok(nw, dqk, dv)) return hipErrorInvalidValue;
   if (grid <= 0) return hipSuccess;
   if (dqk == 192 && dv == 128) {
-    if (fp8_out) launch_one<1, Shape192F8>(p, grid, stream);
-    else launch_one<1, Shape192>(p, grid, stream);
+    if (nw == 8) {
+      if (fp8_out) launch_one<1, Shape192F8W8>(p, grid, stream);
+      else launch_one<1, Shape192W8>(p, grid, stream);
+    } else {
+      if (fp8_out) launch_one<1, Shape192F8>(p, grid, stream);
+      else launch_one<1, Shape192>(p, grid, stream);
+    }
   } else if (dqk == 128 && dv == 128) {
     if (fp8_out) launch_one<1, Shape128F8>(p, grid, stream);
     else launch_one<1, Shape128>(p, grid, stream);
-  } else if (dqk == 256 && dv == 256) {
+  } else {
     if (fp8_out) launch_one<1, Shape256F8>(p, grid, stream);
     else launch_one<1, Shape256>(p, grid, stream);
-  } else {
-    return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

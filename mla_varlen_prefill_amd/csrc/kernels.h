@@ -108,13 +108,16 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_chunk_cu(const int32_t* cu_ctx, int32_t batch, int32_t c0, int32_t w, int32_t* cu_chunk,
                            hipStream_t stream);
 hipError_t launch_upproj(const UpprojParams& p, hipStream_t stream);
-// Dense kernel instances: (dqk, dv) in {(192, 128), (128, 128), (256, 256)}, bf16 or fp8 output;
-// nq (query tiles per wave) is 1.
-hipError_t launch_dense_fwd(const DenseParams& p, int nq, int dqk, int dv, bool fp8_out, hipStream_t stream);
+// Dense kernel instances: (dqk, dv) in {(192, 128), (128, 128), (256, 256)}, bf16 or fp8 output,
+// nw waves (32 query rows each) per work-group: 4 or 8 for (192, 128), dense_default_waves for
+// the others. An unsupported combination launches nothing and returns hipErrorInvalidValue.
+hipError_t launch_dense_fwd(const DenseParams& p, int nw, int dqk, int dv, bool fp8_out, hipStream_t stream);
+bool dense_waves_ok(int nw, int dqk, int dv);
+int dense_default_waves(int dqk, int dv);
 // Resident work-groups per CU of the instance.
-int dense_occupancy_of(int nq, int dqk, int dv);
+int dense_occupancy_of(int nw, int dqk, int dv);
 // Query rows per work item (tile height) of the instance.
-int dense_rows_per_tile(int nq, int dqk, int dv);
+int dense_rows_per_tile(int nw, int dqk, int dv);
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
 

@@ -134,6 +134,27 @@ def test_dense_forced_splits(splits, causal):
     check_parity(o, lse, ro, rl, c.name)
 
 
+@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_long_key_bound_tiles(causal, splits):
+    """With at least 256 query rows the (192, 128) layout runs 256-row query tiles (eight-wave
+    work-groups) from max_seqlen_k = 2048 on (8192 with the causal mask), 128-row tiles below; the
+    bound is only a bound, so the same ragged batch (tiles cut by sequence ends, a one-row
+    sequence with many keys) goes through both and each matches the oracle."""
+    import torch
+    import mla_varlen_prefill_amd as mla
+    c = make_dense(f"bound_tiles_c{int(causal)}_s{splits}", [700, 129, 1, 513, 256, 40],
+                   [700, 300, 2000, 513, 260, 0], heads=3, causal=causal, seed=37, with_sink=True)
+    ro, rl = oracle(c)
+    for bound in (c.max_k, 4096, 8192):
+        announce(f"dense {c.name} max_seqlen_k={bound}")
+        o, lse = mla.mla_prefill_varlen(dev_bf16(c.q), dev_bf16(c.k), dev_bf16(c.v), dev(c.cu_q), dev(c.cu_k),
+                                        c.max_q, bound, c.scale, causal=causal, num_splits=splits,
+                                        sink=dev(c.sink))
+        torch.cuda.synchronize()
+        check_parity(host_f64(o), host_f64(lse), ro, rl, f"{c.name} max_seqlen_k={bound}")
+
+
 def test_dense_auto_splits_small_grid():
     import mla_varlen_prefill_amd as mla
     c = make_dense("auto_split", [4096], [4096], heads=2, causal=True, seed=36)

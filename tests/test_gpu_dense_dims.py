@@ -14,14 +14,16 @@ OTHER_DIMS = [(128, 128), (256, 256)]
 ALL_DIMS = [(192, 128), (128, 128), (256, 256)]
 
 
-def _run(c, num_splits=1, window=None, out_scale=None):
-    """Runs a DenseCase through the library; returns (out tensor, lse as float64 numpy)."""
+def _run(c, num_splits=1, window=None, out_scale=None, max_k=None):
+    """Runs a DenseCase through the library (max_seqlen_k = max_k, else the case's longest
+    sequence); returns (out tensor, lse as float64 numpy)."""
     import torch
     import mla_varlen_prefill_amd as mla
     sink = dev(c.sink) if c.sink is not None else None
     scale_t = None if out_scale is None else torch.tensor([out_scale], dtype=torch.float32, device="cuda")
     out, lse = mla.mla_prefill_varlen(dev_bf16(c.q), dev_bf16(c.k), dev_bf16(c.v), dev(c.cu_q), dev(c.cu_k),
-                                      c.max_q, c.max_k, c.scale, causal=c.causal, num_splits=num_splits,
+                                      c.max_q, c.max_k if max_k is None else max_k, c.scale, causal=c.causal,
+                                      num_splits=num_splits,
                                       sink=sink, window=window, out_scale=scale_t)
     torch.cuda.synchronize()
     return out, host_f64(lse)
@@ -121,18 +123,18 @@ def test_fp8_output_is_exact_when_o_is_v(dims, splits):
 
 
 @pytest.mark.parametrize("splits", [1, 2])
-@pytest.mark.parametrize("dims", ALL_DIMS)
-def test_fp8_output_within_a_rounding_step(dims, splits):
+@pytest.mark.parametrize("dims,max_k", [(d, None) for d in ALL_DIMS] + [((192, 128), 8192)])
+def test_fp8_output_within_a_rounding_step(dims, max_k, splits):
     """General ragged causal case: every decoded code is within half an E4M3 step of the oracle's
     O / scale plus the fp32 accumulation error, no code is NaN, and the LSE is that of the bf16
-    output path bit for bit."""
+    output path bit for bit (also in the 256-row tiles a causal max_seqlen_k of 8192 selects)."""
     dqk, dv = dims
     s = 2.0 ** -8
     c = make_dense(f"fp8 {dqk}x{dv}", [5, 129, 1, 300, 77], [7, 0, 129, 700, 77], heads=4, causal=True,
                    seed=77, with_sink=True, dqk=dqk, dv=dv)
-    announce(f"dense {c.name} splits={splits}")
-    out, lse = _run(c, num_splits=splits, out_scale=s)
-    _, lse_bf16 = _run(c, num_splits=splits)
+    announce(f"dense {c.name} splits={splits} max_seqlen_k={max_k}")
+    out, lse = _run(c, num_splits=splits, out_scale=s, max_k=max_k)
+    _, lse_bf16 = _run(c, num_splits=splits, max_k=max_k)
     ro, rl = O.dense_mla_prefill(c.q, c.k, c.v, c.cu_q, c.cu_k, c.scale, c.causal, sink=c.sink)
     codes = _codes(out)
     assert not np.any((codes & 0x7F) == 0x7F), "NaN code"
