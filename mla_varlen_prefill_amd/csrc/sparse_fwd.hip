@@ -393,9 +393,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
 #undef MLA_SPARSE_STEP
   }
 
-  // ---- epilogue: normalise, fold in the sink logit, write O and LSE
+  // ---- epilogue: normalise, fold in the sink logit, write O and LSE. The head index is formed
+  // again here rather than kept in a register through the block loop.
+  int tid_e = (int)threadIdx.x;
+  asm volatile("" : "+v"(tid_e));
+  const int head_e = c.wave * 16 + (tid_e & 15);
+  const bool hok_e = head_e < p.num_heads;
   const float l_tot = xquad_sum(l_run);
-  const float sink_v = (p.sink != nullptr && hok) ? p.sink[head] : -INFINITY;
+  const float sink_v = (p.sink != nullptr && hok_e) ? p.sink[head_e] : -INFINITY;
   float inv, lse_v;
   if (l_tot == 0.f) {
     inv = 0.f;
@@ -413,14 +418,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
       lse_v = mxs + __logf(z);
     }
   }
-  if (hok) {
-    __bf16* op = p.out + (int64_t)t * p.o_st + (int64_t)head * p.o_sh + 4 * c.g;
+  if (hok_e) {
+    __bf16* op = p.out + (int64_t)t * p.o_st + (int64_t)head_e * p.o_sh + 4 * c.g;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
       u32x2 v = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
       *reinterpret_cast<u32x2*>(op + dt * 16) = v;
     }
-    if (p.lse != nullptr && c.g == 0) p.lse[(int64_t)t * p.l_st + (int64_t)head * p.l_sh] = lse_v;
+    if (p.lse != nullptr && c.g == 0) p.lse[(int64_t)t * p.l_st + (int64_t)head_e * p.l_sh] = lse_v;
   }
 }
 
