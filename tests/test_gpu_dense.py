@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 from oracle import mla_oracle as O
-from workloads import make_dense, dense_small, dense_varlen
+from workloads import make_dense, dense_small, dense_varlen, f32_to_bf16_bits
 from tests.gpu_util import announce, dev_bf16, dev, host_f64, check_parity
 
 pytestmark = pytest.mark.gpu
@@ -151,6 +151,36 @@ def test_dense_long_key_bound_tiles(causal, splits):
         o, lse = mla.mla_prefill_varlen(dev_bf16(c.q), dev_bf16(c.k), dev_bf16(c.v), dev(c.cu_q), dev(c.cu_k),
                                         c.max_q, bound, c.scale, causal=causal, num_splits=splits,
                                         sink=dev(c.sink))
+        torch.cuda.synchronize()
+        check_parity(host_f64(o), host_f64(lse), ro, rl, f"{c.name} max_seqlen_k={bound}")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dense_wide_logit_range_redoes_tiles(causal):
+    """Logits far beyond the 2^64 sum bound: each row's reference logit comes from its first keys
+    (about 5), then a key 77 nats above it arrives in the first 32-key tile of an unmasked block
+    and a key 82 nats above that one in the second tile of a later block, and a third such key
+    sits in the diagonal (masked) region. Each forces the redo of its tile against the exact
+    maximum, with O and l rescaled; the result must still be the definition's, in both the
+    128-row and the 256-row tiles."""
+    import torch
+    import mla_varlen_prefill_amd as mla
+    n = 1000
+    c = make_dense(f"wide_c{int(causal)}", [n], [n], heads=2, causal=causal, seed=38, scale=1.0)
+    rng = np.random.default_rng(7)
+    q = np.zeros((n, 2, 192), dtype=np.float32)
+    q[:, :, 0] = 2.0
+    k = np.zeros((n, 2, 192), dtype=np.float32)
+    k[:, :, 0] = rng.standard_normal((n, 2))
+    k[330, :, 0] = 41.0    # block 5, first tile: logit 82
+    k[616, :, 0] = 82.0    # block 9, second tile: logit 164
+    k[950, :, 0] = 123.0   # block 14, the last tile's diagonal region: logit 246
+    c.q, c.k = f32_to_bf16_bits(q), f32_to_bf16_bits(k)
+    ro, rl = oracle(c)
+    for bound in (n, 8192):
+        announce(f"dense {c.name} max_seqlen_k={bound}")
+        o, lse = mla.mla_prefill_varlen(dev_bf16(c.q), dev_bf16(c.k), dev_bf16(c.v), dev(c.cu_q), dev(c.cu_k),
+                                        n, bound, c.scale, causal=causal, num_splits=1)
         torch.cuda.synchronize()
         check_parity(host_f64(o), host_f64(lse), ro, rl, f"{c.name} max_seqlen_k={bound}")
 
