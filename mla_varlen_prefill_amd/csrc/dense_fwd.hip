@@ -203,8 +203,18 @@ __device__ __forceinline__ void compute_block(const DenseCtx<NQ, S>& c, const It
                                               const char* ks, const char* vs,
                                               bf16x8 (&qf)[NQ][S::DQK / 16], float (&m_run)[NQ],
                                               float (&l_run)[NQ], f32x16 (&o)[NQ][S::DVT / 32],
-                                              float scale_log2, bool causal, QDone&& q_done, Copy&& copy) {
+                                              float scale_log2, bool causal, QDone&& q_done, Copy&& copy,
+                                              bool live) {
   constexpr int DQK = S::DQK, DV = S::DVT, KA_N = S::KA_N, KA_GROUP = S::KA_GROUP;
+  if (!live) {
+    // The wave sees no key of this block: only the copies and the Q hand-over are issued.
+#pragma unroll
+    for (int st = 0; st < NMT * (DQK / 16); ++st) {
+      copy(st);
+      if (st % NMT == NMT - 1) q_done(st / NMT);
+    }
+    return;
+  }
   // ---- S^T = K_blk * Q^T: the 32-key tiles are independent accumulator chains, issued
   // alternately, with the K fragments read from LDS PF steps ahead of their MFMA.
   f32x16 s[NQ][2];
@@ -366,12 +376,12 @@ __device__ __forceinline__ void block_step(const DenseCtx<NQ, S>& c, const Item&
                                            const char* __restrict__ vc, bf16x8 (&qf)[NQ][S::DQK / 16],
                                            float (&m_run)[NQ], float (&l_run)[NQ],
                                            f32x16 (&o)[NQ][S::DVT / 32], float scale_log2, bool causal,
-                                           QDone&& q_done) {
+                                           QDone&& q_done, bool live = true) {
   static_assert(!S::SPREAD_COPIES || S::KCH + S::VCH <= NMT * (S::DQK / 16), "one copy per S product");
   compute_block<NQ, NMT, MASK>(c, it, j, kc, vc, qf, m_run, l_run, o, scale_log2, causal, q_done, [&](int st) {
     if (S::SPREAD_COPIES && st < S::KCH + S::VCH && do_load) issue_copy(c, ld, ld_j, kn, vn, st);
     if (!S::SPREAD_COPIES && st == 0 && do_load) issue_block_load(c, ld, ld_j, kn, vn);
-  });
+  }, live);
 }
 
 // Read-only metadata (plan, cu_seqlens, sink, item count) is read through the constant address
@@ -921,8 +931,9 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
       }
       // Last block: hand over to the next item. Its first key block is copied into the other
       // stage, and each of its Q^T fragments is loaded as soon as the matching fragment of this
-      // item has been read for the last time (without a next item, Q is simply re-read). It
-      // always runs the two-tile body so that the new fragments have a single definition.
+      // item has been read for the last time (without a next item, Q is simply re-read). It runs
+      // the two-tile body (so that the new fragments have a single definition), or, for a wave
+      // that sees no key of the block (the first rows of a causal tile), only the copies and loads.
       {
         prepare(j);
         const __bf16* qp[NQ];
@@ -933,7 +944,7 @@ __global__ __launch_bounds__(64 * S::NW, (dense_occupancy<NQ, S>())) void dense_
 #pragma unroll
                                   for (int nq = 0; nq < NQ; ++nq)
                                     qf[nq][kk] = *reinterpret_cast<const bf16x8*>(qp[nq] + kk * 16);
-                                });
+                                }, vis_end > j * BN);
         wait_vmem();
         __syncthreads();
         st ^= 1;
