@@ -734,7 +734,7 @@ mla_status_t sparse_call(mla::SparseParams& sp, const void* q, int64_t q_stride_
       !(softmax_scale > 0.f))
     return MLA_ERR_INVALID_ARG;
   if (head_dim_qk != kSparseDqk || head_dim_v != kSparseDv || num_heads > 128 || topk > 8192 ||
-      n_kv > INT32_MAX)
+      n_kv > INT32_MAX || kv_stride_row > INT32_MAX)
     return MLA_ERR_UNSUPPORTED;
   const int64_t H = num_heads;
   if (idx_stride_tok < topk || kv_stride_row < kSparseDqk || q_stride_head < 0 || o_stride_head < 0 ||

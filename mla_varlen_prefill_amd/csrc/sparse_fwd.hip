@@ -84,10 +84,21 @@ struct SparseCtx {
   const int32_t* bt_row;   // paged cache: block-table row of the token's sequence (else null)
   int used;                // paged cache: logical positions [0, used) may be valid
   int bs, nblocks;         // paged cache: block size, number of blocks
-  // Gather map of this lane's copies (two per word, 12 bits each: row_key of the slot's row in
+  // Gather map of this lane's copies (two per word, 16 bits each: row_key of the slot's row in
   // bits 0-4, its 16-byte chunk in bits 5-11): the same for every block, so computed once.
   uint32_t gmap[(COPIES_PER_WAVE + 1) / 2];
+  // The latent pool as a buffer of its exact byte extent (pools under 4 GiB): a copy whose offset
+  // lies past the end loads zeros.
+  __amdgpu_buffer_rsrc_t kvrs;
 };
+
+// Bytes of the pool: rows of kv_st elements, the last row's 576 columns.
+__host__ __device__ __forceinline__ int64_t pool_extent(const SparseParams& p) {
+  return p.n_kv <= 0 ? 0 : (p.n_kv - 1) * p.kv_st * 2 + D * 2;
+}
+
+// The source of the copies of invalid slots in pools of 4 GiB or more.
+__device__ const uint4 kZero16 = {0u, 0u, 0u, 0u};
 
 // Row-key index and chunk of copy i of this lane (see SparseCtx::gmap).
 __device__ __forceinline__ uint32_t gather_map_entry(int wave, int lane, int i) {
@@ -141,9 +152,13 @@ __device__ __forceinline__ void stage_indices(const SparseCtx& c, int tid) {
 // last copy repeat it; identical bytes), so the vector-memory counter advances uniformly per
 // block. Pad chunks and the stage tail receive harmless copies of chunk 0 of a valid row.
 // Wave 0 also publishes the block's validity mask (bit k = key k).
-// SMALL: the latent pool spans less than 4 GiB, so a copy's source is a scalar base plus a 32-bit
-// lane offset (no 64-bit address arithmetic per copy).
-template <bool SMALL>
+// Slots that are padded (-1) or name no row of the pool get zeros, never another row's bytes: their
+// logits are masked, and a zero value keeps a non-finite number elsewhere in the pool from
+// reaching the output through 0 * x. BUF: the pool spans less than 4 GiB (less two rows), so a
+// copy is a buffer load at the 32-bit byte offset row * stride + chunk, and an invalid row is
+// replaced by n_kv, which lies past the buffer's end (loads there return zeros). Otherwise each
+// lane forms its 64-bit address and invalid slots read a zero constant.
+template <bool BUF>
 __device__ __forceinline__ void issue_gather(const SparseParams& p, const SparseCtx& c, int j,
                                              char* stage, uint32_t* mask_slot) {
   const int base = j * BNS - c.win0;
@@ -153,20 +168,23 @@ __device__ __forceinline__ void issue_gather(const SparseParams& p, const Sparse
   int rid[COPIES_PER_WAVE], chunk[COPIES_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < COPIES_PER_WAVE; ++i) {
-    const uint32_t e = c.gmap[i >> 1] >> (12 * (i & 1));
+    const uint32_t e = c.gmap[i >> 1] >> (16 * (i & 1));
     chunk[i] = (int)((e >> 5) & 127u);
     rid[i] = c.idx[base + (int)(e & 31u)];
   }
 #pragma unroll
   for (int i = 0; i < COPIES_PER_WAVE; ++i) {
     const int q = min(c.wave + NWAVES * i, COPIES - 1);
-    if (SMALL) {
-      const int r = (uint32_t)rid[i] < (uint32_t)p.n_kv ? rid[i] : 0;
-      const uint32_t off = (uint32_t)r * (uint32_t)(p.kv_st * 2) + (uint32_t)chunk[i] * 16u;
-      g2lds16(reinterpret_cast<const char*>(p.kv) + off, stage + q * 1024);
+    if (BUF) {
+      // an invalid row becomes n_kv, whose bytes start at or past the buffer's end
+      const uint32_t r = min((uint32_t)rid[i], (uint32_t)p.n_kv);
+      const uint32_t off = r * (uint32_t)(p.kv_st * 2) + (uint32_t)chunk[i] * 16u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(c.kvrs, LDS_PTR(void, stage + q * 1024), 16, off, 0, 0, 0);
     } else {
-      const int r = (rid[i] >= 0 && (int64_t)rid[i] < p.n_kv) ? rid[i] : 0;
-      g2lds16(p.kv + (int64_t)r * p.kv_st + chunk[i] * 8, stage + q * 1024);
+      // one 32 x 32 -> 64-bit product per copy (row strides are below 2^31 elements)
+      const bool ok = (uint32_t)rid[i] < (uint32_t)p.n_kv;
+      const uint64_t off = (uint64_t)(uint32_t)rid[i] * (uint32_t)(p.kv_st * 2) + (uint32_t)chunk[i] * 16u;
+      g2lds16(ok ? reinterpret_cast<const char*>(p.kv) + off : reinterpret_cast<const char*>(&kZero16), stage + q * 1024);
     }
   }
   if (c.wave == 0) {
@@ -284,7 +302,7 @@ __device__ __forceinline__ void compute_block(const SparseCtx& c, const char* st
 
 }  // namespace
 
-template <bool SMALL>
+template <bool BUF>
 __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p) {
   __shared__ __attribute__((aligned(1024))) char stage0[STAGE_BYTES];
   __shared__ __attribute__((aligned(1024))) char stage1[STAGE_BYTES];
@@ -313,8 +331,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
 #pragma unroll
   for (int i = 0; i < (COPIES_PER_WAVE + 1) / 2; ++i) {
     c.gmap[i] = gather_map_entry(c.wave, c.lane, 2 * i);
-    if (2 * i + 1 < COPIES_PER_WAVE) c.gmap[i] |= gather_map_entry(c.wave, c.lane, 2 * i + 1) << 12;
+    if (2 * i + 1 < COPIES_PER_WAVE) c.gmap[i] |= gather_map_entry(c.wave, c.lane, 2 * i + 1) << 16;
   }
+  // word 3: the buffer format the gfx9 family expects for untyped loads
+  c.kvrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(p.kv), (short)0, (int)(uint32_t)pool_extent(p),
+                                             0x00020000);
   if (p.block_table != nullptr) {
     // sequence of token t: the last b with cu_q[b] <= t (empty sequences are skipped over)
     int lo = 0, hi = p.batch - 1;
@@ -361,7 +382,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
     __syncthreads();
 #pragma unroll
     for (int b = 0; b < 3; ++b)
-      if (b < nblk) issue_gather<SMALL>(p, c, b, stages[b], &valid_mask[b]);
+      if (b < nblk) issue_gather<BUF>(p, c, b, stages[b], &valid_mask[b]);
     wait_gather(min(nblk, 3) - 1);
     lds_barrier();
 
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
           stage_indices(c, tid);                                                                  \
           __syncthreads();                                                                        \
         }                                                                                         \
-        issue_gather<SMALL>(p, c, jj + 3, NEXT, &valid_mask[((K) + 3) & 3]);                     \
+        issue_gather<BUF>(p, c, jj + 3, NEXT, &valid_mask[((K) + 3) & 3]);                     \
       }                                                                                           \
       if (wave_active)                                                                            \
         compute_block(c, CUR, valid_mask[(K)], qf, m_ref, l_run, o, p.scale_log2);                \
@@ -431,9 +452,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
 
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
-  // the byte extent of the pool (rows of kv_st elements, the last row's 576 columns)
-  const int64_t extent = p.n_kv <= 0 ? 0 : (p.n_kv - 1) * p.kv_st * 2 + D * 2;
-  if (extent <= (int64_t)UINT32_MAX)
+  // byte offsets of an invalid row must still land past a buffer of the pool's extent
+  if (pool_extent(p) <= (int64_t)UINT32_MAX - 2 * p.kv_st * 2)
     hipLaunchKernelGGL(sparse_fwd_kernel<true>, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);
   else
     hipLaunchKernelGGL(sparse_fwd_kernel<false>, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);

@@ -89,6 +89,30 @@ def test_sparse_wide_logit_range_redoes_the_block():
     check_parity(o, lse, ro, rl, c.name)
 
 
+def test_sparse_invalid_slots_read_no_pool_bytes():
+    """Padded (-1), negative and out-of-range indices contribute nothing, whatever the pool holds:
+    here row 0 and every unreferenced row are NaN, and the pool is a strided view whose gap
+    columns are NaN too. The result is the oracle's over the valid slots only."""
+    import torch
+    import mla_varlen_prefill_amd as mla
+    c = make_sparse("sparse_nan_pool", num_tokens=5, heads=128, n_kv=600, topk=160, seed=49, pad_p=0.2,
+                    with_sink=True)
+    n = c.kv.shape[0]
+    idx = c.indices.copy()
+    idx[idx == 0] = 1                      # row 0 is never a valid slot
+    idx[0, 3], idx[1, 7], idx[2, 11], idx[3, 0] = n, n + 100, 2 ** 31 - 1, -5
+    c.indices = idx
+    used = np.unique(idx[(idx >= 0) & (idx < n)])
+    wide = torch.full((n, 640), float("nan"), dtype=torch.bfloat16, device="cuda")
+    wide[torch.from_numpy(used).cuda(), :576] = dev_bf16(c.kv)[torch.from_numpy(used).cuda()]
+    pool = wide[:, :576]
+    announce(f"sparse {c.name}")
+    o, lse = mla.mla_prefill_sparse(dev_bf16(c.q), pool, dev(c.indices), c.scale, sink=dev(c.sink))
+    torch.cuda.synchronize()
+    ro, rl = oracle(c)
+    check_parity(host_f64(o), host_f64(lse), ro, rl, c.name)
+
+
 def test_sparse_deterministic_no_lse():
     c = make_sparse("sparse_det", num_tokens=4, heads=128, n_kv=2000, topk=256, seed=45)
     announce(f"sparse {c.name}")
