@@ -300,7 +300,7 @@ int32_t mla_prefill_varlen_num_splits(int32_t batch, int32_t max_seqlen_q, int32
  *   lse     : nullable float32 [num_tokens, H], strides (lse_stride_tok, lse_stride_head).
  *   workspace : may be NULL when mla_prefill_sparse_workspace_size(...) returns 0.
  * Errors: INVALID_ARG; UNSUPPORTED (head dims other than 576/512, H outside [1, 128], topk
- * outside [1, 8192]); ALIGNMENT; WORKSPACE; HIP.
+ * outside [1, 8192], n_kv or kv_stride_row above 2^31 - 1); ALIGNMENT; WORKSPACE; HIP.
  * ------------------------------------------------------------------------------------------ */
 size_t mla_prefill_sparse_workspace_size(int32_t num_tokens, int32_t num_heads, int32_t topk,
                                          int32_t head_dim_v);
@@ -396,8 +396,9 @@ mla_status_t mla_prefill_sparse_paged(
  *                    h*256 + 128..255 = W_UV_h (a linear layer's weight layout).
  *   sink, out, lse : as for mla_prefill_varlen.
  *   workspace      : mla_prefill_chunked_context_workspace_size(...) bytes, 16-byte aligned.
- * Errors: INVALID_ARG, UNSUPPORTED (batch > 65535, chunk buffer above 2^31 - 1 rows), ALIGNMENT,
- * WORKSPACE, HIP, and those of mla_prefill_varlen for the new-token tensors.
+ * Errors: INVALID_ARG, UNSUPPORTED (batch > 65535, chunk buffer above 2^31 - 1 rows, w_stride_row
+ * of 2^23 elements or more), ALIGNMENT, WORKSPACE, HIP, and those of mla_prefill_varlen for the
+ * new-token tensors.
  * ------------------------------------------------------------------------------------------ */
 size_t mla_prefill_chunked_context_workspace_size(int32_t batch, int32_t total_q, int32_t max_seqlen_q,
                                                   int32_t num_heads, int32_t chunk_tokens);
@@ -425,7 +426,8 @@ mla_status_t mla_prefill_chunked_context(
  *   k_out : bf16 [batch * chunk_tokens, H, 192] (token stride H * 192), written: key columns
  *           0..127 = c W_UK_h^T, 128..191 = the rope columns.
  *   v_out : bf16 [batch * chunk_tokens, H, 128] (token stride H * 128), written.
- * Errors: INVALID_ARG, UNSUPPORTED (batch > 65535), ALIGNMENT, HIP.
+ * Errors: INVALID_ARG, UNSUPPORTED (batch > 65535, w_stride_row of 2^23 elements or more),
+ * ALIGNMENT, HIP.
  * ------------------------------------------------------------------------------------------ */
 mla_status_t mla_latent_upproject(const void* latent, int64_t latent_stride_row,
                                   const int32_t* cu_seqlens_ctx, int32_t batch, int32_t ctx_start,

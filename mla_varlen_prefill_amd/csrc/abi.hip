@@ -609,7 +609,8 @@ mla_status_t mla_latent_upproject(const void* latent, int64_t latent_stride_row,
   if (batch < 0 || ctx_start < 0 || chunk_tokens <= 0 || num_heads <= 0 || latent_stride_row < kSparseDqk ||
       w_stride_row < 512)
     return MLA_ERR_INVALID_ARG;
-  if (batch > 65535 || num_heads > 32767 || chunk_tokens > (1 << 24)) return MLA_ERR_UNSUPPORTED;
+  if (batch > 65535 || num_heads > 32767 || chunk_tokens > (1 << 24) || w_stride_row >= (1 << 23))
+    return MLA_ERR_UNSUPPORTED;  // a head's W_KV rows are addressed with 32-bit byte offsets
   if (!aligned16(latent) || !aligned16(w_kv) || !aligned16(k_out) || !aligned16(v_out) ||
       !stride_ok(latent_stride_row) || !stride_ok(w_stride_row) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens_ctx) & 3u) != 0 || (reinterpret_cast<uintptr_t>(cu_chunk) & 3u) != 0)
@@ -652,7 +653,8 @@ mla_status_t mla_prefill_chunked_context(
       !(softmax_scale > 0.f))
     return MLA_ERR_INVALID_ARG;
   if (batch > 65535 || num_heads > 32767 || chunk_tokens > (1 << 24) ||
-      (int64_t)batch * chunk_tokens > INT32_MAX || (int64_t)num_heads * kDenseDqk >= (1 << 23))
+      (int64_t)batch * chunk_tokens > INT32_MAX || (int64_t)num_heads * kDenseDqk >= (1 << 23) ||
+      w_stride_row >= (1 << 23))
     return MLA_ERR_UNSUPPORTED;
   if (!aligned16(latent) || !aligned16(w_kv) || !stride_ok(latent_stride_row) || !stride_ok(w_stride_row) ||
       (reinterpret_cast<uintptr_t>(cu_seqlens_ctx) & 3u) != 0)

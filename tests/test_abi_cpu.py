@@ -207,9 +207,21 @@ def test_sparse_argument_errors():
     assert _sparse(lib, heads=129) == 2
     assert _sparse(lib, topk=8193, idxst=8193) == 2
     assert _sparse(lib, dqk=512) == 2
+    assert _sparse(lib, kvst=2 ** 31) == 2          # row strides of 2^31 elements or more
     assert _sparse(lib, kv=P + 4) == 3
     assert _sparse(lib, idx=P + 2) == 3
     assert _sparse(lib, t=0) == 0
+
+
+def test_latent_upproject_argument_errors():
+    """Checked before any device access: W_KV row strides of 2^23 elements or more are
+    unsupported (a head's rows are addressed with 32-bit byte offsets)."""
+    lib = mla.load_library()
+    cu = P + 64
+    assert lib.mla_latent_upproject(P, 576, cu, 2, 0, 128, P, 2 ** 23, 4, cu, P, P, None) == 2
+    assert lib.mla_latent_upproject(P, 576, cu, 2, 0, 128, P, 500, 4, cu, P, P, None) == 1
+    assert lib.mla_latent_upproject(P, 576, cu, 65536, 0, 128, P, 512, 4, cu, P, P, None) == 2
+    assert lib.mla_latent_upproject(P, 576, cu, 0, 0, 128, P, 512, 4, cu, P, P, None) == 0
 
 
 def _sparse_paged(lib, **kw):
