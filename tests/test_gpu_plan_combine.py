@@ -18,6 +18,12 @@ PLAN_CASES = [
     ([32768], None, True, 128, 64),
     ([3] * 20000, None, True, 128, 64),          # more slots than the sort capacity
     ([1, 2, 3] * 3000, None, False, 16, 16),     # sorted path, many ties
+    # sequence-order path (no window, up to 1024 sequences): ragged lengths with empty sequences
+    # and ties in key blocks, exactly 1024 sequences, and 1025 (the slot sort again)
+    ([int(x) for x in np.random.default_rng(7).integers(0, 700, 300)],
+     [int(x) for x in np.random.default_rng(8).integers(0, 2000, 300)], True, 64, 64),
+    ([(i % 129) + 1 for i in range(1024)], None, True, 128, 64),
+    ([(i % 129) + 1 for i in range(1025)], None, False, 128, 64),
 ]
 
 
