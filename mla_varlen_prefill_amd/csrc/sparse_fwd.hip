@@ -439,14 +439,28 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
       lse_v = mxs + __logf(z);
     }
   }
-  if (hok_e) {
-    __bf16* op = p.out + (int64_t)t * p.o_st + (int64_t)head_e * p.o_sh + 4 * c.g;
+  if (hok_e && p.lse != nullptr && (tid_e & 48) == 0) p.lse[(int64_t)t * p.l_st + (int64_t)head_e * p.l_sh] = lse_v;
+  // O through LDS: the ring is free (every wave passed the barrier after its last block). Wave w
+  // turns its 16 heads x 512 columns (16 KiB) around in half of ring slot w / 2 (row = head,
+  // 16-byte chunk c of a row at c ^ head, so the 16 heads of a write land on 16 bank groups),
+  // then stores whole 1 KiB head rows, 16 bytes per lane. (Each lane holds 4 columns per output
+  // tile, so direct stores would cover 16 rows x 32 bytes per instruction.)
+  {
+    const int w2 = c.wave >> 1;
+    char* tb = (w2 == 0 ? stage0 : w2 == 1 ? stage1 : w2 == 2 ? stage2 : stage3) + (c.wave & 1) * 16384;
+    // lane-derived values formed again from the thread index (not kept through the block loop)
+    const int l16 = tid_e & 15, g = (tid_e >> 4) & 3, lane = tid_e & 63;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) {
-      u32x2 v = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
-      *reinterpret_cast<u32x2*>(op + dt * 16) = v;
+      const u32x2 v = {pack_bf16x2(o[dt][0] * inv, o[dt][1] * inv), pack_bf16x2(o[dt][2] * inv, o[dt][3] * inv)};
+      *reinterpret_cast<u32x2*>(tb + l16 * 1024 + (((2 * dt + (g >> 1)) ^ l16) << 4) + (g & 1) * 8) = v;
     }
-    if (p.lse != nullptr && c.g == 0) p.lse[(int64_t)t * p.l_st + (int64_t)head_e * p.l_sh] = lse_v;
+    __bf16* orow = p.out + (int64_t)t * p.o_st + (int64_t)(c.wave * 16) * p.o_sh + lane * 8;
+#pragma unroll 4
+    for (int r = 0; r < 16; ++r) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(tb + r * 1024 + ((lane ^ r) << 4));
+      if (c.wave * 16 + r < p.num_heads) *reinterpret_cast<u32x4*>(orow + (int64_t)r * p.o_sh) = x;
+    }
   }
 }
 
