@@ -761,6 +761,7 @@ mla_status_t sparse_call(mla::SparseParams& sp, const void* q, int64_t q_stride_
   sp.idx = indices; sp.idx_st = idx_stride_tok; sp.topk = topk;
   sp.topk_length = topk_length;
   sp.num_tokens = num_tokens;
+  sp.max_wgs = di->cus > 0 ? di->cus : 256;
   sp.num_heads = num_heads;
   sp.scale = softmax_scale;
   sp.scale_log2 = softmax_scale * 1.4426950408889634f;

@@ -77,6 +77,7 @@ struct SparseParams {
   const int32_t* cu_q; int32_t batch;
   const int32_t* seqused;
   const int32_t* seqused_q;  // nullable [batch]: tokens of sequence b at or past cu_q[b] + seqused_q[b] see no key
+  int32_t max_wgs;           // persistent grid: at most this many work-groups (the CU count)
 };
 
 struct CombineParams {

@@ -37,6 +37,8 @@
 //     chunk 8 (kk >> 1) + 2 (kk & 1) + sigma(g), sigma = (0,4,1,5), and Q^T uses the same order,
 //     so the two lane groups of a half-wave sit 64 bytes apart.
 // Every operand read is then a per-lane base plus an immediate offset.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -311,21 +313,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
   __shared__ int idx_lds[IDX_WIN];
   __shared__ uint32_t valid_mask[4];
 
-  const int t = blockIdx.x;
   const int tid = threadIdx.x;
   SparseCtx c;
   c.lane = tid & 63;
   c.wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   c.l16 = c.lane & 15;
   c.g = c.lane >> 4;
-  c.len = p.topk;
-  if (p.topk_length != nullptr) c.len = min(max(p.topk_length[t], 0), p.topk);
-  if (p.n_kv <= 0) c.len = 0;  // an empty pool has no valid slot (and no row to read)
-  c.irow = p.idx + (int64_t)t * p.idx_st;
-  c.win0 = 0;
   c.idx = idx_lds;
-  c.bt_row = nullptr;
-  c.used = 0;
   c.bs = p.block_size;
   c.nblocks = p.num_blocks;
 #pragma unroll
@@ -336,6 +330,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
   // word 3: the buffer format the gfx9 family expects for untyped loads
   c.kvrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<__bf16*>(p.kv), (short)0, (int)(uint32_t)pool_extent(p),
                                              0x00020000);
+
+  // Persistent: one work-group per CU goes through tokens one after the other (no work-group
+  // launch and teardown per token). The tokens are split into 8 contiguous ranges, one per XCD
+  // (work-group i runs on XCD i % 8), dealt round-robin to that XCD's work-groups, so tokens close
+  // in the sequence (which share many gathered rows in practice) run on the same L2.
+  const int xcd = blockIdx.x & 7;
+  const int per_xcd = (p.num_tokens + 7) / 8;
+  const int t_end = min(p.num_tokens, (xcd + 1) * per_xcd);
+  const int wg_x = ((int)gridDim.x - xcd + 7) / 8;  // work-groups on this XCD
+  for (int t = xcd * per_xcd + (int)(blockIdx.x >> 3); t < t_end; t += wg_x) {
+  c.len = p.topk;
+  if (p.topk_length != nullptr) c.len = min(max(p.topk_length[t], 0), p.topk);
+  if (p.n_kv <= 0) c.len = 0;  // an empty pool has no valid slot (and no row to read)
+  c.irow = p.idx + (int64_t)t * p.idx_st;
+  c.win0 = 0;
+  c.bt_row = nullptr;
+  c.used = 0;
   if (p.block_table != nullptr) {
     // sequence of token t: the last b with cu_q[b] <= t (empty sequences are skipped over)
     int lo = 0, hi = p.batch - 1;
@@ -462,15 +473,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
       if (c.wave * 16 + r < p.num_heads) *reinterpret_cast<u32x4*>(orow + (int64_t)r * p.o_sh) = x;
     }
   }
+  }
 }
 
 hipError_t launch_sparse_fwd(const SparseParams& p, hipStream_t stream) {
   if (p.num_tokens <= 0) return hipSuccess;
+  // one work-group per CU (their LDS allows no more), no more than tokens
+  const int grid = std::max(1, std::min(p.num_tokens, p.max_wgs > 0 ? p.max_wgs : 256));
   // byte offsets of an invalid row must still land past a buffer of the pool's extent
   if (pool_extent(p) <= (int64_t)UINT32_MAX - 2 * p.kv_st * 2)
-    hipLaunchKernelGGL(sparse_fwd_kernel<true>, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(sparse_fwd_kernel<true>, dim3(grid), dim3(NTHREADS), 0, stream, p);
   else
-    hipLaunchKernelGGL(sparse_fwd_kernel<false>, dim3(p.num_tokens), dim3(NTHREADS), 0, stream, p);
+    hipLaunchKernelGGL(sparse_fwd_kernel<false>, dim3(grid), dim3(NTHREADS), 0, stream, p);
   return hipGetLastError();
 }
 
