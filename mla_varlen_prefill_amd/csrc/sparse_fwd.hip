@@ -190,7 +190,9 @@ __device__ __forceinline__ void issue_gather(const SparseParams& p, const Sparse
     }
   }
   if (c.wave == 0) {
-    const int rid = c.idx[base + (c.lane & 31)];
+    int ln = c.lane;
+    asm volatile("" : "+v"(ln));  // the address is formed here, not kept in a register across the loop
+    const int rid = c.idx[base + (ln & 31)];
     const bool ok = c.lane < 32 && rid >= 0 && (int64_t)rid < p.n_kv;
     const uint64_t b = __ballot(ok);
     if (c.lane == 0) *mask_slot = (uint32_t)b;
@@ -366,13 +368,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void sparse_fwd_kernel(SparseParams p)
   }
   const int nblk = (c.len + BNS - 1) / BNS;
 
-  // ---- Q^T of this lane's head: the 8 columns of the chunk its lane group contracts per step
-  const int head = c.wave * 16 + c.l16;
-  const bool hok = head < p.num_heads;
+  // ---- Q^T of this lane's head: the 8 columns of the chunk its lane group contracts per step.
+  // The lane's head and chunk are formed again from the thread index for each token (a per-lane
+  // address kept from one token to the next would be spilled: the block loop needs every register).
   const bool wave_active = c.wave * 16 < p.num_heads;
   bf16x8 qf[KSTEPS];
   {
-    const __bf16* qp = p.q + (int64_t)t * p.q_st + (int64_t)(hok ? head : 0) * p.q_sh + chunk_lane(c.g) * 8;
+    int tid_q = (int)threadIdx.x;
+    asm volatile("" : "+v"(tid_q));
+    const int head = c.wave * 16 + (tid_q & 15);
+    const bool hok = head < p.num_heads;
+    const __bf16* qp = p.q + (int64_t)t * p.q_st + (int64_t)(hok ? head : 0) * p.q_sh +
+                       chunk_lane((tid_q >> 4) & 3) * 8;
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       bf16x8 v = *reinterpret_cast<const bf16x8*>(qp + chunk_step(kk) * 8);
