@@ -7,7 +7,8 @@
 // as in page "mla_prefill_branch_sparse_fp8". The 576 columns are 512 latent then 64 rope; the
 // value vector is the first 512 columns of the same row.
 //
-// Work decomposition: one work-group of 8 waves (two per SIMD) per query token. All heads of a
+// Work decomposition: a token is computed by one work-group of 8 waves (two per SIMD); the
+// work-groups are persistent, one per CU, each going through a range of tokens. All heads of a
 // token read the same gathered rows, so the heads form the matrix-core N dimension: wave w owns
 // heads [16w, 16w+16) and every latent row is gathered once per token.
 //   * Q^T of the wave's 16 heads (576 deep) stays in registers (72 per lane); the 16x16 O^T tiles
