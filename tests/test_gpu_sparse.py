@@ -38,6 +38,38 @@ def test_sparse_small_ragged_topk(heads):
     check_parity(o, lse, ro, rl, c.name)
 
 
+def test_sparse_many_tokens_per_work_group():
+    """More tokens than the device has CUs, so each persistent work-group computes several tokens
+    one after the other (1000 tokens: 3 or 4 per work-group, ranges per XCD that do not divide
+    evenly), with token lengths from 0 to the full top-k: each token's softmax state, index window
+    and ring start from scratch whatever the previous token of the work-group left. 40 heads
+    leave part of a wave and whole waves without a head. Checked in full against the oracle."""
+    c = make_sparse("sparse_persist", num_tokens=1000, heads=40, n_kv=5000, topk=192, seed=51,
+                    pad_p=0.05, with_sink=True, with_topk_length=True)
+    tl = c.topk_length.copy()
+    tl[::7] = 0                          # some tokens with no block at all
+    tl[3::11] = 192                      # some with every slot
+    c.topk_length = tl
+    announce(f"sparse {c.name}")
+    o, lse = run_sparse(c)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
+def test_sparse_many_tokens_two_index_windows():
+    """As above with a top-k past one staged index window (2100 slots: a second window is
+    staged part-way through each token), 300 tokens over 16 heads."""
+    c = make_sparse("sparse_persist_win", num_tokens=300, heads=16, n_kv=20000, topk=2100, seed=52,
+                    pad_p=0.05, with_sink=False, with_topk_length=True)
+    tl = c.topk_length.copy()
+    tl[::5] = 2100
+    c.topk_length = tl
+    announce(f"sparse {c.name}")
+    o, lse = run_sparse(c)
+    ro, rl = oracle(c)
+    check_parity(o, lse, ro, rl, c.name)
+
+
 def test_sparse_topk_length_out_of_range_and_duplicates():
     c = make_sparse("sparse_edges", num_tokens=7, heads=128, n_kv=500, topk=96, seed=42, pad_p=0.05,
                     with_sink=False, with_topk_length=True)

@@ -43,6 +43,21 @@ def test_paged_ragged_sequences(block_size):
     check_parity(o, lse, ro, rl, c.name)
 
 
+def test_paged_many_tokens_per_work_group():
+    """More tokens than the device has CUs over 9 sequences (one empty, one with a single cached
+    position), so a persistent work-group's consecutive tokens can belong to different sequences:
+    each token finds its own block-table row, used length and seqused_q state; seqused_q drops
+    part of three sequences. Checked in full against the oracle."""
+    lens_kv = [900, 1, 2500, 0, 64, 1700, 333, 4000, 128]
+    n_tok = [120, 30, 150, 0, 45, 140, 99, 190, 86]
+    c = make_sparse_paged("paged_persist", lens_kv, n_tok, 32, 160, 16, seed=90, with_topk_length=True)
+    used_q = [120, 30, 100, 0, 0, 140, 99, 37, 86]
+    announce(f"sparse paged {c.name}")
+    o, lse = run_paged(c, used_q)
+    ro, rl = oracle(c, used_q)
+    check_parity(o, lse, ro, rl, c.name)
+
+
 @pytest.mark.parametrize("with_sink", [False, True])
 def test_paged_seqused_q(with_sink):
     """seqused_q: only the first seqused_q[b] tokens of each sequence are in use; the others are
